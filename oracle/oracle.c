@@ -1,0 +1,247 @@
+/*
+ * CPU fp64 reference for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. It shares no code,
+ * header, table or helper with the GPU library and must never be used as a
+ * fallback for it.
+ *
+ * What it computes is the plain definition, written out with every N x N
+ * intermediate materialised (no tiling, no online softmax, no fusion):
+ *
+ *   S = scale * Q K^T                (mstx.cn/posts/485 §二.1 "标准 Attention 的计算";
+ *                                     the 1/sqrt(d) factor is the one written in
+ *                                     nanhubrain.csdn.net §二 "反向传播的代价")
+ *   S_ij = -inf where j is not allowed for row i:
+ *        causal: P_ij = 0 for j > i  (nanhubrain.csdn.net §三 "因果掩码下的锯齿形调度")
+ *        fixed block mask: zero blocks are skipped
+ *                                    (lukebest.github.io FlashAttention, "Block-Sparse FlashAttention")
+ *   P = softmax(S) row by row, max-subtracted
+ *                                    (cloud.baidu.com/article/7906313 §工作原理 "数学等价变换";
+ *                                     mstx.cn/posts/485 §三.2 "标准 softmax")
+ *   O = P V                          (mstx.cn/posts/485 §二.1)
+ *   LSE_i = m_i + ln(l_i)            (the saved per-row statistic; the pages save
+ *                                     (m, l), mstx.cn/posts/485 §三.3 "重计算")
+ *
+ * Backward, for a loss L with dL/dO = dO (the recompute method of
+ * lukebest.github.io "反向：重算而非存储" reaches the same gradients):
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *   dS = P o (dP - D 1^T),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ * The printed gradient formula of cloud.baidu.com §工作原理 "梯度计算优化" is
+ * garbled (a matrix product where a row sum belongs); the rule above is the
+ * softmax Jacobian written out, and sum_j P_ij dP_ij = sum_k dO_ik O_ik holds
+ * exactly because O_i = sum_j P_ij V_j.
+ *
+ * Convention for a row with no allowed key (not on the pages): O_i = 0,
+ * LSE_i = -inf, and the row contributes nothing to any gradient.
+ *
+ * Layout: every tensor is contiguous [B][H][N][d] (d fastest), LSE is
+ * [B][H][N]. The block mask is [nb][nb] row-major with nb = ceil(N/blk),
+ * nonzero = keep, shared by all (b, h), and combined with causal by AND.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#include "oracle.h"
+
+static int key_allowed(long i, long j, int causal, const unsigned char *mask,
+                       long blk, long nb)
+{
+    if (causal && j > i)
+        return 0;
+    if (mask && mask[(i / blk) * nb + (j / blk)] == 0)
+        return 0;
+    return 1;
+}
+
+/* One row of the forward for one head: fills srow[0..N) with P_i. (row of P),
+ * writes O_i and LSE_i. */
+static void forward_row(const double *q, const double *k, const double *v,
+                        long N, long d, double scale, int causal,
+                        const unsigned char *mask, long blk, long nb, long i,
+                        double *prow, double *orow, double *lse)
+{
+    double m = -INFINITY;
+    for (long j = 0; j < N; ++j) {
+        if (!key_allowed(i, j, causal, mask, blk, nb)) {
+            prow[j] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        for (long c = 0; c < d; ++c)
+            dot += q[i * d + c] * k[j * d + c];
+        prow[j] = scale * dot;
+        if (prow[j] > m)
+            m = prow[j];
+    }
+    for (long c = 0; c < d; ++c)
+        orow[c] = 0.0;
+    if (m == -INFINITY) {
+        for (long j = 0; j < N; ++j)
+            prow[j] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (long j = 0; j < N; ++j) {
+        double e = (prow[j] == -INFINITY) ? 0.0 : exp(prow[j] - m);
+        prow[j] = e;
+        l += e;
+    }
+    for (long j = 0; j < N; ++j)
+        prow[j] /= l;
+    for (long j = 0; j < N; ++j) {
+        if (prow[j] == 0.0)
+            continue;
+        for (long c = 0; c < d; ++c)
+            orow[c] += prow[j] * v[j * d + c];
+    }
+    *lse = m + log(l);
+}
+
+static int check_args(long B, long H, long N, long d, long blk)
+{
+    if (B < 0 || H < 0 || N < 0 || d <= 0 || blk <= 0)
+        return ORACLE_ERR_ARG;
+    return ORACLE_OK;
+}
+
+int oracle_attention(const double *Q, const double *K, const double *V,
+                     const double *dO, double *O, double *LSE,
+                     double *dQ, double *dK, double *dV,
+                     long B, long H, long N, long d, double scale, int causal,
+                     const unsigned char *blockmask, long blk)
+{
+    int rc = check_args(B, H, N, d, blk);
+    if (rc != ORACLE_OK)
+        return rc;
+    const long nb = (N + blk - 1) / blk;
+    const int want_bwd = (dO != NULL);
+    if (want_bwd && (dQ == NULL || dK == NULL || dV == NULL))
+        return ORACLE_ERR_ARG;
+    if (N == 0)
+        return ORACLE_OK;
+
+    double *P = (double *)malloc(sizeof(double) * (size_t)N * (size_t)N);
+    double *dS = want_bwd ? (double *)malloc(sizeof(double) * (size_t)N * (size_t)N) : NULL;
+    double *D = want_bwd ? (double *)malloc(sizeof(double) * (size_t)N) : NULL;
+    if (!P || (want_bwd && (!dS || !D))) {
+        free(P); free(dS); free(D);
+        return ORACLE_ERR_NOMEM;
+    }
+
+    for (long bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * N * d, *k = K + bh * N * d, *v = V + bh * N * d;
+        double *o = O + bh * N * d, *lse = LSE + bh * N;
+
+        /* Forward: materialise every row of P. */
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i)
+            forward_row(q, k, v, N, d, scale, causal, blockmask, blk, nb, i,
+                        P + i * N, o + i * d, lse + i);
+
+        if (!want_bwd)
+            continue;
+
+        const double *dout = dO + bh * N * d;
+        double *dq = dQ + bh * N * d, *dk = dK + bh * N * d, *dv = dV + bh * N * d;
+
+        /* D_i = rowsum(dO o O); dP_ij = dO_i . V_j; dS = P o (dP - D);
+         * dQ_i = scale * sum_j dS_ij K_j. */
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            double Di = 0.0;
+            for (long c = 0; c < d; ++c)
+                Di += dout[i * d + c] * o[i * d + c];
+            D[i] = Di;
+            for (long j = 0; j < N; ++j) {
+                double pij = P[i * N + j];
+                if (pij == 0.0) {
+                    dS[i * N + j] = 0.0;
+                    continue;
+                }
+                double dp = 0.0;
+                for (long c = 0; c < d; ++c)
+                    dp += dout[i * d + c] * v[j * d + c];
+                dS[i * N + j] = pij * (dp - Di);
+            }
+            for (long c = 0; c < d; ++c)
+                dq[i * d + c] = 0.0;
+            for (long j = 0; j < N; ++j) {
+                double s = dS[i * N + j];
+                if (s == 0.0)
+                    continue;
+                for (long c = 0; c < d; ++c)
+                    dq[i * d + c] += s * k[j * d + c];
+            }
+            for (long c = 0; c < d; ++c)
+                dq[i * d + c] *= scale;
+        }
+
+        /* dK_j = scale * sum_i dS_ij Q_i;  dV_j = sum_i P_ij dO_i. */
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long j = 0; j < N; ++j) {
+            for (long c = 0; c < d; ++c) {
+                dk[j * d + c] = 0.0;
+                dv[j * d + c] = 0.0;
+            }
+            for (long i = 0; i < N; ++i) {
+                double s = dS[i * N + j];
+                double pij = P[i * N + j];
+                if (s != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        dk[j * d + c] += s * q[i * d + c];
+                if (pij != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        dv[j * d + c] += pij * dout[i * d + c];
+            }
+            for (long c = 0; c < d; ++c)
+                dk[j * d + c] *= scale;
+        }
+    }
+    free(P);
+    free(dS);
+    free(D);
+    return ORACLE_OK;
+}
+
+int oracle_attention_rows(const double *Q, const double *K, const double *V,
+                          long B, long H, long N, long d, double scale, int causal,
+                          const unsigned char *blockmask, long blk,
+                          const long *row_bh, const long *row_i, long nrows,
+                          double *O_rows, double *LSE_rows)
+{
+    int rc = check_args(B, H, N, d, blk);
+    if (rc != ORACLE_OK)
+        return rc;
+    for (long r = 0; r < nrows; ++r)
+        if (row_bh[r] < 0 || row_bh[r] >= B * H || row_i[r] < 0 || row_i[r] >= N)
+            return ORACLE_ERR_ARG;
+    const long nb = (N + blk - 1) / blk;
+    int nomem = 0;
+    #pragma omp parallel
+    {
+        double *prow = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        if (!prow) {
+            #pragma omp atomic write
+            nomem = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (long r = 0; r < nrows; ++r) {
+                const long bh = row_bh[r];
+                forward_row(Q + bh * N * d, K + bh * N * d, V + bh * N * d, N, d,
+                            scale, causal, blockmask, blk, nb, row_i[r], prow,
+                            O_rows + r * d, LSE_rows + r);
+            }
+        }
+        free(prow);
+    }
+    return nomem ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}

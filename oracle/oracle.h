@@ -1,0 +1,37 @@
+/*
+ * CPU fp64 attention reference (test infrastructure only; see oracle.c).
+ * Tensors are contiguous [B][H][N][d] doubles, LSE is [B][H][N].
+ * blockmask is NULL (dense) or [ceil(N/blk)][ceil(N/blk)] bytes, nonzero = keep.
+ */
+#ifndef ATTN_ORACLE_H
+#define ATTN_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_OK = 0, ORACLE_ERR_ARG = 1, ORACLE_ERR_NOMEM = 2 };
+
+/* Forward (and, when dO != NULL, backward) of exact attention.
+ * O, LSE always written; dQ, dK, dV written when dO != NULL. */
+int oracle_attention(const double *Q, const double *K, const double *V,
+                     const double *dO, double *O, double *LSE,
+                     double *dQ, double *dK, double *dV,
+                     long B, long H, long N, long d, double scale, int causal,
+                     const unsigned char *blockmask, long blk);
+
+/* Forward for selected rows only: row r is query row_i[r] of head row_bh[r]
+ * (head index b*H + h). Writes O_rows[r][0..d) and LSE_rows[r]. */
+int oracle_attention_rows(const double *Q, const double *K, const double *V,
+                          long B, long H, long N, long d, double scale, int causal,
+                          const unsigned char *blockmask, long blk,
+                          const long *row_bh, const long *row_i, long nrows,
+                          double *O_rows, double *LSE_rows);
+
+/* Number of OpenMP threads the reference runs with. */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
