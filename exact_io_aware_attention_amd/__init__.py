@@ -1,0 +1,189 @@
+"""Python binding of libfa.so, the gfx950 exact IO-aware attention library.
+
+Argument marshalling only: every step of the forward and backward runs in
+the HIP kernels behind the C ABI declared in include/fa.h. torch supplies
+device memory and streams. There is no fallback: if libfa.so is missing or
+fails to load, importing this package raises.
+
+Functions carry the C names:
+    fa_fwd(Q, K, V, O, LSE, scale, causal=False, blockmask=None, stream=None)
+    fa_bwd(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False,
+           blockmask=None, workspace=None, stream=None)
+    fa_fwd_f32(...), fa_bwd_f32(...)  -- the fp32 debug path, same arguments
+    fa_bwd_workspace_bytes(B, H, N, d)
+Tensors are contiguous CUDA (HIP) tensors of shape [B, H, N, d]: bfloat16 for
+fa_fwd / fa_bwd, float32 for the _f32 entry points; LSE is float32 [B, H, N];
+blockmask is uint8 [ceil(N/128), ceil(N/128)] on the same device, or None.
+"""
+import ctypes
+import os
+
+# torch first: it loads its own HIP runtime, and libfa.so must bind to that
+# same runtime (two HIP runtimes in one process do not share the device).
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python exact_io_aware_attention_amd/build.py` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FA_OK = 0
+FA_MASK_BLOCK = 128
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM",
+                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_lib.fa_fwd.restype = _i
+_lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]
+_lib.fa_fwd_f32.restype = _i
+_lib.fa_fwd_f32.argtypes = _lib.fa_fwd.argtypes
+_lib.fa_bwd.restype = _i
+_lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                        _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.fa_bwd_f32.restype = _i
+_lib.fa_bwd_f32.argtypes = _lib.fa_bwd.argtypes
+_lib.fa_bwd_workspace_bytes.restype = _sz
+_lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.fa_status_str.restype = ctypes.c_char_p
+_lib.fa_status_str.argtypes = [_i]
+_lib.fa_last_hip_error.restype = ctypes.c_char_p
+_lib.fa_last_hip_error.argtypes = []
+_lib.fa_version.restype = ctypes.c_char_p
+_lib.fa_version.argtypes = []
+
+# Symbols declared in include/fa.h (checked by the ABI test).
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_workspace_bytes",
+            "fa_status_str", "fa_last_hip_error", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = f"{STATUS_NAMES.get(status, status)}: {_lib.fa_status_str(status).decode()}"
+        if status == 7:
+            msg += f" ({_lib.fa_last_hip_error().decode()})"
+        super().__init__(msg)
+
+
+def lib():
+    """The loaded ctypes library (raw pointer-level access)."""
+    return _lib
+
+
+def version() -> str:
+    return _lib.fa_version().decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return tuple(int(x) for x in q.shape)
+
+
+def _require(ts, dtype, shape):
+    for t in ts:
+        if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"expected contiguous {dtype} device tensors of shape {shape}")
+
+
+def _require_lse(lse, shape):
+    import torch
+    B, H, N, _ = shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError(f"LSE must be contiguous float32 of shape {(B, H, N)}")
+
+
+def _require_mask(mask, N):
+    import torch
+    if mask is None:
+        return
+    nb = (N + FA_MASK_BLOCK - 1) // FA_MASK_BLOCK
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (nb, nb) or not mask.is_contiguous():
+        raise ValueError(f"blockmask must be contiguous uint8 of shape {(nb, nb)}")
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def _fwd(fn, dtype, Q, K, V, O, LSE, scale, causal, blockmask, stream):
+    shape = _shape(Q)
+    _require((Q, K, V, O), dtype, shape)
+    _require_lse(LSE, shape)
+    _require_mask(blockmask, shape[2])
+    B, H, N, d = shape
+    _check(fn(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, N, d, float(scale),
+              int(bool(causal)), _ptr(blockmask), _stream_ptr(stream)))
+
+
+def _workspace(shape, workspace, device):
+    import torch
+    need = fa_bwd_workspace_bytes(*shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _bwd(fn, dtype, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal, blockmask, workspace,
+         stream):
+    shape = _shape(Q)
+    _require((dO, Q, K, V, O, dQ, dK, dV), dtype, shape)
+    _require_lse(LSE, shape)
+    _require_mask(blockmask, shape[2])
+    ws = _workspace(shape, workspace, Q.device)
+    B, H, N, d = shape
+    _check(fn(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(dQ), _ptr(dK),
+              _ptr(dV), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
+              _ptr(ws), ws.numel() * ws.element_size(), _stream_ptr(stream)))
+
+
+def fa_fwd(Q, K, V, O, LSE, scale, causal=False, blockmask=None, stream=None):
+    """Forward, bf16: writes O and LSE in place."""
+    import torch
+    _fwd(_lib.fa_fwd, torch.bfloat16, Q, K, V, O, LSE, scale, causal, blockmask, stream)
+
+
+def fa_fwd_f32(Q, K, V, O, LSE, scale, causal=False, blockmask=None, stream=None):
+    """Forward, fp32 debug path: writes O and LSE in place."""
+    import torch
+    _fwd(_lib.fa_fwd_f32, torch.float32, Q, K, V, O, LSE, scale, causal, blockmask, stream)
+
+
+def fa_bwd(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False, blockmask=None,
+           workspace=None, stream=None):
+    """Backward, bf16: writes dQ, dK, dV in place."""
+    import torch
+    _bwd(_lib.fa_bwd, torch.bfloat16, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal,
+         blockmask, workspace, stream)
+
+
+def fa_bwd_f32(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False, blockmask=None,
+               workspace=None, stream=None):
+    """Backward, fp32 debug path: writes dQ, dK, dV in place."""
+    import torch
+    _bwd(_lib.fa_bwd_f32, torch.float32, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal,
+         blockmask, workspace, stream)

@@ -1,0 +1,213 @@
+// C ABI of the attention library: argument validation, dispatch to the
+// kernel launchers, status codes. No exception crosses this boundary and no
+// device memory is allocated here.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+fa_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return FA_OK;
+    std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d): %s",
+                  hipGetErrorName(e), (int)e, hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Checks common to every entry point, in a fixed order. *empty is set when
+// the problem has no elements (then nothing is launched).
+fa_status check_common(int B, int H, int N, int d, float scale, int causal, bool *empty)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return FA_ERR_SHAPE;
+    if (d != 64 && d != 128)
+        return FA_ERR_HEADDIM;
+    if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1))
+        return FA_ERR_SCALE;
+    // every element index of a [B][H][N][d] tensor must fit in 63 bits and a
+    // per-head slab in 31 bits of elements
+    const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+    const unsigned long long head = (unsigned long long)N * (unsigned long long)d;
+    if (head > (unsigned long long)std::numeric_limits<int>::max())
+        return FA_ERR_SHAPE;
+    if (bh > 0 && head > 0 && bh > (unsigned long long)std::numeric_limits<long long>::max() / head)
+        return FA_ERR_SHAPE;
+    // work items per launch (B*H*ceil(N/64)) must fit in an int
+    if (bh * (((unsigned long long)N + 63) / 64) > (unsigned long long)std::numeric_limits<int>::max() / 2)
+        return FA_ERR_SHAPE;
+    *empty = (B == 0 || H == 0 || N == 0);
+    return FA_OK;
+}
+
+fa_status check_ptrs(std::initializer_list<const void *> ptrs)
+{
+    for (const void *p : ptrs)
+        if (p == nullptr)
+            return FA_ERR_NULL;
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+fa::Problem make_problem(int B, int H, int N, int d, float scale, int causal,
+                         const uint8_t *mask, void *stream)
+{
+    fa::Problem p;
+    p.B = B;
+    p.H = H;
+    p.N = N;
+    p.d = d;
+    p.scale = scale;
+    p.causal = causal;
+    p.mask = mask;
+    p.stream = static_cast<hipStream_t>(stream);
+    return p;
+}
+
+template <typename T>
+fa_status fwd_common(const T *Q, const T *K, const T *V, T *O, float *LSE, int B, int H, int N,
+                     int d, float scale, int causal, const uint8_t *blockmask, void *stream,
+                     bool f32)
+{
+    bool empty = false;
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    if (empty)
+        return FA_OK;
+    st = check_ptrs({Q, K, V, O, LSE});
+    if (st != FA_OK)
+        return st;
+    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    if (f32)
+        return hip_status(fa::launch_fwd_f32(p, reinterpret_cast<const float *>(Q),
+                                             reinterpret_cast<const float *>(K),
+                                             reinterpret_cast<const float *>(V),
+                                             reinterpret_cast<float *>(O), LSE));
+    return hip_status(fa::launch_fwd_bf16(p, reinterpret_cast<const uint16_t *>(Q),
+                                          reinterpret_cast<const uint16_t *>(K),
+                                          reinterpret_cast<const uint16_t *>(V),
+                                          reinterpret_cast<uint16_t *>(O), LSE));
+}
+
+template <typename T>
+fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O,
+                     const float *LSE, T *dQ, T *dK, T *dV, int B, int H, int N, int d,
+                     float scale, int causal, const uint8_t *blockmask, void *workspace,
+                     size_t workspace_bytes, void *stream, bool f32)
+{
+    bool empty = false;
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    if (empty)
+        return FA_OK;
+    st = check_ptrs({dO, Q, K, V, O, LSE, dQ, dK, dV});
+    if (st != FA_OK)
+        return st;
+    const fa::BwdWorkspace L = fa::bwd_workspace_layout(B, H, N, d);
+    if (workspace == nullptr || workspace_bytes < L.bytes ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return FA_ERR_WORKSPACE;
+    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    if (f32)
+        return hip_status(fa::launch_bwd_f32(
+            p, reinterpret_cast<const float *>(dO), reinterpret_cast<const float *>(Q),
+            reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(V),
+            reinterpret_cast<const float *>(O), LSE, reinterpret_cast<float *>(dQ),
+            reinterpret_cast<float *>(dK), reinterpret_cast<float *>(dV), workspace));
+    return hip_status(fa::launch_bwd_bf16(
+        p, reinterpret_cast<const uint16_t *>(dO), reinterpret_cast<const uint16_t *>(Q),
+        reinterpret_cast<const uint16_t *>(K), reinterpret_cast<const uint16_t *>(V),
+        reinterpret_cast<const uint16_t *>(O), LSE, reinterpret_cast<uint16_t *>(dQ),
+        reinterpret_cast<uint16_t *>(dK), reinterpret_cast<uint16_t *>(dV), workspace));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int H,
+                 int N, int d, float scale, int causal, const uint8_t *blockmask, void *stream)
+{
+    return fwd_common<uint16_t>(static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
+                                static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), LSE,
+                                B, H, N, d, scale, causal, blockmask, stream, false);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
+{
+    if (B <= 0 || H <= 0 || N <= 0)
+        return 0;
+    return fa::bwd_workspace_layout(B, H, N, d).bytes;
+}
+
+fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V, const void *O,
+                 const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int N, int d,
+                 float scale, int causal, const uint8_t *blockmask, void *workspace,
+                 size_t workspace_bytes, void *stream)
+{
+    return bwd_common<uint16_t>(
+        static_cast<const uint16_t *>(dO), static_cast<const uint16_t *>(Q),
+        static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
+        static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
+        static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
+        blockmask, workspace, workspace_bytes, stream, false);
+}
+
+fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE, int B,
+                     int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                     void *stream)
+{
+    return fwd_common<float>(Q, K, V, O, LSE, B, H, N, d, scale, causal, blockmask, stream, true);
+}
+
+fa_status fa_bwd_f32(const float *dO, const float *Q, const float *K, const float *V,
+                     const float *O, const float *LSE, float *dQ, float *dK, float *dV, int B,
+                     int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    return bwd_common<float>(dO, Q, K, V, O, LSE, dQ, dK, dV, B, H, N, d, scale, causal,
+                             blockmask, workspace, workspace_bytes, stream, true);
+}
+
+const char *fa_status_str(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *fa_last_hip_error(void)
+{
+    return g_last_hip_error;
+}
+
+const char *fa_version(void)
+{
+    return "fa-gfx950 0.1.0";
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Shared device-side definitions of the gfx950 attention kernels.
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64),
+// measured on gfx950 with an in-bounds probe:
+//   A (32 x 16, rows m, depth k): lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   B (16 x 32, depth k, cols n): lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   C (32 x 32):                   lane l, register r holds
+//                                  C[8 * (r / 4) + 4 * (l / 32) + (r % 4)][l % 32]
+// The contraction index k may be permuted freely as long as A and B use the
+// same permutation; the kernels use this to feed an accumulator (C layout)
+// straight back in as a B operand: registers 8h..8h+7 of a C tile become the
+// 16-deep k-slice h, with slot s of lane half g standing for row
+//   16 h + 8 (s / 4) + 4 g + (s % 4)
+// of the C tile.
+//
+// LDS transpose read (ds_read_b64_tr_b16), measured on gfx950: within each
+// group of 16 lanes, lane i receives element (i % 4) of the 8-byte rows
+// addressed by lanes 4t + i / 4, t = 0..3. Pointing lane 4t + u of a group at
+// row key_t, columns c0 + 4u .. c0 + 4u + 3 of a row-major tile gives lane i
+// the four values tile[key_t][c0 + i], t = 0..3: a column slice, i.e. the
+// transposed operand, without a transposing copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaskBlock = 128;
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight consecutive bf16 values from LDS (16-byte aligned address).
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t *p)
+{
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Two transpose reads (4 + 4 values) forming one 8-slot MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint16_t *p0, const uint16_t *p1)
+{
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Registers 8h..8h+7 of an fp32 accumulator tile, rounded to bf16 (RNE).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const f32x16 &c, int h)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        r[i] = (__bf16)c[8 * h + i];
+    return r;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float exp2_fast(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float lane_swap32(float x)
+{
+    return __shfl_xor(x, 32, kWave);
+}
+
+// Maps a launched workgroup to a work item so that each XCD (workgroups are
+// dealt to the XCDs round-robin) receives one contiguous range of the work
+// list: items of one head then run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_work_item(int per_xcd)
+{
+    const int b = blockIdx.x;
+    return (b % kXcds) * per_xcd + (b / kXcds);
+}
+
+}  // namespace fa

@@ -1,0 +1,42 @@
+// Host-side interface between the C ABI layer (fa_api.cpp) and the kernel
+// translation units. Arguments reaching these launchers are already
+// validated: non-empty shapes, supported head dimension, aligned pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct Problem {
+    int B, H, N, d;
+    float scale;
+    int causal;
+    const uint8_t *mask;  // device pointer or nullptr
+    hipStream_t stream;
+};
+
+// Scratch layout of the backward (offsets in bytes from the workspace base).
+struct BwdWorkspace {
+    size_t delta_off;  // float [B*H][N]: D_i = rowsum(dO o O)
+    size_t lse2_off;   // float [B*H][N]: LSE_i * log2(e)
+    size_t bytes;      // total
+};
+BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d);
+
+// Each launcher enqueues its kernels on p.stream and returns the
+// hipGetLastError() status of the launches.
+hipError_t launch_fwd_bf16(const Problem &p, const uint16_t *Q, const uint16_t *K,
+                           const uint16_t *V, uint16_t *O, float *LSE);
+hipError_t launch_bwd_bf16(const Problem &p, const uint16_t *dO, const uint16_t *Q,
+                           const uint16_t *K, const uint16_t *V, const uint16_t *O,
+                           const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
+                           void *workspace);
+hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
+                          float *O, float *LSE);
+hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,
+                          const float *V, const float *O, const float *LSE, float *dQ,
+                          float *dK, float *dV, void *workspace);
+
+}  // namespace fa

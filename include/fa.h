@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact IO-aware attention library.
+ *
+ * The operation is exact scaled-dot-product attention, computed tile by tile
+ * with an online softmax so that the N x N score and probability matrices
+ * never reach device memory:
+ *
+ *   S = scale * Q K^T, masked;  P = softmax(S) row by row;  O = P V
+ *
+ * Definitions followed:
+ *   - S, P, O: mstx.cn/posts/485 §二.1 "标准 Attention 的计算"; the 1/sqrt(d)
+ *     scale as written in nanhubrain.csdn.net §二 "反向传播的代价".
+ *   - tiling and the online max / exp-sum rescaling across key/value blocks:
+ *     mstx.cn/posts/485 §三.1 "Tiling" and §三.2 "Online Softmax";
+ *     lukebest.github.io FlashAttention, "算法要点".
+ *   - one fused kernel QK^T -> softmax (+mask) -> PV:
+ *     lukebest.github.io FlashAttention, "Kernel fusion".
+ *   - backward by recomputation from Q, K, V and the saved row statistics:
+ *     lukebest.github.io FlashAttention, "反向：重算而非存储";
+ *     mstx.cn/posts/485 §三.3 "重计算".
+ *   - causal mask P_ij = 0 for j > i (top-left aligned, diagonal kept):
+ *     nanhubrain.csdn.net §三 "因果掩码下的锯齿形调度".
+ *   - fixed block-sparse mask whose zero blocks are skipped:
+ *     lukebest.github.io FlashAttention, "Block-Sparse FlashAttention".
+ *
+ * Common argument rules (all entry points):
+ *   - Q, K, V, O, dO, dQ, dK, dV are DEVICE pointers to contiguous
+ *     [B][H][N][d] tensors, d fastest, 16-byte aligned. In the bf16 entry
+ *     points each element is a bf16 bit pattern (uint16); in the _f32 entry
+ *     points each element is an IEEE float.
+ *   - LSE is a DEVICE pointer to a contiguous [B][H][N] float tensor holding
+ *     the natural-log log-sum-exp of each row of S: LSE_i = ln sum_j exp(S_ij).
+ *     A row with no visible key gets O_i = 0 and LSE_i = -inf and contributes
+ *     no gradient.
+ *   - blockmask is NULL (dense) or a DEVICE pointer to uint8
+ *     [ceil(N/128)][ceil(N/128)], row-major, nonzero = keep the 128 x 128
+ *     block of (query block, key block). One mask serves every (b, h); it is
+ *     combined with the causal mask by AND.
+ *   - B, H, N >= 0 (any zero means an empty problem: FA_OK, nothing done);
+ *     d in {64, 128}; scale finite and > 0; causal is 0 or 1.
+ *   - stream is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously on it; argument checks happen synchronously, before any
+ *     HIP call, and a failed check enqueues nothing.
+ *   - Ownership: the caller owns every buffer. The library allocates and
+ *     frees no device or host memory; backward scratch is passed in as
+ *     `workspace`.
+ *   - Errors are returned as fa_status; no exception crosses the ABI. After
+ *     FA_ERR_HIP, fa_last_hip_error() describes the failure (thread-local).
+ *   - Entry points keep no state between calls and may be called from
+ *     several host threads on different streams.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,     /* B, H or N negative, or sizes overflow */
+    FA_ERR_HEADDIM = 3,   /* d not supported */
+    FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+    FA_ERR_SCALE = 5,     /* scale not finite or not > 0, or causal not 0/1 */
+    FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_bwd_workspace_bytes */
+    FA_ERR_HIP = 7        /* a HIP call failed; see fa_last_hip_error() */
+} fa_status;
+
+#define FA_MASK_BLOCK 128
+
+/* Forward, bf16 storage, fp32 softmax statistics and accumulation.
+ * Reads Q, K, V (and blockmask); writes O (bf16) and LSE (float). */
+fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const uint8_t *blockmask, void *stream);
+
+/* Bytes of device scratch fa_bwd / fa_bwd_f32 need for this shape
+ * (0 for an empty problem). The buffer needs no initialisation. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward, bf16 storage. Given the forward's O and LSE and dO = dL/dO,
+ * writes dQ, dK, dV (bf16) for the loss L, scale being a constant.
+ * Reads dO, Q, K, V, O, LSE (and blockmask); workspace is device scratch of
+ * at least fa_bwd_workspace_bytes(B, H, N, d) bytes, 256-byte aligned. */
+fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V,
+                 const void *O, const float *LSE, void *dQ, void *dK, void *dV,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const uint8_t *blockmask, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* fp32 debug path: the same tiled online-softmax algorithm with every tensor
+ * in float and fp32 arithmetic throughout. Same argument rules. */
+fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const uint8_t *blockmask, void *stream);
+
+fa_status fa_bwd_f32(const float *dO, const float *Q, const float *K, const float *V,
+                     const float *O, const float *LSE, float *dQ, float *dK, float *dV,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const uint8_t *blockmask, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Static text for a status code. */
+const char *fa_status_str(fa_status s);
+
+/* Text of the last HIP failure seen by this host thread ("" if none). */
+const char *fa_last_hip_error(void);
+
+/* Library version string. */
+const char *fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H */

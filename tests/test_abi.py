@@ -1,0 +1,112 @@
+"""C-ABI boundary on the CPU: the library loads, exports every entry point
+that include/fa.h declares, and rejects bad arguments with status codes
+before any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_attention_amd as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "fa.h")
+
+# fake, 256-byte-aligned non-null addresses: never dereferenced, because every
+# call below fails validation before reaching HIP
+P = 0x100000
+MIS = 0x100008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED), names
+    lib = fa.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def _fwd(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H=1, N=128, d=64, scale=0.125, causal=0, mask=None)
+    a.update(kw)
+    return fa.lib().fa_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"],
+                           a["d"], a["scale"], a["causal"], a["mask"], None)
+
+
+def _bwd(**kw):
+    a = dict(dO=P, Q=P, K=P, V=P, O=P, LSE=P, dQ=P, dK=P, dV=P, B=1, H=1, N=128, d=64,
+             scale=0.125, causal=0, mask=None, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return fa.lib().fa_bwd(a["dO"], a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dQ"], a["dK"],
+                           a["dV"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                           a["mask"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", ["fwd", "fwd_f32"])
+def test_forward_validation(fn):
+    f = {"fwd": fa.lib().fa_fwd, "fwd_f32": fa.lib().fa_fwd_f32}[fn]
+
+    def call(**kw):
+        a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H=1, N=128, d=64, scale=0.125, causal=0)
+        a.update(kw)
+        return f(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["d"],
+                 a["scale"], a["causal"], None, None)
+
+    assert call(Q=None) == 1
+    assert call(LSE=None) == 1
+    assert call(N=-1) == 2
+    assert call(B=-3) == 2
+    assert call(d=96) == 3
+    assert call(d=0) == 3
+    assert call(O=MIS) == 4
+    assert call(scale=0.0) == 5
+    assert call(scale=-1.0) == 5
+    assert call(scale=float("nan")) == 5
+    assert call(scale=float("inf")) == 5
+    assert call(causal=2) == 5
+    assert call(N=1 << 30, d=128) == 2          # per-head slab exceeds 31 bits
+    # empty problems are valid no-ops and touch nothing (even with NULL pointers)
+    assert call(B=0, Q=None) == 0
+    assert call(H=0) == 0
+    assert call(N=0) == 0
+
+
+def test_backward_validation():
+    ws = fa.fa_bwd_workspace_bytes(1, 1, 128, 64)
+    assert ws > 0 and ws % 256 == 0
+    assert _bwd(dQ=None) == 1
+    assert _bwd(d=32) == 3
+    assert _bwd(dV=MIS) == 4
+    assert _bwd(scale=0.0) == 5
+    assert _bwd(ws=None) == 6
+    assert _bwd(wsb=ws - 1) == 6
+    assert _bwd(ws=P + 128, wsb=ws) == 6          # workspace must be 256-byte aligned
+    assert _bwd(B=0, dO=None) == 0
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 0, 64) == 0
+    # two fp32 vectors per row (D and LSE in base 2), each 256-byte padded
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * 2 * 16 * 8192 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 2 * 256
+
+
+def test_status_strings():
+    lib = fa.lib()
+    for s in range(8):
+        assert lib.fa_status_str(s)
+    assert lib.fa_last_hip_error() is not None
+    assert fa.version().startswith("fa-gfx950")
+
+
+def test_binding_raises_on_bad_status():
+    with pytest.raises(fa.FaError) as e:
+        fa._check(3)
+    assert "FA_ERR_HEADDIM" in str(e.value)
