@@ -1,0 +1,190 @@
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+fa_fwd, then the backward's three kernels (fa_bwd_prep, fa_bwd_dq,
+fa_bwd_dkdv, which together are fa_bwd). The default workload is the
+long-context causal configuration B=2, H=16, N=8192, d=128 (Q and K scaled
+by 2), bf16 storage, inputs resident in HBM before timing starts.
+
+Throughput uses the algorithmic FLOP count of the method: forward
+4*B*H*N^2*d, backward 2.5x that, both halved under the causal mask (and
+scaled by the kept-block fraction under a block mask). Per-kernel durations
+come from HIP events recorded on the stream the kernels run on.
+
+Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
+--cpu-heads H (heads of the CPU fp64 reference timed as the baseline; 0 skips).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "attention fwd+bwd TFLOP/s and % of MFMA bf16 peak at N=8192, d=128, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    return ap.parse_args()
+
+
+def flop_counts(cfg, mask):
+    """Algorithmic FLOPs of one forward and of one backward."""
+    fwd = 4.0 * cfg.B * cfg.H * cfg.N ** 2 * cfg.d
+    if cfg.causal:
+        fwd *= 0.5
+    if mask is not None:
+        fwd *= float(mask.mean())
+    return fwd, 2.5 * fwd
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
+              "path here is a single-GPU kernel library and has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_attention_amd as fa
+    import synthetic as syn
+
+    cfg = syn.CONFIGS[args.config]
+    if not cfg.has_bwd:
+        raise SystemExit(f"config {cfg.cfg_id} has no backward; pick 1, 2, 3 or 5")
+    q, k, v, do, mask = syn.config_inputs(cfg)
+    dev = torch.device("cuda:0")
+
+    def t(x):
+        return torch.from_numpy(x).to(dev).to(torch.bfloat16)
+
+    Q, K, V, dO = t(q), t(k), t(v), t(do)
+    M = None if mask is None else torch.from_numpy(mask).to(dev)
+    O = torch.empty_like(Q)
+    LSE = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    ws = fa.new_workspace(cfg.B, cfg.H, cfg.N, cfg.d, dev)
+    scale, causal = cfg.scale, cfg.causal
+
+    names = ["fwd", "bwd_prep", "bwd_dq", "bwd_dkdv"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        fa.fa_fwd(Q, K, V, O, LSE, scale, causal=causal, blockmask=M)
+        if evs is not None:
+            evs[1].record()
+        fa.fa_bwd_prep(dO, O, LSE, ws)
+        if evs is not None:
+            evs[2].record()
+        fa.fa_bwd_dq(dO, Q, K, V, dQ, scale, ws, causal=causal, blockmask=M)
+        if evs is not None:
+            evs[3].record()
+        fa.fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, ws, causal=causal, blockmask=M)
+        if evs is not None:
+            evs[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dur = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            dur[n] += ev[j].elapsed_time(ev[j + 1]) * 1e-3  # seconds
+    avg = {n: dur[n] / args.steps for n in names}
+
+    fwd_flops, bwd_flops = flop_counts(cfg, mask)
+    step_s = wall / args.steps
+    value = (fwd_flops + bwd_flops) / step_s / 1e12
+    fwd_s = avg["fwd"]
+    bwd_s = avg["bwd_prep"] + avg["bwd_dq"] + avg["bwd_dkdv"]
+
+    # algorithmic work per launch of each kernel: the forward's two
+    # contractions; dK/dV's four (S and dP rebuilt, dV, dK); dQ's one
+    # (its S and dP rebuild is extra work of this split); prep moves bytes
+    E = cfg.B * cfg.H * cfg.N * cfg.d
+    rows = cfg.B * cfg.H * cfg.N
+    kernel_flops = {"fwd": fwd_flops, "bwd_dkdv": 0.8 * bwd_flops, "bwd_dq": 0.2 * bwd_flops,
+                    "bwd_prep": 0.0}
+    kernel_bytes = {"fwd": 4 * E * 2 + rows * 4, "bwd_prep": 2 * E * 2 + rows * 4 + 2 * rows * 4,
+                    "bwd_dq": 4 * E * 2 + 2 * rows * 4 + E * 2,
+                    "bwd_dkdv": 4 * E * 2 + 2 * rows * 4 + 2 * E * 2}
+    dominant = max(names, key=lambda n: avg[n])
+    ach = kernel_flops[dominant] / avg[dominant] / 1e12
+    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_bytes": kernel_bytes[dominant]}
+
+    kernels = {n: {"avg_us": round(avg[n] * 1e6, 2),
+                   "tflops": round(kernel_flops[n] / avg[n] / 1e12, 2) if kernel_flops[n] else None,
+                   "gbs": round(kernel_bytes[n] / avg[n] / 1e9, 1)} for n in names}
+
+    cpu = None
+    if args.cpu_heads > 0:
+        import oracle
+        nh = min(args.cpu_heads, cfg.B * cfg.H)
+        sl = (slice(0, 1), slice(0, nh))
+        t1 = time.perf_counter()
+        oracle.attention(q[sl], k[sl], v[sl], scale, causal=causal, blockmask=mask, do=do[sl])
+        cpu_s = time.perf_counter() - t1
+        head_flops = (fwd_flops + bwd_flops) / (cfg.B * cfg.H)
+        cpu = {"value": round(nh * head_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{nh} of {cfg.B * cfg.H} heads of the same workload, fwd+bwd, "
+                         f"fp64, {cpu_s:.1f} s"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + " attention fwd+bwd", "B": cfg.B, "H": cfg.H,
+                   "N": cfg.N, "d": cfg.d, "causal": cfg.causal,
+                   "block_sparse": mask is not None, "qk_mult": cfg.qk_mult,
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_s * 1e3, 4), "tflops": round(fwd_flops / fwd_s / 1e12, 2),
+                "frac_of_peak": round(fwd_flops / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_s * 1e3, 4), "tflops": round(bwd_flops / bwd_s / 1e12, 2),
+                "frac_of_peak": round(bwd_flops / bwd_s / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

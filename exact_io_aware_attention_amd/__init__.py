@@ -51,6 +51,13 @@ _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                         _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
 _lib.fa_bwd_f32.restype = _i
 _lib.fa_bwd_f32.argtypes = _lib.fa_bwd.argtypes
+_lib.fa_bwd_prep.restype = _i
+_lib.fa_bwd_prep.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.fa_bwd_dq.restype = _i
+_lib.fa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.fa_bwd_dkdv.restype = _i
+_lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                             _sz, _vp]
 _lib.fa_bwd_workspace_bytes.restype = _sz
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.fa_status_str.restype = ctypes.c_char_p
@@ -61,8 +68,9 @@ _lib.fa_version.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 
 # Symbols declared in include/fa.h (checked by the ABI test).
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_workspace_bytes",
-            "fa_status_str", "fa_last_hip_error", "fa_version")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_f32",
+            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_status_str", "fa_last_hip_error",
+            "fa_version")
 
 
 class FaError(RuntimeError):
@@ -187,3 +195,43 @@ def fa_bwd_f32(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False, blockmask=N
     import torch
     _bwd(_lib.fa_bwd_f32, torch.float32, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal,
          blockmask, workspace, stream)
+
+
+def fa_bwd_prep(dO, O, LSE, workspace, stream=None):
+    """Backward phase 1: D and LSE*log2(e) into the workspace."""
+    shape = _shape(dO)
+    _require((dO, O), torch.bfloat16, shape)
+    _require_lse(LSE, shape)
+    B, H, N, d = shape
+    _check(_lib.fa_bwd_prep(_ptr(dO), _ptr(O), _ptr(LSE), B, H, N, d, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+
+
+def fa_bwd_dq(dO, Q, K, V, dQ, scale, workspace, causal=False, blockmask=None, stream=None):
+    """Backward phase 2: dQ (needs fa_bwd_prep's workspace)."""
+    shape = _shape(Q)
+    _require((dO, Q, K, V, dQ), torch.bfloat16, shape)
+    _require_mask(blockmask, shape[2])
+    B, H, N, d = shape
+    _check(_lib.fa_bwd_dq(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(dQ), B, H, N, d,
+                          float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+
+
+def fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, workspace, causal=False, blockmask=None,
+                stream=None):
+    """Backward phase 3: dK and dV (needs fa_bwd_prep's workspace)."""
+    shape = _shape(Q)
+    _require((dO, Q, K, V, dK, dV), torch.bfloat16, shape)
+    _require_mask(blockmask, shape[2])
+    B, H, N, d = shape
+    _check(_lib.fa_bwd_dkdv(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(dK), _ptr(dV), B, H, N,
+                            d, float(scale), int(bool(causal)), _ptr(blockmask),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream_ptr(stream)))
+
+
+def new_workspace(B, H, N, d, device="cuda"):
+    """A device buffer of fa_bwd_workspace_bytes (torch allocates it)."""
+    return torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
+                       device=device)

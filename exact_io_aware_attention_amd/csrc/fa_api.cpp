@@ -104,6 +104,8 @@ fa_status fwd_common(const T *Q, const T *K, const T *V, T *O, float *LSE, int B
                                           reinterpret_cast<uint16_t *>(O), LSE));
 }
 
+fa_status check_workspace(int B, int H, int N, int d, const void *workspace, size_t bytes);
+
 template <typename T>
 fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O,
                      const float *LSE, T *dQ, T *dK, T *dV, int B, int H, int N, int d,
@@ -119,10 +121,9 @@ fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O
     st = check_ptrs({dO, Q, K, V, O, LSE, dQ, dK, dV});
     if (st != FA_OK)
         return st;
-    const fa::BwdWorkspace L = fa::bwd_workspace_layout(B, H, N, d);
-    if (workspace == nullptr || workspace_bytes < L.bytes ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return FA_ERR_WORKSPACE;
+    st = check_workspace(B, H, N, d, workspace, workspace_bytes);
+    if (st != FA_OK)
+        return st;
     const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
     if (f32)
         return hip_status(fa::launch_bwd_f32(
@@ -135,6 +136,29 @@ fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O
         reinterpret_cast<const uint16_t *>(K), reinterpret_cast<const uint16_t *>(V),
         reinterpret_cast<const uint16_t *>(O), LSE, reinterpret_cast<uint16_t *>(dQ),
         reinterpret_cast<uint16_t *>(dK), reinterpret_cast<uint16_t *>(dV), workspace));
+}
+
+fa_status check_workspace(int B, int H, int N, int d, const void *workspace, size_t bytes)
+{
+    const fa::BwdWorkspace L = fa::bwd_workspace_layout(B, H, N, d);
+    if (workspace == nullptr || bytes < L.bytes ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
+// Validation shared by the backward phase entry points; *empty as above.
+fa_status bwd_phase_checks(int B, int H, int N, int d, float scale, int causal,
+                           std::initializer_list<const void *> ptrs, const void *workspace,
+                           size_t workspace_bytes, bool *empty)
+{
+    fa_status st = check_common(B, H, N, d, scale, causal, empty);
+    if (st != FA_OK || *empty)
+        return st;
+    st = check_ptrs(ptrs);
+    if (st != FA_OK)
+        return st;
+    return check_workspace(B, H, N, d, workspace, workspace_bytes);
 }
 
 }  // namespace
@@ -167,6 +191,52 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V, co
         static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
         blockmask, workspace, workspace_bytes, stream, false);
+}
+
+fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE, int B, int H, int N, int d,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    fa_status st = bwd_phase_checks(B, H, N, d, 1.f, 0, {dO, O, LSE}, workspace, workspace_bytes,
+                                    &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const fa::Problem p = make_problem(B, H, N, d, 1.f, 0, nullptr, stream);
+    return hip_status(fa::launch_bwd_prep_bf16(p, static_cast<const uint16_t *>(dO),
+                                               static_cast<const uint16_t *>(O), LSE, workspace));
+}
+
+fa_status fa_bwd_dq(const void *dO, const void *Q, const void *K, const void *V, void *dQ, int B,
+                    int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                    const void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    fa_status st = bwd_phase_checks(B, H, N, d, scale, causal, {dO, Q, K, V, dQ}, workspace,
+                                    workspace_bytes, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    return hip_status(fa::launch_bwd_dq_bf16(
+        p, static_cast<const uint16_t *>(dO), static_cast<const uint16_t *>(Q),
+        static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
+        static_cast<uint16_t *>(dQ), workspace));
+}
+
+fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *V, void *dK,
+                      void *dV, int B, int H, int N, int d, float scale, int causal,
+                      const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    bool empty = false;
+    fa_status st = bwd_phase_checks(B, H, N, d, scale, causal, {dO, Q, K, V, dK, dV}, workspace,
+                                    workspace_bytes, &empty);
+    if (st != FA_OK || empty)
+        return st;
+    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    return hip_status(fa::launch_bwd_dkdv_bf16(
+        p, static_cast<const uint16_t *>(dO), static_cast<const uint16_t *>(Q),
+        static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
+        static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), workspace));
 }
 
 fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE, int B,

@@ -486,64 +486,84 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
-hipError_t bwd_t(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
+struct BwdPtrs {
+    const uint16_t *dO, *Q, *K, *V, *O;
+    const float *LSE;
+    uint16_t *dQ, *dK, *dV;
+    float *delta, *lse2;
+};
+
+BwdPtrs bwd_ptrs(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
                  const uint16_t *V, const uint16_t *O, const float *LSE, uint16_t *dQ,
                  uint16_t *dK, uint16_t *dV, void *ws)
 {
     const BwdWorkspace L = bwd_workspace_layout(pr.B, pr.H, pr.N, pr.d);
-    float *delta = reinterpret_cast<float *>(static_cast<char *>(ws) + L.delta_off);
-    float *lse2 = reinterpret_cast<float *>(static_cast<char *>(ws) + L.lse2_off);
+    BwdPtrs b;
+    b.dO = dO; b.Q = Q; b.K = K; b.V = V; b.O = O; b.LSE = LSE;
+    b.dQ = dQ; b.dK = dK; b.dV = dV;
+    b.delta = reinterpret_cast<float *>(static_cast<char *>(ws) + L.delta_off);
+    b.lse2 = reinterpret_cast<float *>(static_cast<char *>(ws) + L.lse2_off);
+    return b;
+}
+
+template <int D>
+hipError_t prep_d(const Problem &pr, const BwdPtrs &b)
+{
     const long rows = (long)pr.B * pr.H * pr.N;
-    const int nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
-    const float c = pr.scale * kLog2e;
+    const long threads = rows * (D / 8);
+    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       pr.stream, b.dO, b.O, b.LSE, b.delta, b.lse2, rows);
+    return hipGetLastError();
+}
 
-    const long pre_threads = rows * (D / 8);
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0,
-                       pr.stream, dO, O, LSE, delta, lse2, rows);
-
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
+{
     DqParams qp{};
-    qp.dO = dO; qp.Q = Q; qp.K = K; qp.V = V;
-    qp.delta = delta; qp.lse2 = lse2; qp.dQ = dQ; qp.mask = pr.mask;
+    qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
+    qp.delta = b.delta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
     qp.nqb = (pr.N + 127) / 128;
     qp.nkt = (pr.N + 63) / 64;
-    qp.nmb = nmb;
+    qp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     qp.items = pr.B * pr.H * qp.nqb;
     qp.per_xcd = (qp.items + kXcds - 1) / kXcds;
-    qp.c = c;
+    qp.c = pr.scale * kLog2e;
     qp.scale = pr.scale;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(256), 0,
                        pr.stream, qp);
+    return hipGetLastError();
+}
 
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
+{
     DkvParams kp{};
-    kp.dO = dO; kp.Q = Q; kp.K = K; kp.V = V;
-    kp.delta = delta; kp.lse2 = lse2; kp.dK = dK; kp.dV = dV; kp.mask = pr.mask;
+    kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
+    kp.delta = b.delta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
     kp.nkb = (pr.N + 127) / 128;
     kp.nqt = (pr.N + 63) / 64;
-    kp.nmb = nmb;
+    kp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     kp.items = pr.B * pr.H * kp.nkb;
     kp.per_xcd = (kp.items + kXcds - 1) / kXcds;
-    kp.c = c;
+    kp.c = pr.scale * kLog2e;
     kp.scale = pr.scale;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(256), 0,
                        pr.stream, kp);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t bwd_d(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
-                 const uint16_t *V, const uint16_t *O, const float *LSE, uint16_t *dQ,
-                 uint16_t *dK, uint16_t *dV, void *ws)
-{
-    const bool sparse = pr.mask != nullptr;
-    if (pr.causal)
-        return sparse ? bwd_t<D, true, true>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, ws)
-                      : bwd_t<D, true, false>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
-    return sparse ? bwd_t<D, false, true>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, ws)
-                  : bwd_t<D, false, false>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
-}
+// Dispatch on (d, causal, sparse) for a kernel template taking <D, CAUSAL, SPARSE>.
+#define FA_DISPATCH(FN, pr, b)                                                              \
+    ((pr).d == 64 ? ((pr).causal ? ((pr).mask ? FN<64, true, true>(pr, b)                  \
+                                              : FN<64, true, false>(pr, b))                \
+                                 : ((pr).mask ? FN<64, false, true>(pr, b)                 \
+                                              : FN<64, false, false>(pr, b)))              \
+                  : ((pr).causal ? ((pr).mask ? FN<128, true, true>(pr, b)                 \
+                                              : FN<128, true, false>(pr, b))               \
+                                 : ((pr).mask ? FN<128, false, true>(pr, b)                \
+                                              : FN<128, false, false>(pr, b))))
 
 }  // namespace
 
@@ -559,13 +579,44 @@ BwdWorkspace bwd_workspace_layout(int B, int H, int N, int d)
     return w;
 }
 
+hipError_t launch_bwd_prep_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *O,
+                                const float *LSE, void *workspace)
+{
+    const BwdPtrs b = bwd_ptrs(pr, dO, nullptr, nullptr, nullptr, O, LSE, nullptr, nullptr,
+                               nullptr, workspace);
+    return pr.d == 64 ? prep_d<64>(pr, b) : prep_d<128>(pr, b);
+}
+
+hipError_t launch_bwd_dq_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
+                              const uint16_t *K, const uint16_t *V, uint16_t *dQ,
+                              const void *workspace)
+{
+    const BwdPtrs b = bwd_ptrs(pr, dO, Q, K, V, nullptr, nullptr, dQ, nullptr, nullptr,
+                               const_cast<void *>(workspace));
+    return FA_DISPATCH(dq_t, pr, b);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
+                                const uint16_t *K, const uint16_t *V, uint16_t *dK,
+                                uint16_t *dV, const void *workspace)
+{
+    const BwdPtrs b = bwd_ptrs(pr, dO, Q, K, V, nullptr, nullptr, nullptr, dK, dV,
+                               const_cast<void *>(workspace));
+    return FA_DISPATCH(dkdv_t, pr, b);
+}
+
 hipError_t launch_bwd_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
                            const uint16_t *K, const uint16_t *V, const uint16_t *O,
                            const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                            void *workspace)
 {
-    return pr.d == 64 ? bwd_d<64>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, workspace)
-                      : bwd_d<128>(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, workspace);
+    hipError_t e = launch_bwd_prep_bf16(pr, dO, O, LSE, workspace);
+    if (e != hipSuccess)
+        return e;
+    e = launch_bwd_dq_bf16(pr, dO, Q, K, V, dQ, workspace);
+    if (e != hipSuccess)
+        return e;
+    return launch_bwd_dkdv_bf16(pr, dO, Q, K, V, dK, dV, workspace);
 }
 
 }  // namespace fa

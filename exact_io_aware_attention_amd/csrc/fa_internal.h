@@ -33,6 +33,17 @@ hipError_t launch_bwd_bf16(const Problem &p, const uint16_t *dO, const uint16_t 
                            const uint16_t *K, const uint16_t *V, const uint16_t *O,
                            const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                            void *workspace);
+// The three phases of launch_bwd_bf16 (each one kernel), in the order they
+// must run on one workspace: prep writes D and LSE*log2(e) that dq and dkdv
+// read; dq and dkdv are independent of each other.
+hipError_t launch_bwd_prep_bf16(const Problem &p, const uint16_t *dO, const uint16_t *O,
+                                const float *LSE, void *workspace);
+hipError_t launch_bwd_dq_bf16(const Problem &p, const uint16_t *dO, const uint16_t *Q,
+                              const uint16_t *K, const uint16_t *V, uint16_t *dQ,
+                              const void *workspace);
+hipError_t launch_bwd_dkdv_bf16(const Problem &p, const uint16_t *dO, const uint16_t *Q,
+                                const uint16_t *K, const uint16_t *V, uint16_t *dK,
+                                uint16_t *dV, const void *workspace);
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE);
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,

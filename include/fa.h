@@ -92,6 +92,26 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V,
                  const uint8_t *blockmask, void *workspace, size_t workspace_bytes,
                  void *stream);
 
+/* The three phases of fa_bwd, one kernel each, for callers that schedule them
+ * themselves (e.g. fa_bwd_dq and fa_bwd_dkdv on two streams) or time them.
+ * fa_bwd_prep must complete on a workspace before fa_bwd_dq / fa_bwd_dkdv
+ * read it; those two are independent of each other. Arguments as in fa_bwd.
+ *   fa_bwd_prep: reads dO, O, LSE; writes D_i = sum_k dO_ik O_ik and
+ *                LSE_i * log2(e) into the workspace.
+ *   fa_bwd_dq:   reads dO, Q, K, V and the workspace; writes dQ.
+ *   fa_bwd_dkdv: reads dO, Q, K, V and the workspace; writes dK and dV. */
+fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE,
+                      int B, int H, int N, int d,
+                      void *workspace, size_t workspace_bytes, void *stream);
+fa_status fa_bwd_dq(const void *dO, const void *Q, const void *K, const void *V, void *dQ,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
+                    void *stream);
+fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *V,
+                      void *dK, void *dV, int B, int H, int N, int d, float scale, int causal,
+                      const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* fp32 debug path: the same tiled online-softmax algorithm with every tensor
  * in float and fp32 arithmetic throughout. Same argument rules. */
 fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE,
