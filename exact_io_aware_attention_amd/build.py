@@ -23,6 +23,9 @@ COMMON_FLAGS = [
     "-Wall", "-Wextra", "-Wno-unused-parameter",
     # no packed-fp32 (v_pk_*_f32) instructions in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax rescale and the dS / P packing
+    # read and write them with vector ALU ops, which cannot address AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

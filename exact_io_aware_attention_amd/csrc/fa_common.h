@@ -85,6 +85,21 @@ __device__ __forceinline__ float lane_swap32(float x)
     return __shfl_xor(x, 32, kWave);
 }
 
+// Asks the scheduler to interleave, within the current basic block, NM
+// groups of {1 MFMA, DSR LDS reads, NV vector ALU ops}, so that the vector
+// work of a wave issues in the shadow of its own matrix instructions.
+template <int NM, int DSR, int NV>
+__device__ __forceinline__ void sched_interleave()
+{
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if (DSR > 0)
+            __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);       // VALU
+    }
+}
+
 // Maps a launched workgroup to a work item so that each XCD (workgroups are
 // dealt to the XCDs round-robin) receives one contiguous range of the work
 // list: items of one head then run on one XCD and share its L2.

@@ -5,33 +5,56 @@
 // §三.1 "Tiling", §三.2 "Online Softmax").
 //
 // Work decomposition (a re-derivation for CDNA4, not the pages' A100 tiles):
-//   - one workgroup = 4 waves (one per SIMD) owns BR = 128*QB consecutive
-//     query rows of one (b, h); each wave owns 32*QB rows and keeps its Q
-//     rows in registers for the whole key loop, so O, m and l never leave
-//     registers (the key loop is the inner loop, the order the pages'
-//     sequence-parallel successor uses, lukebest.github.io "谱系");
-//   - K and V stream through LDS in 64-key tiles, double-buffered: the global
-//     loads of tile j+1 are in flight while tile j is computed;
+//   - a workgroup of 8 waves (two per SIMD) owns 256 consecutive query rows
+//     of one (b, h); each wave owns 32 rows and keeps its Q rows in
+//     registers for the whole key loop, so O, m and l never leave registers
+//     (the key loop is the inner loop, the order of the pages'
+//     sequence-parallel successor, lukebest.github.io "谱系");
+//   - K and V stream through LDS in 64-key tiles (K triple-, V
+//     double-buffered) by direct global->LDS loads, which need no staging
+//     registers; the loads of later tiles are in flight while one is
+//     computed, and one barrier per tile orders the buffers;
 //   - scores are computed transposed, S^T = K Q^T, so that each lane owns one
 //     query and row max / row sum are lane-local plus one exchange between
 //     the two 32-lane halves;
+//   - software pipeline at 32-key granularity: the MFMAs of S^T for the next
+//     32 keys are issued in the same basic blocks as the softmax and the
+//     P V MFMAs of the current 32 keys, so the matrix cores and the vector
+//     ALU work at the same time; the second wave of each SIMD covers what
+//     one wave's dependencies leave idle;
 //   - P^T goes back into the MFMA as the B operand of O^T = V^T P^T, the V^T
 //     operand coming from the row-major V tile by LDS transpose reads.
 //
-// Online softmax (mstx.cn/posts/485 §三.2 update rule), in base 2 with
-// c = scale * log2(e):
-//   m' = max(m, c * rowmax(S_tile)),  alpha = 2^(m - m'),
-//   p = 2^(c * s - m'),  l' = alpha * l + sum p,  O' = alpha * O + p V,
-// and O = O / l, LSE = (m + log2 l) * ln 2 at the end. A row that has seen
-// no visible key keeps m = -inf; exponents are then taken against 0 so that
-// no (-inf) - (-inf) arises, and such a row ends with O = 0, LSE = -inf.
+// LDS layouts (no padding; XOR swizzles of the 16-byte chunks of each row
+// keep the reads free of bank conflicts on the 64-bank LDS, which serves 16
+// lanes of a b128 read per cycle): K row r, chunk c is stored at chunk
+// c ^ (r % 16) for 256-byte rows (d = 128) or c ^ ((r / 2) % 8) for 128-byte
+// rows (d = 64), so the 16 rows of one b128 read cycle land in 16 different
+// bank groups; V row r, chunk c at c ^ 2 (r % 4) -- the four rows x 32 bytes
+// of one 16-lane transpose read cover 32 different banks.
+//
+// Online softmax (mstx.cn/posts/485 §三.2 update rule) in base 2, c = scale
+// * log2(e). Each row keeps a reference max m (the exponent offset of its
+// partial sums). For the next 32 keys with row max t = c * max_j s_j:
+//   - if t > m + 8 (or m = -inf): m' = t, O and l are multiplied by 2^(m - m')
+//     (the pages' rescaling step, taken only when the max grows enough);
+//   - else m' = m and the new weights 2^(c s - m) stay <= 2^8;
+//   - p = 2^(c s - m'),  l' = l + sum p,  O' = O + p V.
+// Both branches keep O = sum_j 2^(c s_j - m) V_j and l = sum_j 2^(c s_j - m)
+// for the current m, so O / l and LSE = (m + log2 l) ln 2 are exact; skipping
+// the rescale while the max moves by less than 2^8 saves the O multiply on
+// almost every step. A row that has seen no visible key keeps m = -inf and
+// takes exponents against 0, so no (-inf) - (-inf) arises; it ends with
+// O = 0, LSE = -inf.
 //
 // Masking: causal (key j visible to query i iff j <= i, nanhubrain.csdn.net
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
-// never loaded, and the per-element mask runs only on tiles that straddle the
-// diagonal or the end of the sequence; block-sparse (lukebest.github.io
-// "Block-Sparse FlashAttention") -- key tiles whose 128 x 128 mask block is
-// zero for every wave of the workgroup are skipped without being loaded.
+// never loaded, and the per-element mask runs only on 32-key steps that
+// straddle the diagonal or the end of the sequence; block-sparse
+// (lukebest.github.io "Block-Sparse FlashAttention") -- key tiles whose
+// 128 x 128 mask block is zero for every wave of the workgroup are skipped
+// without being loaded. Rows past the end of the sequence are loaded from
+// the last row (so every load stays in bounds) and always masked.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -51,22 +74,24 @@ struct FwdParams {
     float c;      // scale * log2(e)
 };
 
-template <int D, int QB, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdParams p)
+constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated without rescale
+
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
 {
-    constexpr int BR = 128 * QB;    // query rows per workgroup
-    constexpr int RW = 32 * QB;     // query rows per wave
+    constexpr int W = 8;            // waves
+    constexpr int RW = 32;          // query rows per wave
+    constexpr int BR = RW * W;      // query rows per workgroup
     constexpr int BC = 64;          // keys per LDS tile
-    constexpr int KSTR = D + 8;     // K tile row stride in elements (conflict-free b128 reads)
-    constexpr int VSTR = D + 16;    // V tile row stride in elements (conflict-free transpose reads)
     constexpr int KK = D / 16;      // depth steps of Q K^T
     constexpr int DB = D / 32;      // 32-row blocks of O^T
     constexpr int CPR = D / 8;      // 16-byte chunks per row
-    constexpr int RPI = 256 / CPR;  // rows per staging pass
-    constexpr int NI = BC / RPI;    // staging passes per tile
+    constexpr int TILE = BC * D;    // elements per K or V tile
+    constexpr int LPW = TILE * 2 / 1024 / W;  // 1 KB direct loads per wave per tile
+    static_assert(LPW >= 1, "tile too small for the direct-load layout");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * VSTR];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
@@ -76,6 +101,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdParams p)
     const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;  // causal: longest rows first
     const int q0 = qblk * BR;
     const int N = p.N;
+    const float c = p.c;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -83,6 +109,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdParams p)
     const int l32 = lane % 32;
     const int hi = lane / 32;
     const int wr0 = q0 + wave * RW;
+    const int row = wr0 + l32;
 
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t *Qh = p.Q + head;
@@ -90,27 +117,21 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdParams p)
     const uint16_t *Vh = p.V + head;
 
     // This wave's query rows as MFMA B operands (d-slices of 16).
-    bf16x8 qf[QB][KK];
+    bf16x8 qf[KK];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = wr0 + 32 * qb + l32;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            if (row < N)
-                qf[qb][kk] = *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi);
-            else
-                qf[qb][kk] = bf16x8{};
-        }
-    }
+    for (int kk = 0; kk < KK; ++kk)
+        qf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
+                         : bf16x8{};
 
     int t_end = p.nkt;
     if (CAUSAL)
         t_end = min(p.nkt, (q0 + BR - 1) / BC + 1);
 
-    // Block-sparse: the mask rows this workgroup and this wave fall in.
+    // Block-sparse: a key tile is loaded when any wave's mask row keeps it;
+    // a wave whose own mask row drops it masks the whole tile.
     const int mr_lo = q0 / kMaskBlock;
     const int mr_hi = min(q0 + BR - 1, N - 1) / kMaskBlock;
-    const int wmr = wr0 / kMaskBlock;
+    const int wmr = min(wr0, N - 1) / kMaskBlock;
     auto tile_needed = [&](int t) -> bool {
         if (!SPARSE)
             return true;
@@ -128,211 +149,253 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdParams p)
         return t;
     };
 
-    uint4 kst[NI], vst[NI];
-    auto load_tile = [&](int t) {
+    // Direct global->LDS loads: lane `lane` of 1 KB block b writes chunk
+    // `lane` of the block, i.e. row r = b * (64 / CPR) + lane / CPR, physical
+    // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ swz(r).
+    auto k_swz = [](int r) -> int { return CPR == 16 ? (r % 16) : ((r / 2) % 8); };
+    auto v_swz = [](int r) -> int { return 2 * (r % 4); };
+    auto issue_tile = [&](const uint16_t *src, uint16_t *dst, int t, bool is_k) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            const int key = t * BC + r;
-            if (key < N) {
-                kst[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)key * D + 8 * c);
-                vst[i] = *reinterpret_cast<const uint4 *>(Vh + (size_t)key * D + 8 * c);
-            } else {
-                kst[i] = uint4{0, 0, 0, 0};
-                vst[i] = uint4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < LPW; ++i) {
+            const int b = wave * LPW + i;
+            const int r = b * (64 / CPR) + lane / CPR;
+            const int lc = (lane % CPR) ^ (is_k ? k_swz(r) : v_swz(r));
+            const int key = min(t * BC + r, N - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(src + (size_t)key * D + 8 * lc),
+                (__attribute__((address_space(3))) void *)(dst + b * 512), 16, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto issue_k = [&](int t, int buf) { issue_tile(Kh, Ks[buf], t, true); };
+    auto issue_v = [&](int t, int buf) { issue_tile(Vh, Vs[buf], t, false); };
+
+    // K operand reads: row 32*h + l32 of the tile, logical chunk 2*kk + hi.
+    auto qk_half = [&](const uint16_t *kt, int h, f32x16 &s) {
+        s = f32x16{};
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            *reinterpret_cast<uint4 *>(&Ks[buf][r * KSTR + 8 * c]) = kst[i];
-            *reinterpret_cast<uint4 *>(&Vs[buf][r * VSTR + 8 * c]) = vst[i];
+        for (int kk = 0; kk < KK; ++kk) {
+            const int r = 32 * h + l32;
+            const int pc = (2 * kk + hi) ^ k_swz(r);
+            s = mfma32x32x16(lds_read_b128(kt + r * D + 8 * pc), qf[kk], s);
         }
     };
-
-    f32x16 o[QB][DB];
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            o[qb][db] = f32x16{};
-    }
-
-    // Transpose-read addressing of the V^T operand: lane 4t+u of each
-    // 16-lane group g points at key row 4*(g/2)+t, columns 16*(g%2)+4u.
+    // V^T operand (transpose reads): lane 4t+u of 16-lane group g points at
+    // key row 4*(g/2)+t, columns 32*db + 16*(g%2) + 4u, i.e. logical chunk
+    // 4*db + 2*(g%2) + u/2, element offset 4*(u%2) within it.
     const int g = lane / 16;
     const int sl = lane % 16;
-    const int v_key = 4 * (g / 2) + sl / 4;
-    const int v_col = 16 * (g % 2) + 4 * (sl % 4);
+    const int v_row = 4 * (g / 2) + sl / 4;
+    const int v_lc = 2 * (g % 2) + (sl % 4) / 2;
+    const int v_in = 4 * (sl % 2);
+    auto v_addr = [&](const uint16_t *vt, int r, int db) -> const uint16_t * {
+        const int pc = (4 * db + v_lc) ^ v_swz(r);
+        return vt + r * D + 8 * pc + v_in;
+    };
 
-    int t = next_tile(-1);
-    if (t < t_end) {
-        load_tile(t);
-        store_tile(0);
+    // Element mask of 32 keys starting at kbase: keys past the end of the
+    // sequence, keys above the diagonal (causal), or all of them when this
+    // wave's block-mask row drops the tile.
+    auto mask_half = [&](int kbase, f32x16 &s) {
+        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
+        const bool edge = (kbase + 32 > N) || (CAUSAL && kbase + 31 > wr0);
+        if (drop) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[r] = -INFINITY;
+        } else if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (key >= N || (CAUSAL && key > row))
+                    s[r] = -INFINITY;
+            }
+        }
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        o[db] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    const int t0 = next_tile(-1);
+    if (t0 >= t_end) {
+        // no visible key tile at all (fully masked rows): O = 0, LSE = -inf
+        if (row < N) {
+            uint16_t *Oh = p.O + head + (size_t)row * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * j + 4 * hi) = uint2{0, 0};
+            if (hi == 0)
+                p.LSE[(size_t)bh * N + row] = -INFINITY;
+        }
+        return;
     }
-    __syncthreads();
-    int buf = 0;
-    while (t < t_end) {
-        const int tn = next_tile(t);
-        if (tn < t_end)
-            load_tile(tn);
+    int t1 = next_tile(t0);
+    issue_k(t0, 0);
+    issue_v(t0, 0);
+    if (t1 < t_end)
+        issue_k(t1, 1);
+    __syncthreads();  // waits for the direct loads, then orders them
 
-        const int kbase = t * BC;
-        bool active = wr0 < N;
-        if (SPARSE)
-            active = active && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] != 0;
-        if (CAUSAL)
-            active = active && kbase <= wr0 + RW - 1;
-        if (active) {
-            const uint16_t *ks = Ks[buf];
-            const uint16_t *vs = Vs[buf];
-            f32x16 s[QB][2];
+    f32x16 s_cur;
+    qk_half(Ks[0], 0, s_cur);
+    mask_half(t0 * BC, s_cur);
+
+    int t = t0;
+    int j = 0;
+    int kb_cur = 0, kb_nxt = 1;  // K buffers of tiles j and j+1
+    while (t < t_end) {
+        const int tn = t1;                                   // tile j+1
+        const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
+        const int kb_nn = 3 - kb_cur - kb_nxt;               // K buffer of tile j+2
+        // K of tile j+2 replaces tile j-1's K; V of tile j+1 replaces tile
+        // j-1's V; both were last read before the previous barrier.
+        if (tnn < t_end)
+            issue_k(tnn, kb_nn);
+        if (tn < t_end)
+            issue_v(tn, (j + 1) & 1);
+
+        const uint16_t *vt = Vs[j & 1];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                s[qb][0] = f32x16{};
-                s[qb][1] = f32x16{};
+        for (int h = 0; h < 2; ++h) {
+            // S^T of the next 32 keys: the second half of this tile, then the
+            // first half of tile j+1 (on the last tile a stale buffer is read
+            // and the result unused). Its first half-depth runs beside the
+            // row max, its second beside the exponentials.
+            const uint16_t *kt = (h == 0 ? Ks[kb_cur] : Ks[kb_nxt]) + (32 * (h ^ 1) + l32) * D;
+            const int ksw = k_swz(32 * (h ^ 1) + l32);
+            f32x16 s_nxt = f32x16{};
+            bf16x8 kf[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK / 2; ++kk)
+                kf[kk] = lds_read_b128(kt + 8 * ((2 * kk + hi) ^ ksw));
+            float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                mx0 = fmaxf(mx0, s_cur[r]);
+                mx1 = fmaxf(mx1, s_cur[r + 1]);
             }
-            // S^T = K Q^T for two 32-key halves of the tile.
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 kf = lds_read_b128(ks + (32 * kb + l32) * KSTR + 16 * kk + 8 * hi);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        s[qb][kb] = mfma32x32x16(kf, qf[qb][kk], s[qb][kb]);
-                }
-            }
-            // Element mask: keys past the end of the sequence, and (causal)
-            // keys above the diagonal.
-            const bool need_mask = (kbase + BC > N) || (CAUSAL && kbase + BC - 1 > wr0);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int row = wr0 + 32 * qb + l32;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = kbase + 32 * kb + 8 * (r / 4) + 4 * hi + (r % 4);
-                            if (key >= N || (CAUSAL && key > row))
-                                s[qb][kb][r] = -INFINITY;
-                        }
-                }
-            }
-            // Online softmax update (base 2).
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        mx = fmaxf(mx, s[qb][kb][r]);
-                mx = fmaxf(mx, lane_swap32(mx));
-                const float mnew = fmaxf(m[qb], mx * p.c);
-                const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-                const float alpha = exp2_fast(m[qb] - mref);
-                m[qb] = mnew;
-                float lsum = l[qb] * alpha;
+            for (int kk = 0; kk < KK / 2; ++kk)
+                s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
+            float mx = fmaxf(mx0, mx1);
+            mx = fmaxf(mx, lane_swap32(mx)) * c;
+            sched_interleave<KK / 2, 0, 2>();
+            if (__any(mx > m + kRescaleSlack)) {
+                const float mnew = fmaxf(m, mx);
+                const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - mnew);
+                m = mnew;
+                l *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        o[qb][db][r] *= alpha;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float e = exp2_fast(fmaf(s[qb][kb][r], p.c, -mref));
-                        s[qb][kb][r] = e;
-                        lsum += e;
-                    }
-                l[qb] = lsum;
+                        o[db][r] *= alpha;
             }
-            // O^T += V^T P^T, 16 keys per MFMA.
+            const float mref = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kk = KK / 2; kk < KK; ++kk)
+                kf[kk] = lds_read_b128(kt + 8 * ((2 * kk + hi) ^ ksw));
+            bf16x8 vf[2][DB];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    bf16x8 pf[QB];
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r0 = 32 * h + 16 * hh + v_row;
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        pf[qb] = pack_bf16x8(s[qb][kb], hh);
-                    const uint16_t *vrow = vs + (32 * kb + 16 * hh + v_key) * VSTR + v_col;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 vf = lds_read_tr_pair(vrow + 32 * db, vrow + 8 * VSTR + 32 * db);
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            o[qb][db] = mfma32x32x16(vf, pf[qb], o[qb][db]);
-                    }
-                }
+                for (int db = 0; db < DB; ++db)
+                    vf[hh][db] = lds_read_tr_pair(v_addr(vt, r0, db), v_addr(vt, r0 + 8, db));
             }
-        }
+            float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) {
+                const float e0 = exp2_fast(fmaf(s_cur[r], c, -mref));
+                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, -mref));
+                s_cur[r] = e0;
+                s_cur[r + 1] = e1;
+                ls0 += e0;
+                ls1 += e1;
+            }
+#pragma unroll
+            for (int kk = KK / 2; kk < KK; ++kk)
+                s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
+            // O^T += V^T P^T over these 32 keys, 16 keys per MFMA.
+            const bf16x8 p0 = pack_bf16x8(s_cur, 0);
+#pragma unroll
+            for (int r = 8; r < 16; r += 2) {
+                const float e0 = exp2_fast(fmaf(s_cur[r], c, -mref));
+                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, -mref));
+                s_cur[r] = e0;
+                s_cur[r + 1] = e1;
+                ls0 += e0;
+                ls1 += e1;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
+            l += ls0 + ls1;
+            const bf16x8 p1 = pack_bf16x8(s_cur, 1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
+            sched_interleave<KK / 2 + 2 * DB, 2, 4>();
 
-        if (tn < t_end)
-            store_tile(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+            if (h == 0)
+                mask_half(t * BC + 32, s_nxt);
+            else if (tn < t_end)
+                mask_half(tn * BC, s_nxt);
+            s_cur = s_nxt;
+        }
+        __syncthreads();  // tile j+1's V and tile j+2's K have landed
         t = tn;
+        t1 = tnn;
+        ++j;
+        kb_cur = kb_nxt;
+        kb_nxt = kb_nn;
     }
 
     // Epilogue: O = O^T / l (transposed back per lane), LSE in natural log.
-    uint16_t *Oh = p.O + head;
-    float *Lh = p.LSE + (size_t)bh * N;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lt = l[qb] + lane_swap32(l[qb]);
-        const int row = wr0 + 32 * qb + l32;
+    const float lt = l + lane_swap32(l);
+    if (row < N) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        if (row < N) {
+        uint16_t *Oh = p.O + head + (size_t)row * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int dcol = 32 * db + 8 * j + 4 * hi;
-                    uint2 pk;
-                    pk.x = (uint32_t)f32_to_bf16_bits(o[qb][db][4 * j + 0] * inv) |
-                           ((uint32_t)f32_to_bf16_bits(o[qb][db][4 * j + 1] * inv) << 16);
-                    pk.y = (uint32_t)f32_to_bf16_bits(o[qb][db][4 * j + 2] * inv) |
-                           ((uint32_t)f32_to_bf16_bits(o[qb][db][4 * j + 3] * inv) << 16);
-                    *reinterpret_cast<uint2 *>(Oh + (size_t)row * D + dcol) = pk;
-                }
-            if (hi == 0)
-                Lh[row] = lt > 0.f ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;
-        }
+            for (int jj = 0; jj < 4; ++jj) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16_bits(o[db][4 * jj + 0] * inv) |
+                       ((uint32_t)f32_to_bf16_bits(o[db][4 * jj + 1] * inv) << 16);
+                pk.y = (uint32_t)f32_to_bf16_bits(o[db][4 * jj + 2] * inv) |
+                       ((uint32_t)f32_to_bf16_bits(o[db][4 * jj + 3] * inv) << 16);
+                *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * jj + 4 * hi) = pk;
+            }
+        if (hi == 0)
+            p.LSE[(size_t)bh * N + row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
-template <int D, int QB, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
 {
     FwdParams fp = fp0;
-    constexpr int BR = 128 * QB;
+    constexpr int BR = 256;
     fp.nqb = (pr.N + BR - 1) / BR;
     fp.items = pr.B * pr.H * fp.nqb;
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, CAUSAL, SPARSE>), dim3(grid), dim3(256), 0,
-                       pr.stream, fp);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3(grid), dim3(512), 0, pr.stream, fp);
     return hipGetLastError();
 }
 
-template <int D, int QB>
+template <int D>
 static hipError_t launch_fwd_d(const Problem &pr, const FwdParams &fp)
 {
     const bool sparse = pr.mask != nullptr;
     if (pr.causal)
-        return sparse ? launch_fwd_t<D, QB, true, true>(pr, fp) : launch_fwd_t<D, QB, true, false>(pr, fp);
-    return sparse ? launch_fwd_t<D, QB, false, true>(pr, fp) : launch_fwd_t<D, QB, false, false>(pr, fp);
+        return sparse ? launch_fwd_t<D, true, true>(pr, fp) : launch_fwd_t<D, true, false>(pr, fp);
+    return sparse ? launch_fwd_t<D, false, true>(pr, fp) : launch_fwd_t<D, false, false>(pr, fp);
 }
 
 hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t *K,
@@ -350,8 +413,8 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     fp.c = pr.scale * kLog2e;
     if (pr.d == 64)
-        return launch_fwd_d<64, 2>(pr, fp);
-    return launch_fwd_d<128, 2>(pr, fp);
+        return launch_fwd_d<64>(pr, fp);
+    return launch_fwd_d<128>(pr, fp);
 }
 
 }  // namespace fa
