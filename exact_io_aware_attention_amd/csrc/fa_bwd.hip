@@ -12,15 +12,17 @@
 // Kernels, all on the caller's stream:
 //   1. bwd_pre:  D and LSE * log2(e) per row (bandwidth-bound, one pass
 //      over dO and O);
-//   2. bwd_dq:   one workgroup per query block, key tiles streamed through
-//      LDS; recomputes S^T and dP^T, forms dS^T and accumulates
-//      dQ^T = K^T dS^T in registers (lane = query, as in the forward);
-//   3. bwd_dkdv: one workgroup per key block (32 keys per wave, K and V in
-//      registers), query tiles streamed through LDS; recomputes S and dP,
-//      accumulates dV^T = dO^T P and dK^T = Q^T dS in registers
-//      (lane = key).
+//   2. bwd_dq:   one workgroup per 256 query rows, key/value tiles streamed
+//      through LDS; recomputes S^T and dP^T, forms dS^T and accumulates
+//      dQ^T = K^T dS^T (lane = query, as in the forward);
+//   3. bwd_dkdv: one workgroup per 256 keys (K and V rows in registers),
+//      query tiles streamed through LDS; recomputes S and dP, accumulates
+//      dV^T = dO^T P and dK^T = Q^T dS (lane = key).
 // Splitting dQ from dK/dV recomputes S and dP once more (7 contractions
-// instead of 5) but needs no atomics and is deterministic.
+// instead of 5) but needs no atomics and is deterministic. (Accumulating dQ
+// across key blocks with fp32 global atomics instead was measured at about
+// 1.4 TB/s of atomic traffic on MI355X, which at 256 keys per block costs
+// more time than the two extra contractions.)
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -60,6 +62,99 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const 
     }
 }
 
+// ------------------------------------------------------- shared pieces ---
+//
+// Both main kernels give each workgroup 256 rows. For d = 64 that is 4
+// waves of 64 rows (one wave per SIMD, up to 512 registers each), so each
+// operand fragment read from LDS feeds two MFMAs; for d = 128 the operands
+// alone would not fit in that register file, so it is 8 waves of 32 rows
+// (two waves per SIMD, 256 registers each). The long-lived accumulators
+// (dQ^T, or dK^T and dV^T) stay in AGPRs; operands, S, dP and the softmax
+// temporaries use the VGPRs.
+//
+// Tiles of 64 rows stream through LDS, double-buffered, by direct
+// global->LDS loads (rows past the end of the sequence are loaded from the
+// last row and masked). The row-major tiles are read two ways: b128 operand
+// reads (16 consecutive rows per LDS cycle) and transpose reads (4
+// consecutive rows x 32 bytes per 16 lanes). The swizzle f(r) below stores
+// logical 16-byte chunk c of row r at chunk c ^ f(r); f is a bijection on
+// any 16 consecutive rows (b128 reads conflict-free) and f(r) / 2 differs
+// across any 4 aligned rows (transpose reads conflict-free).
+template <int D>
+__device__ __forceinline__ int tile_swz(int r)
+{
+    if (D == 128)  // 16 chunks per 256-byte row
+        return 2 * (r % 4) + 8 * ((r / 4) % 2) + ((r / 8) % 2);
+    return 2 * ((r / 2) % 4) + ((r / 8) % 2);  // 8 chunks per 128-byte row
+}
+
+// Issues the direct loads of one 64-row tile (row-major, d contiguous) into
+// LDS: 1 KB blocks spread over the workgroup's waves.
+template <int D, int W>
+__device__ __forceinline__ void issue_rows_tile(const uint16_t *src, uint16_t *dst, int row0, int N,
+                                                int wave, int lane)
+{
+    constexpr int CPR = D / 8;
+    constexpr int BLOCKS = 64 * D * 2 / 1024;
+    static_assert(BLOCKS % W == 0, "tile blocks per wave");
+#pragma unroll
+    for (int i = 0; i < BLOCKS / W; ++i) {
+        const int b = wave * (BLOCKS / W) + i;
+        const int r = b * (64 / CPR) + lane / CPR;
+        const int lc = (lane % CPR) ^ tile_swz<D>(r);
+        const int row = min(row0 + r, N - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)row * D + 8 * lc),
+                                         (__attribute__((address_space(3))) void *)(dst + b * 512), 16,
+                                         0, 0);
+    }
+}
+
+// Direct load of 64 consecutive floats (one wave): row-vector statistics.
+__device__ __forceinline__ void issue_vec64(const float *src, float *dst, int row0, int N, int lane)
+{
+    const int row = min(row0 + lane, N - 1);
+    __builtin_amdgcn_global_load_lds((const void *)(src + row), (__attribute__((address_space(3))) void *)dst,
+                                     4, 0, 0);
+}
+
+// b128 operand read: row r, logical chunk c of a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_b128(const uint16_t *t, int r, int c)
+{
+    return lds_read_b128(t + r * D + 8 * (c ^ tile_swz<D>(r)));
+}
+
+// Transpose-read operand (32 columns x 16 rows, as the A operand whose k
+// index runs over rows): lane 4t+u of 16-lane group g points at row
+// r0 + 4*(g/2) + t (and r0 + 8 + ... for slots 4..7), columns
+// col0 + 16*(g%2) + 4u.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr(const uint16_t *t, int r0, int col0, int lane)
+{
+    const int g = lane / 16, sl = lane % 16;
+    const int r = r0 + 4 * (g / 2) + sl / 4;
+    const int col = col0 + 16 * (g % 2) + 4 * (sl % 4);
+    const int c = col / 8, e = col % 8;
+    return lds_read_tr_pair(t + r * D + 8 * (c ^ tile_swz<D>(r)) + e,
+                            t + (r + 8) * D + 8 * (c ^ tile_swz<D>(r + 8)) + e);
+}
+
+// Stores a 32-row accumulator block (lane = row, registers = 32 columns in
+// runs of 4) as bf16, times a factor.
+__device__ __forceinline__ void store_rows_bf16(uint16_t *dst_row, const f32x16 &acc, int col0, int hi,
+                                                float mul)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(acc[4 * j + 0] * mul) |
+               ((uint32_t)f32_to_bf16_bits(acc[4 * j + 1] * mul) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(acc[4 * j + 2] * mul) |
+               ((uint32_t)f32_to_bf16_bits(acc[4 * j + 3] * mul) << 16);
+        *reinterpret_cast<uint2 *>(dst_row + col0 + 8 * j + 4 * hi) = pk;
+    }
+}
+
 // ----------------------------------------------------------------- dQ ----
 
 struct DqParams {
@@ -71,22 +166,32 @@ struct DqParams {
     float c, scale;
 };
 
+// One workgroup owns 256 query rows of one (b, h) (64 per wave, Q and dO
+// rows held as MFMA B operands); key/value tiles of 64 stream through LDS.
+// Per 32 keys: S^T = K Q^T and dP^T = V dO^T (lane = query), then
+// dS^T = P^T o (dP^T - D) with P^T = 2^(c s - lse2), then
+// dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
+template <int D>
+struct BwdShape {
+    static constexpr int W = 4;                  // waves per workgroup
+    static constexpr int NB = D == 128 ? 1 : 2;  // 32-row blocks per wave
+    static constexpr int ROWS = 32 * NB * W;     // rows per workgroup
+};
+
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
+__global__ void __launch_bounds__(64 * BwdShape<D>::W, 1) bwd_dq_kernel(DqParams p)
 {
-    constexpr int RW = 32;         // query rows per wave
-    constexpr int BR = 4 * RW;     // query rows per workgroup
-    constexpr int BC = 64;         // keys per LDS tile
-    constexpr int KSTR = D + 16;   // K tile: row reads and transpose reads
-    constexpr int VSTR = D + 8;    // V tile: row reads
+    constexpr int W = BwdShape<D>::W;
+    constexpr int NB = BwdShape<D>::NB;
+    constexpr int QW = 32 * NB;     // query rows per wave
+    constexpr int BR = W * QW;      // query rows per workgroup
+    constexpr int BC = 64;          // keys per LDS tile
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 256 / CPR;
-    constexpr int NI = BC / RPI;
+    constexpr int TILE = BC * D;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * VSTR];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
@@ -102,33 +207,41 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     const int lane = tid % kWave;
     const int l32 = lane % 32;
     const int hi = lane / 32;
-    const int wr0 = q0 + wave * RW;
-    const int row = wr0 + l32;
+    const int wr0 = q0 + wave * QW;
 
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
 
-    bf16x8 qf[KK], gf[KK];
+    bf16x8 qf[NB][KK], gf[NB][KK];
+    float lse2[NB], Di[NB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        if (row < N) {
-            qf[kk] = *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi);
-            gf[kk] = *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * D + 16 * kk + 8 * hi);
-        } else {
-            qf[kk] = bf16x8{};
-            gf[kk] = bf16x8{};
+    for (int qb = 0; qb < NB; ++qb) {
+        const int row = wr0 + 32 * qb + l32;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            qf[qb][kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
+                                 : bf16x8{};
+            gf[qb][kk] = row < N ? *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * D + 16 * kk + 8 * hi)
+                                 : bf16x8{};
         }
+        lse2[qb] = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
+        Di[qb] = row < N ? p.delta[(size_t)bh * N + row] : 0.f;
     }
-    const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
-    const float Di = row < N ? p.delta[(size_t)bh * N + row] : 0.f;
 
     int t_end = p.nkt;
     if (CAUSAL)
         t_end = min(p.nkt, (q0 + BR - 1) / BC + 1);
-    const int mrow = q0 / kMaskBlock;  // BR = 128: one mask row per workgroup
+    const int mr_lo = q0 / kMaskBlock;
+    const int mr_hi = min(q0 + BR - 1, N - 1) / kMaskBlock;
+    const int wmr = min(wr0, N - 1) / kMaskBlock;  // <= 64 rows: one mask row per wave
     auto tile_needed = [&](int t) -> bool {
-        return !SPARSE || p.mask[(size_t)mrow * p.nmb + (t * BC) / kMaskBlock] != 0;
+        if (!SPARSE)
+            return true;
+        bool keep = false;
+        for (int mr = mr_lo; mr <= mr_hi; ++mr)
+            keep |= p.mask[(size_t)mr * p.nmb + (t * BC) / kMaskBlock] != 0;
+        return keep;
     };
     auto next_tile = [&](int t) -> int {
         ++t;
@@ -138,122 +251,95 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         return t;
     };
 
-    uint4 kst[NI], vst[NI];
-    auto load_tile = [&](int t) {
+    f32x16 dq[NB][DB];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            const int key = t * BC + r;
-            if (key < N) {
-                kst[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)key * D + 8 * c);
-                vst[i] = *reinterpret_cast<const uint4 *>(Vh + (size_t)key * D + 8 * c);
-            } else {
-                kst[i] = uint4{0, 0, 0, 0};
-                vst[i] = uint4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
+    for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            *reinterpret_cast<uint4 *>(&Ks[buf][r * KSTR + 8 * c]) = kst[i];
-            *reinterpret_cast<uint4 *>(&Vs[buf][r * VSTR + 8 * c]) = vst[i];
-        }
-    };
-
-    f32x16 dq[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-        dq[db] = f32x16{};
-
-    const int g = lane / 16;
-    const int sl = lane % 16;
-    const int t_key = 4 * (g / 2) + sl / 4;
-    const int t_col = 16 * (g % 2) + 4 * (sl % 4);
+        for (int db = 0; db < DB; ++db)
+            dq[qb][db] = f32x16{};
 
     int t = next_tile(-1);
     if (t < t_end) {
-        load_tile(t);
-        store_tile(0);
+        issue_rows_tile<D, W>(Kh, Ks[0], t * BC, N, wave, lane);
+        issue_rows_tile<D, W>(Vh, Vs[0], t * BC, N, wave, lane);
     }
     __syncthreads();
     int buf = 0;
     while (t < t_end) {
         const int tn = next_tile(t);
-        if (tn < t_end)
-            load_tile(tn);
+        if (tn < t_end) {
+            issue_rows_tile<D, W>(Kh, Ks[buf ^ 1], tn * BC, N, wave, lane);
+            issue_rows_tile<D, W>(Vh, Vs[buf ^ 1], tn * BC, N, wave, lane);
+        }
         const int kbase = t * BC;
-        bool active = wr0 < N;
-        if (CAUSAL)
-            active = active && kbase <= wr0 + RW - 1;
-        if (active) {
+        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
+        {
             const uint16_t *ks = Ks[buf];
             const uint16_t *vs = Vs[buf];
-            f32x16 s[2], dp[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
-                dp[kb] = f32x16{};
+            for (int kh = 0; kh < 2; ++kh) {
+                f32x16 s[NB], dp[NB];
+#pragma unroll
+                for (int qb = 0; qb < NB; ++qb)
+                    s[qb] = dp[qb] = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 kf = lds_read_b128(ks + (32 * kb + l32) * KSTR + 16 * kk + 8 * hi);
-                    const bf16x8 vf = lds_read_b128(vs + (32 * kb + l32) * VSTR + 16 * kk + 8 * hi);
-                    s[kb] = mfma32x32x16(kf, qf[kk], s[kb]);
-                    dp[kb] = mfma32x32x16(vf, gf[kk], dp[kb]);
-                }
-            }
-            const bool need_mask = (kbase + BC > N) || (CAUSAL && kbase + BC - 1 > wr0);
-            // dS^T = P^T o (dP^T - D), P^T = 2^(c s - lse2); masked entries 0.
+                    const bf16x8 ka = tile_b128<D>(ks, 32 * kh + l32, 2 * kk + hi);
+                    const bf16x8 va = tile_b128<D>(vs, 32 * kh + l32, 2 * kk + hi);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pr = exp2_fast(fmaf(s[kb][r], p.c, -lse2));
-                    if (need_mask) {
-                        const int key = kbase + 32 * kb + 8 * (r / 4) + 4 * hi + (r % 4);
-                        if (key >= N || (CAUSAL && key > row))
-                            pr = 0.f;
+                    for (int qb = 0; qb < NB; ++qb) {
+                        s[qb] = mfma32x32x16(ka, qf[qb][kk], s[qb]);
+                        dp[qb] = mfma32x32x16(va, gf[qb][kk], dp[qb]);
                     }
-                    s[kb][r] = pr * (dp[kb][r] - Di);
                 }
-            // dQ^T += K^T dS^T (transpose reads of the K tile).
+                const int k0 = kbase + 32 * kh;
+                const bool need_mask = drop || (k0 + 32 > N) || (CAUSAL && k0 + 31 > wr0);
+                bf16x8 sb[NB][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int qb = 0; qb < NB; ++qb) {
+                    const int row = wr0 + 32 * qb + l32;
+                    f32x16 ds;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8 sf = pack_bf16x8(s[kb], hh);
-                    const uint16_t *krow = ks + (32 * kb + 16 * hh + t_key) * KSTR + t_col;
+                    for (int r = 0; r < 16; ++r) {
+                        float pr = exp2_fast(fmaf(s[qb][r], p.c, -lse2[qb]));
+                        if (need_mask) {
+                            const int key = k0 + 8 * (r / 4) + 4 * hi + (r % 4);
+                            if (drop || key >= N || (CAUSAL && key > row))
+                                pr = 0.f;
+                        }
+                        ds[r] = pr * (dp[qb][r] - Di[qb]);
+                    }
+                    sb[qb][0] = pack_bf16x8(ds, 0);
+                    sb[qb][1] = pack_bf16x8(ds, 1);
+                }
+                // dQ^T += K^T dS^T: K^T (32 d x 16 keys) by transpose reads,
+                // one read per NB MFMAs.
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const bf16x8 kt = lds_read_tr_pair(krow + 32 * db, krow + 8 * KSTR + 32 * db);
-                        dq[db] = mfma32x32x16(kt, sf, dq[db]);
+                        const bf16x8 kt = tile_tr<D>(ks, 32 * kh + 16 * hh, 32 * db, lane);
+#pragma unroll
+                        for (int qb = 0; qb < NB; ++qb)
+                            mfma_acc_agpr(dq[qb][db], kt, sb[qb][hh]);
                     }
-                }
+            }
         }
-        if (tn < t_end)
-            store_tile(buf ^ 1);
         __syncthreads();
         buf ^= 1;
         t = tn;
     }
 
-    if (row < N) {
-        uint16_t *dQh = p.dQ + head;
+    mfma_drain();
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < NB; ++qb) {
+        const int row = wr0 + 32 * qb + l32;
+        if (row < N) {
+            uint16_t *dst = p.dQ + head + (size_t)row * D;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int dcol = 32 * db + 8 * j + 4 * hi;
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16_bits(dq[db][4 * j + 0] * p.scale) |
-                       ((uint32_t)f32_to_bf16_bits(dq[db][4 * j + 1] * p.scale) << 16);
-                pk.y = (uint32_t)f32_to_bf16_bits(dq[db][4 * j + 2] * p.scale) |
-                       ((uint32_t)f32_to_bf16_bits(dq[db][4 * j + 3] * p.scale) << 16);
-                *reinterpret_cast<uint2 *>(dQh + (size_t)row * D + dcol) = pk;
-            }
+            for (int db = 0; db < DB; ++db)
+                store_rows_bf16(dst, dq[qb][db], 32 * db, hi, p.scale);
+        }
     }
 }
 
@@ -268,29 +354,33 @@ struct DkvParams {
     float c, scale;
 };
 
+// One workgroup owns 256 keys of one (b, h) (64 per wave, K and V rows held
+// as MFMA B operands); query tiles of 64 (Q, dO, LSE, D) stream through
+// LDS. Per 32 queries: S = Q K^T and dP = dO V^T (lane = key), then
+// P = 2^(c s - lse2), dS = P o (dP - D), then dV^T += dO^T P and
+// dK^T += Q^T dS with dO^T, Q^T from transpose reads of the tiles.
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
+__global__ void __launch_bounds__(64 * BwdShape<D>::W, 1) bwd_dkdv_kernel(DkvParams p)
 {
-    constexpr int KW = 32;         // keys per wave
-    constexpr int BK = 4 * KW;     // keys per workgroup
-    constexpr int BQ = 64;         // queries per LDS tile
-    constexpr int STR = D + 16;    // Q / dO tiles: row reads and transpose reads
+    constexpr int W = BwdShape<D>::W;
+    constexpr int NB = BwdShape<D>::NB;
+    constexpr int KW = 32 * NB;     // keys per wave
+    constexpr int BK = W * KW;      // keys per workgroup
+    constexpr int BQ = 64;          // queries per LDS tile
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 256 / CPR;
-    constexpr int NI = BQ / RPI;
+    constexpr int TILE = BQ * D;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * STR];
-    __shared__ __attribute__((aligned(16))) uint16_t Gs[2][BQ * STR];
-    __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-    __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][TILE];
+    __shared__ __attribute__((aligned(256))) float Ls[2][BQ];
+    __shared__ __attribute__((aligned(256))) float Ds[2][BQ];
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
         return;
     const int bh = item / p.nkb;
-    const int kblk = item - bh * p.nkb;  // causal: later key blocks see fewer queries
+    const int kblk = item - bh * p.nkb;  // causal: low key blocks see the most queries
     const int k0 = kblk * BK;
     const int N = p.N;
 
@@ -300,7 +390,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const int l32 = lane % 32;
     const int hi = lane / 32;
     const int wk0 = k0 + wave * KW;
-    const int key = wk0 + l32;
 
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
@@ -308,23 +397,31 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const float *lse2h = p.lse2 + (size_t)bh * N;
     const float *deltah = p.delta + (size_t)bh * N;
 
-    // This wave's keys as MFMA B operands (lane = key, 8 d-values each).
-    bf16x8 kf[KK], vf[KK];
+    bf16x8 kf[NB][KK], vf[NB][KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        if (key < N) {
-            kf[kk] = *reinterpret_cast<const bf16x8 *>(Kh + (size_t)key * D + 16 * kk + 8 * hi);
-            vf[kk] = *reinterpret_cast<const bf16x8 *>(Vh + (size_t)key * D + 16 * kk + 8 * hi);
-        } else {
-            kf[kk] = bf16x8{};
-            vf[kk] = bf16x8{};
+    for (int kb = 0; kb < NB; ++kb) {
+        const int key = wk0 + 32 * kb + l32;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            kf[kb][kk] = key < N ? *reinterpret_cast<const bf16x8 *>(Kh + (size_t)key * D + 16 * kk + 8 * hi)
+                                 : bf16x8{};
+            vf[kb][kk] = key < N ? *reinterpret_cast<const bf16x8 *>(Vh + (size_t)key * D + 16 * kk + 8 * hi)
+                                 : bf16x8{};
         }
     }
 
     const int t_begin = CAUSAL ? k0 / BQ : 0;
-    const int kmb = k0 / kMaskBlock;  // BK = 128: one mask column per workgroup
+    const int mc_lo = k0 / kMaskBlock;
+    const int mc_hi = min(k0 + BK - 1, N - 1) / kMaskBlock;
+    const int wmc = min(wk0, N - 1) / kMaskBlock;  // <= 64 keys: one mask column per wave
     auto tile_needed = [&](int t) -> bool {
-        return !SPARSE || p.mask[(size_t)((t * BQ) / kMaskBlock) * p.nmb + kmb] != 0;
+        if (!SPARSE)
+            return true;
+        const size_t mrow = (size_t)((t * BQ) / kMaskBlock) * p.nmb;
+        bool keep = false;
+        for (int mc = mc_lo; mc <= mc_hi; ++mc)
+            keep |= p.mask[mrow + mc] != 0;
+        return keep;
     };
     auto next_tile = [&](int t) -> int {
         ++t;
@@ -333,156 +430,127 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                 ++t;
         return t;
     };
-
-    uint4 qst[NI], gst[NI];
-    float lst = 0.f, dst = 0.f;
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            const int q = t * BQ + r;
-            if (q < N) {
-                qst[i] = *reinterpret_cast<const uint4 *>(Qh + (size_t)q * D + 8 * c);
-                gst[i] = *reinterpret_cast<const uint4 *>(dOh + (size_t)q * D + 8 * c);
-            } else {
-                qst[i] = uint4{0, 0, 0, 0};
-                gst[i] = uint4{0, 0, 0, 0};
-            }
-        }
-        if (tid < BQ) {
-            const int q = t * BQ + tid;
-            lst = q < N ? lse2h[q] : INFINITY;
-            dst = q < N ? deltah[q] : 0.f;
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = tid / CPR + i * RPI;
-            const int c = tid % CPR;
-            *reinterpret_cast<uint4 *>(&Qs[buf][r * STR + 8 * c]) = qst[i];
-            *reinterpret_cast<uint4 *>(&Gs[buf][r * STR + 8 * c]) = gst[i];
-        }
-        if (tid < BQ) {
-            Ls[buf][tid] = lst;
-            Ds[buf][tid] = dst;
-        }
+    auto issue_tile = [&](int t, int b) {
+        issue_rows_tile<D, W>(Qh, Qs[b], t * BQ, N, wave, lane);
+        issue_rows_tile<D, W>(dOh, Gs[b], t * BQ, N, wave, lane);
+        if (wave == 0)
+            issue_vec64(lse2h, Ls[b], t * BQ, N, lane);
+        else if (wave == 1)
+            issue_vec64(deltah, Ds[b], t * BQ, N, lane);
     };
 
-    f32x16 dk[DB], dv[DB];
+    f32x16 dk[NB][DB], dv[NB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
-
-    const int g = lane / 16;
-    const int sl = lane % 16;
-    const int t_row = 4 * (g / 2) + sl / 4;
-    const int t_col = 16 * (g % 2) + 4 * (sl % 4);
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            dk[kb][db] = f32x16{};
+            dv[kb][db] = f32x16{};
+        }
 
     int t = t_begin;
     if (SPARSE && t < p.nqt && !tile_needed(t))
         t = next_tile(t);
-    if (t < p.nqt) {
-        load_tile(t);
-        store_tile(0);
-    }
+    if (t < p.nqt)
+        issue_tile(t, 0);
     __syncthreads();
     int buf = 0;
     while (t < p.nqt) {
         const int tn = next_tile(t);
         if (tn < p.nqt)
-            load_tile(tn);
+            issue_tile(tn, buf ^ 1);
         const int qbase = t * BQ;
-        bool active = wk0 < N;
-        if (CAUSAL)
-            active = active && qbase + BQ - 1 >= wk0;
-        if (active) {
+        // a wave whose block-mask column drops this tile keeps computing (in
+        // step with the workgroup) with every weight masked to zero
+        const bool drop = SPARSE && p.mask[(size_t)(qbase / kMaskBlock) * p.nmb + wmc] == 0;
+        {
             const uint16_t *qs = Qs[buf];
             const uint16_t *gs = Gs[buf];
             const float *ls = Ls[buf];
             const float *ds = Ds[buf];
 #pragma unroll
             for (int qh = 0; qh < 2; ++qh) {
-                // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-                // (lane = key, register r = query 8(r/4) + 4 hi + r%4).
-                f32x16 s = f32x16{}, dpv = f32x16{};
+                // S = Q K^T, dP = dO V^T: 32 queries x 64 keys (lane = key,
+                // register r = query 8(r/4) + 4hi + r%4 of this step).
+                f32x16 s[NB], dp[NB];
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb)
+                    s[kb] = dp[kb] = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 qa = lds_read_b128(qs + (32 * qh + l32) * STR + 16 * kk + 8 * hi);
-                    const bf16x8 ga = lds_read_b128(gs + (32 * qh + l32) * STR + 16 * kk + 8 * hi);
-                    s = mfma32x32x16(qa, kf[kk], s);
-                    dpv = mfma32x32x16(ga, vf[kk], dpv);
+                    const bf16x8 qa = tile_b128<D>(qs, 32 * qh + l32, 2 * kk + hi);
+                    const bf16x8 ga = tile_b128<D>(gs, 32 * qh + l32, 2 * kk + hi);
+#pragma unroll
+                    for (int kb = 0; kb < NB; ++kb) {
+                        s[kb] = mfma32x32x16(qa, kf[kb][kk], s[kb]);
+                        dp[kb] = mfma32x32x16(ga, vf[kb][kk], dp[kb]);
+                    }
                 }
                 const int qrow0 = qbase + 32 * qh;
-                const bool need_mask = (qrow0 + 32 > N) || (CAUSAL && qrow0 < wk0 + KW - 1);
-                f32x16 pm, dsm;
+                const bool need_mask = drop || (qrow0 + 32 > N) || (CAUSAL && qrow0 < wk0 + KW - 1);
+                bf16x8 pb[NB][2], sb[NB][2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 lv = *reinterpret_cast<const float4 *>(ls + 32 * qh + 8 * j + 4 * hi);
-                    const float4 dv4 = *reinterpret_cast<const float4 *>(ds + 32 * qh + 8 * j + 4 * hi);
-                    const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
-                    const float dq[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+                for (int kb = 0; kb < NB; ++kb) {
+                    const int key = wk0 + 32 * kb + l32;
+                    f32x16 pm, dsm;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r = 4 * j + u;
-                        float pr = exp2_fast(fmaf(s[r], p.c, -lq[u]));
-                        if (need_mask) {
-                            const int q = qrow0 + 8 * j + 4 * hi + u;
-                            if (q >= N || (CAUSAL && key > q))
-                                pr = 0.f;
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 lv = *reinterpret_cast<const float4 *>(ls + 32 * qh + 8 * j + 4 * hi);
+                        const float4 dv4 = *reinterpret_cast<const float4 *>(ds + 32 * qh + 8 * j + 4 * hi);
+                        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
+                        const float dq4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int r = 4 * j + u;
+                            float pr = exp2_fast(fmaf(s[kb][r], p.c, -lq[u]));
+                            if (need_mask) {
+                                const int q = qrow0 + 8 * j + 4 * hi + u;
+                                if (drop || q >= N || (CAUSAL && key > q))
+                                    pr = 0.f;
+                            }
+                            pm[r] = pr;
+                            dsm[r] = pr * (dp[kb][r] - dq4[u]);
                         }
-                        pm[r] = pr;
-                        dsm[r] = pr * (dpv[r] - dq[u]);
                     }
+                    pb[kb][0] = pack_bf16x8(pm, 0);
+                    pb[kb][1] = pack_bf16x8(pm, 1);
+                    sb[kb][0] = pack_bf16x8(dsm, 0);
+                    sb[kb][1] = pack_bf16x8(dsm, 1);
                 }
-                // dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the
-                // query tiles; P and dS enter as B operands, k = queries).
+                // dV^T += dO^T P, dK^T += Q^T dS: one transpose read per NB
+                // MFMAs (all key blocks of the wave).
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8 pf = pack_bf16x8(pm, hh);
-                    const bf16x8 sf = pack_bf16x8(dsm, hh);
-                    const int trow = 32 * qh + 16 * hh + t_row;
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const uint16_t *gp = gs + trow * STR + t_col + 32 * db;
-                        const uint16_t *qp = qs + trow * STR + t_col + 32 * db;
-                        const bf16x8 gt = lds_read_tr_pair(gp, gp + 8 * STR);
-                        const bf16x8 qt = lds_read_tr_pair(qp, qp + 8 * STR);
-                        dv[db] = mfma32x32x16(gt, pf, dv[db]);
-                        dk[db] = mfma32x32x16(qt, sf, dk[db]);
+                        const bf16x8 gt = tile_tr<D>(gs, 32 * qh + 16 * hh, 32 * db, lane);
+                        const bf16x8 qt = tile_tr<D>(qs, 32 * qh + 16 * hh, 32 * db, lane);
+#pragma unroll
+                        for (int kb = 0; kb < NB; ++kb) {
+                            mfma_acc_agpr(dv[kb][db], gt, pb[kb][hh]);
+                            mfma_acc_agpr(dk[kb][db], qt, sb[kb][hh]);
+                        }
                     }
-                }
             }
         }
-        if (tn < p.nqt)
-            store_tile(buf ^ 1);
         __syncthreads();
         buf ^= 1;
         t = tn;
     }
 
-    if (key < N) {
-        uint16_t *dKh = p.dK + head, *dVh = p.dV + head;
+    mfma_drain();
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int kb = 0; kb < NB; ++kb) {
+        const int key = wk0 + 32 * kb + l32;
+        if (key < N) {
+            uint16_t *dKr = p.dK + head + (size_t)key * D;
+            uint16_t *dVr = p.dV + head + (size_t)key * D;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int dcol = 32 * db + 8 * j + 4 * hi;
-                uint2 pk, pv;
-                pk.x = (uint32_t)f32_to_bf16_bits(dk[db][4 * j + 0] * p.scale) |
-                       ((uint32_t)f32_to_bf16_bits(dk[db][4 * j + 1] * p.scale) << 16);
-                pk.y = (uint32_t)f32_to_bf16_bits(dk[db][4 * j + 2] * p.scale) |
-                       ((uint32_t)f32_to_bf16_bits(dk[db][4 * j + 3] * p.scale) << 16);
-                pv.x = (uint32_t)f32_to_bf16_bits(dv[db][4 * j + 0]) |
-                       ((uint32_t)f32_to_bf16_bits(dv[db][4 * j + 1]) << 16);
-                pv.y = (uint32_t)f32_to_bf16_bits(dv[db][4 * j + 2]) |
-                       ((uint32_t)f32_to_bf16_bits(dv[db][4 * j + 3]) << 16);
-                *reinterpret_cast<uint2 *>(dKh + (size_t)key * D + dcol) = pk;
-                *reinterpret_cast<uint2 *>(dVh + (size_t)key * D + dcol) = pv;
+            for (int db = 0; db < DB; ++db) {
+                store_rows_bf16(dKr, dk[kb][db], 32 * db, hi, p.scale);
+                store_rows_bf16(dVr, dv[kb][db], 32 * db, hi, 1.f);
             }
+        }
     }
 }
 
@@ -523,14 +591,14 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
     qp.delta = b.delta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
-    qp.nqb = (pr.N + 127) / 128;
+    qp.nqb = (pr.N + BwdShape<D>::ROWS - 1) / BwdShape<D>::ROWS;
     qp.nkt = (pr.N + 63) / 64;
     qp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     qp.items = pr.B * pr.H * qp.nqb;
     qp.per_xcd = (qp.items + kXcds - 1) / kXcds;
     qp.c = pr.scale * kLog2e;
     qp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(64 * BwdShape<D>::W), 0,
                        pr.stream, qp);
     return hipGetLastError();
 }
@@ -542,14 +610,14 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
     kp.delta = b.delta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
-    kp.nkb = (pr.N + 127) / 128;
+    kp.nkb = (pr.N + BwdShape<D>::ROWS - 1) / BwdShape<D>::ROWS;
     kp.nqt = (pr.N + 63) / 64;
     kp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     kp.items = pr.B * pr.H * kp.nkb;
     kp.per_xcd = (kp.items + kXcds - 1) / kXcds;
     kp.c = pr.scale * kLog2e;
     kp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(64 * BwdShape<D>::W), 0,
                        pr.stream, kp);
     return hipGetLastError();
 }

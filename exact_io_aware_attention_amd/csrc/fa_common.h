@@ -44,6 +44,27 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Accumulating MFMA whose accumulator lives in AGPRs (acc += A B). The
+// compiler keeps values an MFMA builtin produces in VGPRs when built with
+// the VGPR MFMA form, which a long-lived accumulator does not need: this
+// form leaves the 256 VGPRs to operands and softmax temporaries. The
+// statement carries its own hazard wait (two wait states between a vector
+// ALU write of an operand and the MFMA read of it), since the compiler's
+// hazard tracking does not look inside asm.
+__device__ __forceinline__ void mfma_acc_agpr(f32x16 &acc, bf16x8 a, bf16x8 b)
+{
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last AGPR-accumulating MFMA and any vector
+// instruction that reads its accumulator (more than the 8-pass MFMA needs).
+__device__ __forceinline__ void mfma_drain()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Eight consecutive bf16 values from LDS (16-byte aligned address).
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t *p)
 {
