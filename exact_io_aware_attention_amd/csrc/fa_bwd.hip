@@ -171,18 +171,22 @@ struct DqParams {
 // Per 32 keys: S^T = K Q^T and dP^T = V dO^T (lane = query), then
 // dS^T = P^T o (dP^T - D) with P^T = 2^(c s - lse2), then
 // dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
-template <int D>
+// Waves per workgroup and 32-row MFMA blocks per wave. The dK/dV kernel
+// holds K and V operands plus two accumulators per block, which for d = 128
+// only fit the register file with one block per wave.
+template <int D, bool DKDV>
 struct BwdShape {
-    static constexpr int W = 4;                  // waves per workgroup
-    static constexpr int NB = D == 128 ? 1 : 2;  // 32-row blocks per wave
-    static constexpr int ROWS = 32 * NB * W;     // rows per workgroup
+    static constexpr int W = 4;
+    static constexpr int NB = D == 128 ? 1 : 2;
+    static constexpr int ROWS = 32 * NB * W;  // rows per workgroup
 };
 
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(64 * BwdShape<D>::W, 1) bwd_dq_kernel(DqParams p)
+__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
 {
-    constexpr int W = BwdShape<D>::W;
-    constexpr int NB = BwdShape<D>::NB;
+    static_assert(BwdShape<D, false>::W * 64 == 256, "launch bounds");
+    constexpr int W = BwdShape<D, false>::W;
+    constexpr int NB = BwdShape<D, false>::NB;
     constexpr int QW = 32 * NB;     // query rows per wave
     constexpr int BR = W * QW;      // query rows per workgroup
     constexpr int BC = 64;          // keys per LDS tile
@@ -360,10 +364,11 @@ struct DkvParams {
 // P = 2^(c s - lse2), dS = P o (dP - D), then dV^T += dO^T P and
 // dK^T += Q^T dS with dO^T, Q^T from transpose reads of the tiles.
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(64 * BwdShape<D>::W, 1) bwd_dkdv_kernel(DkvParams p)
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 {
-    constexpr int W = BwdShape<D>::W;
-    constexpr int NB = BwdShape<D>::NB;
+    static_assert(BwdShape<D, true>::W * 64 == 256, "launch bounds");
+    constexpr int W = BwdShape<D, true>::W;
+    constexpr int NB = BwdShape<D, true>::NB;
     constexpr int KW = 32 * NB;     // keys per wave
     constexpr int BK = W * KW;      // keys per workgroup
     constexpr int BQ = 64;          // queries per LDS tile
@@ -591,14 +596,14 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
     qp.delta = b.delta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
-    qp.nqb = (pr.N + BwdShape<D>::ROWS - 1) / BwdShape<D>::ROWS;
+    qp.nqb = (pr.N + BwdShape<D, false>::ROWS - 1) / BwdShape<D, false>::ROWS;
     qp.nkt = (pr.N + 63) / 64;
     qp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     qp.items = pr.B * pr.H * qp.nqb;
     qp.per_xcd = (qp.items + kXcds - 1) / kXcds;
     qp.c = pr.scale * kLog2e;
     qp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(64 * BwdShape<D>::W), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(256), 0,
                        pr.stream, qp);
     return hipGetLastError();
 }
@@ -610,14 +615,14 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
     kp.delta = b.delta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
-    kp.nkb = (pr.N + BwdShape<D>::ROWS - 1) / BwdShape<D>::ROWS;
+    kp.nkb = (pr.N + BwdShape<D, true>::ROWS - 1) / BwdShape<D, true>::ROWS;
     kp.nqt = (pr.N + 63) / 64;
     kp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     kp.items = pr.B * pr.H * kp.nkb;
     kp.per_xcd = (kp.items + kXcds - 1) / kXcds;
     kp.c = pr.scale * kLog2e;
     kp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(64 * BwdShape<D>::W), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(256), 0,
                        pr.stream, kp);
     return hipGetLastError();
 }
