@@ -40,6 +40,38 @@ def parse():
     return ap.parse_args()
 
 
+def kernel_source_sha256():
+    """sha256 over the kernel sources and their build script (as recorded in
+    the traffic profile when its counters were taken)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "exact_io_aware_attention_amd")
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_tag, symbol):
+    """HBM bytes per dispatch of `symbol` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when there is none for this
+    workload or the kernels changed since the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_tag}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sha256 \(csrc/\* \+ build\.py\): `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_sha256():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if cells and cells[0] == symbol:
+            return int(cells[-1])
+    return None
+
+
 def flop_counts(cfg, mask):
     """Algorithmic FLOPs of one forward and of one backward."""
     fwd = 4.0 * cfg.B * cfg.H * cfg.N ** 2 * cfg.d
@@ -134,9 +166,15 @@ def main():
                     "bwd_dkdv": 4 * E * 2 + 2 * rows * 4 + 2 * E * 2}
     dominant = max(names, key=lambda n: avg[n])
     ach = kernel_flops[dominant] / avg[dominant] / 1e12
+    tf = lambda b: "true" if b else "false"  # noqa: E731
+    flags = f"{cfg.d}, {tf(cfg.causal)}, {tf(mask is not None)}"
+    symbols = {"fwd": f"fwd_bf16_kernel<{flags}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
+               "bwd_dq": f"bwd_dq_kernel<{flags}>", "bwd_dkdv": f"bwd_dkdv_kernel<{flags}>"}
+    tag = f"{cfg.name.replace('-', '_')}_b{cfg.B}h{cfg.H}n{cfg.N}d{cfg.d}"
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(tag, symbols[dominant]),
                 "algorithmic_bytes": kernel_bytes[dominant]}
 
     kernels = {n: {"avg_us": round(avg[n] * 1e6, 2),
