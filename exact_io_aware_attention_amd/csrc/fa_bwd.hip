@@ -10,19 +10,22 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Kernels, all on the caller's stream:
-//   1. bwd_pre:  D and LSE * log2(e) per row (bandwidth-bound, one pass
+//   1. bwd_pre:  -D and LSE * log2(e) per row (bandwidth-bound, one pass
 //      over dO and O);
-//   2. bwd_dq:   one workgroup per 256 query rows, key/value tiles streamed
-//      through LDS; recomputes S^T and dP^T, forms dS^T and accumulates
-//      dQ^T = K^T dS^T (lane = query, as in the forward);
-//   3. bwd_dkdv: one workgroup per 256 keys (K and V rows in registers),
-//      query tiles streamed through LDS; recomputes S and dP, accumulates
-//      dV^T = dO^T P and dK^T = Q^T dS (lane = key).
+//   2. bwd_dq:   one workgroup per 128 (d = 128) or 256 (d = 64) query
+//      rows, key/value tiles streamed through LDS; recomputes S^T and dP^T,
+//      forms dS^T and accumulates dQ^T = K^T dS^T (lane = query, as in the
+//      forward);
+//   3. bwd_dkdv: one workgroup per 128 or 256 keys (K and V rows in
+//      registers), query tiles streamed through LDS; recomputes S and dP,
+//      accumulates dV^T = dO^T P and dK^T = Q^T dS (lane = key).
 // Splitting dQ from dK/dV recomputes S and dP once more (7 contractions
 // instead of 5) but needs no atomics and is deterministic. (Accumulating dQ
 // across key blocks with fp32 global atomics instead was measured at about
-// 1.4 TB/s of atomic traffic on MI355X, which at 256 keys per block costs
+// 1.4 TB/s of atomic traffic on MI355X, which at 128 keys per block costs
 // more time than the two extra contractions.)
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -34,7 +37,7 @@ namespace {
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const uint16_t *O,
-                                                      const float *LSE, float *delta,
+                                                      const float *LSE, float *ndelta,
                                                       float *lse2, long rows)
 {
     constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
@@ -56,7 +59,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const 
     for (int off = LPR / 2; off > 0; off /= 2)
         acc += __shfl_xor(acc, off, kWave);
     if (row < rows && part == 0) {
-        delta[row] = acc;
+        ndelta[row] = -acc;
         const float L = LSE[row];
         lse2[row] = (L == -INFINITY) ? INFINITY : L * kLog2e;
     }
@@ -64,22 +67,20 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const 
 
 // ------------------------------------------------------- shared pieces ---
 //
-// Both main kernels give each workgroup 256 rows. For d = 64 that is 4
-// waves of 64 rows (one wave per SIMD, up to 512 registers each), so each
-// operand fragment read from LDS feeds two MFMAs; for d = 128 the operands
-// alone would not fit in that register file, so it is 8 waves of 32 rows
-// (two waves per SIMD, 256 registers each). The long-lived accumulators
-// (dQ^T, or dK^T and dV^T) stay in AGPRs; operands, S, dP and the softmax
-// temporaries use the VGPRs.
+// Both main kernels run 4 waves per workgroup, one per SIMD (up to 512
+// registers each), with 32 rows per wave for d = 128 and 64 for d = 64 (so
+// each operand fragment read from LDS feeds two MFMAs). The long-lived
+// accumulators (dQ^T, or dK^T and dV^T) stay in AGPRs; operands, S, dP and
+// the softmax temporaries use the VGPRs.
 //
-// Tiles of 64 rows stream through LDS, double-buffered, by direct
-// global->LDS loads (rows past the end of the sequence are loaded from the
-// last row and masked). The row-major tiles are read two ways: b128 operand
-// reads (16 consecutive rows per LDS cycle) and transpose reads (4
-// consecutive rows x 32 bytes per 16 lanes). The swizzle f(r) below stores
-// logical 16-byte chunk c of row r at chunk c ^ f(r); f is a bijection on
-// any 16 consecutive rows (b128 reads conflict-free) and f(r) / 2 differs
-// across any 4 aligned rows (transpose reads conflict-free).
+// Tiles of 64 rows stream through LDS by direct global->LDS loads (rows past
+// the end of the sequence are loaded from the last row and masked). The
+// row-major tiles are read two ways: b128 operand reads (16 consecutive rows
+// per LDS cycle) and transpose reads (4 consecutive rows x 32 bytes per 16
+// lanes). The swizzle f(r) below stores logical 16-byte chunk c of row r at
+// chunk c ^ f(r); f is a bijection on any 16 consecutive rows (b128 reads
+// conflict-free) and f(r) / 2 differs across any 4 aligned rows (transpose
+// reads conflict-free).
 template <int D>
 __device__ __forceinline__ int tile_swz(int r)
 {
@@ -159,7 +160,7 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t *dst_row, const f32x16 
 
 struct DqParams {
     const uint16_t *dO, *Q, *K, *V;
-    const float *delta, *lse2;
+    const float *ndelta, *lse2;  // -D and LSE * log2(e) per row
     uint16_t *dQ;
     const uint8_t *mask;
     int N, nqb, nkt, nmb, items, per_xcd;
@@ -172,12 +173,13 @@ struct DqParams {
 // dS^T = P^T o (dP^T - D) with P^T = 2^(c s - lse2), then
 // dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
 // Waves per workgroup and 32-row MFMA blocks per wave. The dK/dV kernel
-// holds K and V operands plus two accumulators per block, which for d = 128
-// only fit the register file with one block per wave.
+// holds K and V operands, two accumulators per block and two pipelined steps
+// of S, dP, P and dS, which only fit the register file with one block per
+// wave; its workgroup then covers 128 keys, one block-mask column.
 template <int D, bool DKDV>
 struct BwdShape {
     static constexpr int W = 4;
-    static constexpr int NB = D == 128 ? 1 : 2;
+    static constexpr int NB = (D == 128 || DKDV) ? 1 : 2;
     static constexpr int ROWS = 32 * NB * W;  // rows per workgroup
 };
 
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
 
     bf16x8 qf[NB][KK], gf[NB][KK];
-    float lse2[NB], Di[NB];
+    float lse2[NB], nDi[NB];
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
         const int row = wr0 + 32 * qb + l32;
@@ -230,7 +232,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
                                  : bf16x8{};
         }
         lse2[qb] = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
-        Di[qb] = row < N ? p.delta[(size_t)bh * N + row] : 0.f;
+        nDi[qb] = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
     }
 
     int t_end = p.nkt;
@@ -311,7 +313,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
                             if (drop || key >= N || (CAUSAL && key > row))
                                 pr = 0.f;
                         }
-                        ds[r] = pr * (dp[qb][r] - Di[qb]);
+                        ds[r] = pr * (dp[qb][r] + nDi[qb]);
                     }
                     sb[qb][0] = pack_bf16x8(ds, 0);
                     sb[qb][1] = pack_bf16x8(ds, 1);
@@ -329,12 +331,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
                     }
             }
         }
+        // before the loop edges, where the compiler may move accumulators
+        mfma_drain();
         __syncthreads();
         buf ^= 1;
         t = tn;
     }
 
     mfma_drain();
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            mfma_settle(dq[qb][db]);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
         const int row = wr0 + 32 * qb + l32;
@@ -351,18 +360,26 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
 
 struct DkvParams {
     const uint16_t *dO, *Q, *K, *V;
-    const float *delta, *lse2;
+    const float *ndelta, *lse2;  // -D and LSE * log2(e) per row
     uint16_t *dK, *dV;
     const uint8_t *mask;
     int N, nkb, nqt, nmb, items, per_xcd;
     float c, scale;
 };
 
-// One workgroup owns 256 keys of one (b, h) (64 per wave, K and V rows held
-// as MFMA B operands); query tiles of 64 (Q, dO, LSE, D) stream through
-// LDS. Per 32 queries: S = Q K^T and dP = dO V^T (lane = key), then
-// P = 2^(c s - lse2), dS = P o (dP - D), then dV^T += dO^T P and
-// dK^T += Q^T dS with dO^T, Q^T from transpose reads of the tiles.
+// One workgroup owns 128 keys of one (b, h), K and V rows held as MFMA B
+// operands; query tiles of 64 (Q, dO, LSE, -D) stream
+// through LDS. Per 32 queries (a step):
+//   A: S = Q K^T and dP - D = dO V^T - D (lane = key, MFMA; the dP
+//      accumulator starts from -D);
+//   B: P = 2^(c s - lse2), dS = P o (dP - D) (vector ALU);
+//   C: dV^T += dO^T P and dK^T += Q^T dS (MFMA, dO^T and Q^T by transpose
+//      reads; accumulators in AGPRs).
+// With one wave per SIMD nothing hides a wave's own latencies, so the steps
+// are software-pipelined and the order is fixed by hand: step i runs A(i),
+// then C(i-1) with B(i) spread over its MFMA slots, every LDS operand read
+// issued a few MFMAs ahead of its use. Scheduling fences keep the compiler
+// from regrouping the slots (it cannot see the asm MFMAs' latencies).
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 {
@@ -375,11 +392,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = BQ * D;
+    constexpr int NPR = 2 * DB;          // transpose-operand pairs (dO^T, Q^T) per step
+    constexpr int EPP = 16 * NB / NPR;   // softmax elements per pair slot
+    constexpr int PA = D == 128 ? 3 : 2; // A operand reads issued this many slots ahead
+    constexpr int PD = D == 128 ? 3 : 2; // C operand pairs issued this many slots ahead
+    static_assert(2 * NB * NPR == KK * NB * 2, "as many MFMAs in A as in C");
+    static_assert(PA <= KK && PD <= KK && EPP * NPR == 16 * NB && 8 % EPP == 0, "slot plan");
+    // One mask column per workgroup: a tile it visits is kept for all waves.
+    static_assert(BK == kMaskBlock, "workgroup keys = one mask block");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs[2][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Gs[2][TILE];
-    __shared__ __attribute__((aligned(256))) float Ls[2][BQ];
-    __shared__ __attribute__((aligned(256))) float Ds[2][BQ];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs[3][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Gs[3][TILE];
+    __shared__ __attribute__((aligned(256))) float Ls[3][BQ];
+    __shared__ __attribute__((aligned(256))) float Ds[3][BQ];
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
@@ -388,6 +413,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const int kblk = item - bh * p.nkb;  // causal: low key blocks see the most queries
     const int k0 = kblk * BK;
     const int N = p.N;
+    const float c = p.c;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -400,7 +426,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
     const float *lse2h = p.lse2 + (size_t)bh * N;
-    const float *deltah = p.delta + (size_t)bh * N;
+    const float *ndh = p.ndelta + (size_t)bh * N;
 
     bf16x8 kf[NB][KK], vf[NB][KK];
 #pragma unroll
@@ -416,32 +442,23 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     }
 
     const int t_begin = CAUSAL ? k0 / BQ : 0;
-    const int mc_lo = k0 / kMaskBlock;
-    const int mc_hi = min(k0 + BK - 1, N - 1) / kMaskBlock;
-    const int wmc = min(wk0, N - 1) / kMaskBlock;  // <= 64 keys: one mask column per wave
-    auto tile_needed = [&](int t) -> bool {
-        if (!SPARSE)
-            return true;
-        const size_t mrow = (size_t)((t * BQ) / kMaskBlock) * p.nmb;
-        bool keep = false;
-        for (int mc = mc_lo; mc <= mc_hi; ++mc)
-            keep |= p.mask[mrow + mc] != 0;
-        return keep;
+    auto tile_needed = [&](int t) __attribute__((always_inline)) -> bool {
+        return !SPARSE || p.mask[(size_t)((t * BQ) / kMaskBlock) * p.nmb + kblk] != 0;
     };
-    auto next_tile = [&](int t) -> int {
+    auto next_tile = [&](int t) __attribute__((always_inline)) -> int {
         ++t;
         if (SPARSE)
             while (t < p.nqt && !tile_needed(t))
                 ++t;
         return t;
     };
-    auto issue_tile = [&](int t, int b) {
+    auto issue_tile = [&](int t, int b) __attribute__((always_inline)) {
         issue_rows_tile<D, W>(Qh, Qs[b], t * BQ, N, wave, lane);
         issue_rows_tile<D, W>(dOh, Gs[b], t * BQ, N, wave, lane);
         if (wave == 0)
             issue_vec64(lse2h, Ls[b], t * BQ, N, lane);
         else if (wave == 1)
-            issue_vec64(deltah, Ds[b], t * BQ, N, lane);
+            issue_vec64(ndh, Ds[b], t * BQ, N, lane);
     };
 
     f32x16 dk[NB][DB], dv[NB][DB];
@@ -453,97 +470,189 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             dv[kb][db] = f32x16{};
         }
 
+    // P and dS of the previous step (bf16, the B operands of C), and where
+    // its Q and dO rows are.
+    bf16x8 pb[NB][2], sb[NB][2];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+        pb[kb][0] = pb[kb][1] = sb[kb][0] = sb[kb][1] = bf16x8{};
+    int pbuf = 0, pqh = 0;
+
+    // Transpose-read operands of pair pr = (hh, db) of a step: dO^T and Q^T,
+    // 32 columns x 16 queries starting at query 32 qh + 16 hh.
+    auto read_pair = [&](int b, int qh, int pr, bf16x8 &g, bf16x8 &q) __attribute__((always_inline)) {
+        const int hh = pr / DB, db = pr % DB;
+        g = tile_tr<D>(Gs[b], 32 * qh + 16 * hh, 32 * db, lane);
+        q = tile_tr<D>(Qs[b], 32 * qh + 16 * hh, 32 * db, lane);
+    };
+    auto c_mfmas = [&](int pr, const bf16x8 &g, const bf16x8 &q) __attribute__((always_inline)) {
+        const int hh = pr / DB, db = pr % DB;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            mfma_acc_agpr_ordered(dv[kb][db], g, pb[kb][hh]);
+            mfma_acc_agpr_ordered(dk[kb][db], q, sb[kb][hh]);
+        }
+    };
+
+    // One step: 32 queries (rows 32 qh.. of tile buffer b, first query
+    // qrow0). MASKED applies the element mask: query past the end or key
+    // above the query (causal).
+    auto step = [&](auto mtag, int b, int qh, int qrow0) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        const uint16_t *qs = Qs[b];
+        const uint16_t *gs = Gs[b];
+        // lse2 and -D of the 16 queries a lane's S/dP registers cover:
+        // register r <-> query 8 (r / 4) + 4 hi + r % 4 of the step.
+        float lq[16];
+        f32x16 nd;
+        {
+            const float *ls = Ls[b] + 32 * qh + 4 * hi;
+            const float *ds = Ds[b] + 32 * qh + 4 * hi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 dv4 = *reinterpret_cast<const float4 *>(ds + 8 * j);
+                nd[4 * j + 0] = dv4.x; nd[4 * j + 1] = dv4.y;
+                nd[4 * j + 2] = dv4.z; nd[4 * j + 3] = dv4.w;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 lv = *reinterpret_cast<const float4 *>(ls + 8 * j);
+                lq[4 * j + 0] = lv.x; lq[4 * j + 1] = lv.y;
+                lq[4 * j + 2] = lv.z; lq[4 * j + 3] = lv.w;
+            }
+        }
+        bf16x8 qa[KK], ga[KK];
+#pragma unroll
+        for (int kk = 0; kk < PA; ++kk) {
+            qa[kk] = tile_b128<D>(qs, 32 * qh + l32, 2 * kk + hi);
+            ga[kk] = tile_b128<D>(gs, 32 * qh + l32, 2 * kk + hi);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- A(i), with the first C(i-1) operand pairs issued behind it
+        f32x16 s[NB], dp[NB];
+        bf16x8 gt[NPR], qt[NPR];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) {
+                s[kb] = mfma32x32x16(qa[kk], kf[kb][kk], kk == 0 ? f32x16{} : s[kb]);
+                dp[kb] = mfma32x32x16(ga[kk], vf[kb][kk], kk == 0 ? nd : dp[kb]);
+            }
+            if (kk + PA < KK) {
+                qa[kk + PA] = tile_b128<D>(qs, 32 * qh + l32, 2 * (kk + PA) + hi);
+                ga[kk + PA] = tile_b128<D>(gs, 32 * qh + l32, 2 * (kk + PA) + hi);
+            }
+            if (kk >= KK - PD)
+                read_pair(pbuf, pqh, kk - (KK - PD), gt[kk - (KK - PD)], qt[kk - (KK - PD)]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- C(i-1) beside B(i)
+        bf16x8 pb2[NB][2], sb2[NB][2];
+        float pm[NB][16], dsm[NB][16];
+#pragma unroll
+        for (int pr = 0; pr < NPR; ++pr) {
+            c_mfmas(pr, gt[pr], qt[pr]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (pr + PD < NPR)
+                read_pair(pbuf, pqh, pr + PD, gt[pr + PD], qt[pr + PD]);
+#pragma unroll
+            for (int e = pr * EPP; e < (pr + 1) * EPP; ++e) {
+                const int kb = e / 16, r = e % 16;
+                float pe = exp2_fast(fmaf(s[kb][r], c, -lq[r]));
+                if (MASKED) {
+                    const int key = wk0 + 32 * kb + l32;
+                    const int q = qrow0 + 8 * (r / 4) + 4 * hi + (r % 4);
+                    if (q >= N || (CAUSAL && key > q))
+                        pe = 0.f;
+                }
+                pm[kb][r] = pe;
+                dsm[kb][r] = pe * dp[kb][r];
+                if (r % 8 == 7) {
+                    const int h = r / 8;
+                    bf16x8 pk, sk;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        pk[i] = (__bf16)pm[kb][8 * h + i];
+                        sk[i] = (__bf16)dsm[kb][8 * h + i];
+                    }
+                    pb2[kb][h] = pk;
+                    sb2[kb][h] = sk;
+                    slot_done(pk);
+                    slot_done(sk);
+                } else {
+                    slot_done(pe);
+                    slot_done(dsm[kb][r]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                pb[kb][h] = pb2[kb][h];
+                sb[kb][h] = sb2[kb][h];
+            }
+        pbuf = b;
+        pqh = qh;
+    };
+
     int t = t_begin;
     if (SPARSE && t < p.nqt && !tile_needed(t))
         t = next_tile(t);
-    if (t < p.nqt)
+    if (t < p.nqt) {
         issue_tile(t, 0);
-    __syncthreads();
-    int buf = 0;
-    while (t < p.nqt) {
-        const int tn = next_tile(t);
-        if (tn < p.nqt)
-            issue_tile(tn, buf ^ 1);
-        const int qbase = t * BQ;
-        // a wave whose block-mask column drops this tile keeps computing (in
-        // step with the workgroup) with every weight masked to zero
-        const bool drop = SPARSE && p.mask[(size_t)(qbase / kMaskBlock) * p.nmb + wmc] == 0;
-        {
-            const uint16_t *qs = Qs[buf];
-            const uint16_t *gs = Gs[buf];
-            const float *ls = Ls[buf];
-            const float *ds = Ds[buf];
-#pragma unroll
-            for (int qh = 0; qh < 2; ++qh) {
-                // S = Q K^T, dP = dO V^T: 32 queries x 64 keys (lane = key,
-                // register r = query 8(r/4) + 4hi + r%4 of this step).
-                f32x16 s[NB], dp[NB];
-#pragma unroll
-                for (int kb = 0; kb < NB; ++kb)
-                    s[kb] = dp[kb] = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 qa = tile_b128<D>(qs, 32 * qh + l32, 2 * kk + hi);
-                    const bf16x8 ga = tile_b128<D>(gs, 32 * qh + l32, 2 * kk + hi);
-#pragma unroll
-                    for (int kb = 0; kb < NB; ++kb) {
-                        s[kb] = mfma32x32x16(qa, kf[kb][kk], s[kb]);
-                        dp[kb] = mfma32x32x16(ga, vf[kb][kk], dp[kb]);
-                    }
-                }
-                const int qrow0 = qbase + 32 * qh;
-                const bool need_mask = drop || (qrow0 + 32 > N) || (CAUSAL && qrow0 < wk0 + KW - 1);
-                bf16x8 pb[NB][2], sb[NB][2];
-#pragma unroll
-                for (int kb = 0; kb < NB; ++kb) {
-                    const int key = wk0 + 32 * kb + l32;
-                    f32x16 pm, dsm;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float4 lv = *reinterpret_cast<const float4 *>(ls + 32 * qh + 8 * j + 4 * hi);
-                        const float4 dv4 = *reinterpret_cast<const float4 *>(ds + 32 * qh + 8 * j + 4 * hi);
-                        const float lq[4] = {lv.x, lv.y, lv.z, lv.w};
-                        const float dq4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int r = 4 * j + u;
-                            float pr = exp2_fast(fmaf(s[kb][r], p.c, -lq[u]));
-                            if (need_mask) {
-                                const int q = qrow0 + 8 * j + 4 * hi + u;
-                                if (drop || q >= N || (CAUSAL && key > q))
-                                    pr = 0.f;
-                            }
-                            pm[r] = pr;
-                            dsm[r] = pr * (dp[kb][r] - dq4[u]);
-                        }
-                    }
-                    pb[kb][0] = pack_bf16x8(pm, 0);
-                    pb[kb][1] = pack_bf16x8(pm, 1);
-                    sb[kb][0] = pack_bf16x8(dsm, 0);
-                    sb[kb][1] = pack_bf16x8(dsm, 1);
-                }
-                // dV^T += dO^T P, dK^T += Q^T dS: one transpose read per NB
-                // MFMAs (all key blocks of the wave).
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 gt = tile_tr<D>(gs, 32 * qh + 16 * hh, 32 * db, lane);
-                        const bf16x8 qt = tile_tr<D>(qs, 32 * qh + 16 * hh, 32 * db, lane);
-#pragma unroll
-                        for (int kb = 0; kb < NB; ++kb) {
-                            mfma_acc_agpr(dv[kb][db], gt, pb[kb][hh]);
-                            mfma_acc_agpr(dk[kb][db], qt, sb[kb][hh]);
-                        }
-                    }
-            }
-        }
         __syncthreads();
-        buf ^= 1;
-        t = tn;
+        int j = 0;
+        // Whether this wave's elements of tile t need the element mask.
+        auto tile_masked = [&](int t) __attribute__((always_inline)) -> bool {
+            const int qbase = t * BQ;
+            return (qbase + BQ > N) || (CAUSAL && qbase < wk0 + KW - 1);
+        };
+        // One tile: its two steps, then the barrier after which tile t+1
+        // has landed and buffer (j+2)%3 is free.
+        auto tile = [&](auto mtag) __attribute__((always_inline)) {
+            const int tn = next_tile(t);
+            const int bc = j % 3;
+            if (tn < p.nqt)
+                issue_tile(tn, (j + 1) % 3);
+            const int qbase = t * BQ;
+            step(mtag, bc, 0, qbase);
+            step(mtag, bc, 1, qbase + 32);
+            mfma_drain();  // before the loop edges, where accumulators may be moved
+            __syncthreads();
+            t = tn;
+            ++j;
+        };
+        // Runs of masked and unmasked tiles each get a loop of their own, so
+        // the hot loop has no join at which the compiler could reassign the
+        // accumulators (causal: the masked tiles are the first ones, on the
+        // diagonal, and the ragged last one).
+        while (t < p.nqt) {
+            while (t < p.nqt && tile_masked(t))
+                tile(std::true_type{});
+            while (t < p.nqt && !tile_masked(t))
+                tile(std::false_type{});
+        }
+        // C of the last step
+#pragma unroll
+        for (int pr = 0; pr < NPR; ++pr) {
+            bf16x8 g, q;
+            read_pair(pbuf, pqh, pr, g, q);
+            c_mfmas(pr, g, q);
+        }
+        mfma_drain();
     }
 
-    mfma_drain();
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            mfma_settle(dk[kb][db]);
+            mfma_settle(dv[kb][db]);
+        }
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
         const int key = wk0 + 32 * kb + l32;
@@ -563,7 +672,7 @@ struct BwdPtrs {
     const uint16_t *dO, *Q, *K, *V, *O;
     const float *LSE;
     uint16_t *dQ, *dK, *dV;
-    float *delta, *lse2;
+    float *ndelta, *lse2;
 };
 
 BwdPtrs bwd_ptrs(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
@@ -574,7 +683,7 @@ BwdPtrs bwd_ptrs(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const
     BwdPtrs b;
     b.dO = dO; b.Q = Q; b.K = K; b.V = V; b.O = O; b.LSE = LSE;
     b.dQ = dQ; b.dK = dK; b.dV = dV;
-    b.delta = reinterpret_cast<float *>(static_cast<char *>(ws) + L.delta_off);
+    b.ndelta = reinterpret_cast<float *>(static_cast<char *>(ws) + L.delta_off);
     b.lse2 = reinterpret_cast<float *>(static_cast<char *>(ws) + L.lse2_off);
     return b;
 }
@@ -585,7 +694,7 @@ hipError_t prep_d(const Problem &pr, const BwdPtrs &b)
     const long rows = (long)pr.B * pr.H * pr.N;
     const long threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       pr.stream, b.dO, b.O, b.LSE, b.delta, b.lse2, rows);
+                       pr.stream, b.dO, b.O, b.LSE, b.ndelta, b.lse2, rows);
     return hipGetLastError();
 }
 
@@ -594,7 +703,7 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
 {
     DqParams qp{};
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
-    qp.delta = b.delta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
+    qp.ndelta = b.ndelta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
     qp.nqb = (pr.N + BwdShape<D, false>::ROWS - 1) / BwdShape<D, false>::ROWS;
     qp.nkt = (pr.N + 63) / 64;
@@ -613,7 +722,7 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
 {
     DkvParams kp{};
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
-    kp.delta = b.delta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
+    kp.ndelta = b.ndelta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
     kp.nkb = (pr.N + BwdShape<D, true>::ROWS - 1) / BwdShape<D, true>::ROWS;
     kp.nqt = (pr.N + 63) / 64;

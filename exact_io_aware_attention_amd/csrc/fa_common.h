@@ -56,6 +56,24 @@ __device__ __forceinline__ void mfma_acc_agpr(f32x16 &acc, bf16x8 a, bf16x8 b)
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// The same, as a volatile statement: kept in program order with the other
+// volatile statements (slot_done below), for hand-scheduled loops.
+__device__ __forceinline__ void mfma_acc_agpr_ordered(f32x16 &acc, bf16x8 a, bf16x8 b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Marks a value as needed at this point of a hand-scheduled loop: code that
+// computes it cannot be sunk past the next ordered MFMA.
+__device__ __forceinline__ void slot_done(float x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void slot_done(bf16x8 x)
+{
+    asm volatile("" ::"v"(x));
+}
+
 // Wait states between the last AGPR-accumulating MFMA and any vector
 // instruction that reads its accumulator (more than the 8-pass MFMA needs).
 __device__ __forceinline__ void mfma_drain()
@@ -63,6 +81,15 @@ __device__ __forceinline__ void mfma_drain()
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Re-defines an accumulator in place, after mfma_drain(): copies the compiler
+// makes of it (to VGPRs for the epilogue, or at a control-flow join) then read
+// this value, which exists only once the wait states have passed, instead of
+// the MFMA result the compiler cannot see is still in flight.
+__device__ __forceinline__ void mfma_settle(f32x16 &acc)
+{
+    asm volatile("" : "+a"(acc));
 }
 
 // Eight consecutive bf16 values from LDS (16-byte aligned address).

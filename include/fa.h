@@ -96,8 +96,9 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V,
  * themselves (e.g. fa_bwd_dq and fa_bwd_dkdv on two streams) or time them.
  * fa_bwd_prep must complete on a workspace before fa_bwd_dq / fa_bwd_dkdv
  * read it; those two are independent of each other. Arguments as in fa_bwd.
- *   fa_bwd_prep: reads dO, O, LSE; writes D_i = sum_k dO_ik O_ik and
- *                LSE_i * log2(e) into the workspace.
+ *   fa_bwd_prep: reads dO, O, LSE; writes the row statistics the other two
+ *                read (-D_i with D_i = sum_k dO_ik O_ik, and LSE_i * log2(e))
+ *                into the workspace.
  *   fa_bwd_dq:   reads dO, Q, K, V and the workspace; writes dQ.
  *   fa_bwd_dkdv: reads dO, Q, K, V and the workspace; writes dK and dV. */
 fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE,
