@@ -104,9 +104,7 @@ __device__ __forceinline__ void issue_rows_tile(const uint16_t *src, uint16_t *d
         const int r = b * (64 / CPR) + lane / CPR;
         const int lc = (lane % CPR) ^ tile_swz<D>(r);
         const int row = min(row0 + r, N - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)row * D + 8 * lc),
-                                         (__attribute__((address_space(3))) void *)(dst + b * 512), 16,
-                                         0, 0);
+        lds_dma_b128(src + (size_t)row * D + 8 * lc, lds_byte_addr(dst) + b * 1024);
     }
 }
 
@@ -114,8 +112,7 @@ __device__ __forceinline__ void issue_rows_tile(const uint16_t *src, uint16_t *d
 __device__ __forceinline__ void issue_vec64(const float *src, float *dst, int row0, int N, int lane)
 {
     const int row = min(row0 + lane, N - 1);
-    __builtin_amdgcn_global_load_lds((const void *)(src + row), (__attribute__((address_space(3))) void *)dst,
-                                     4, 0, 0);
+    lds_dma_b32(src + row, lds_byte_addr(dst));
 }
 
 // b128 operand read: row r, logical chunk c of a swizzled tile.
@@ -269,6 +266,17 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         issue_rows_tile<D, W>(Kh, Ks[0], t * BC, N, wave, lane);
         issue_rows_tile<D, W>(Vh, Vs[0], t * BC, N, wave, lane);
     }
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            wait_loaded(qf[qb][kk]);
+            wait_loaded(gf[qb][kk]);
+        }
+        wait_loaded(lse2[qb]);
+        wait_loaded(nDi[qb]);
+    }
+    lds_dma_wait<0>();
     __syncthreads();
     int buf = 0;
     while (t < t_end) {
@@ -333,6 +341,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         }
         // before the loop edges, where the compiler may move accumulators
         mfma_drain();
+        lds_dma_wait<0>();  // the next tile has landed (all waves: barrier)
         __syncthreads();
         buf ^= 1;
         t = tn;
@@ -604,6 +613,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         t = next_tile(t);
     if (t < p.nqt) {
         issue_tile(t, 0);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                wait_loaded(kf[kb][kk]);
+                wait_loaded(vf[kb][kk]);
+            }
+        lds_dma_wait<0>();
         __syncthreads();
         int j = 0;
         // Whether this wave's elements of tile t need the element mask.
@@ -622,6 +639,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             step(mtag, bc, 0, qbase);
             step(mtag, bc, 1, qbase + 32);
             mfma_drain();  // before the loop edges, where accumulators may be moved
+            lds_dma_wait<0>();
             __syncthreads();
             t = tn;
             ++j;

@@ -74,6 +74,18 @@ __device__ __forceinline__ void slot_done(bf16x8 x)
     asm volatile("" ::"v"(x));
 }
 
+// Uses a register value here, so that the compiler waits for the load that
+// produced it here (before a loop) rather than at its first use inside the
+// loop, where that wait would also stall on the loop's own prefetches.
+__device__ __forceinline__ void wait_loaded(const bf16x8 &x)
+{
+    asm volatile("" ::"v"(x));
+}
+__device__ __forceinline__ void wait_loaded(float x)
+{
+    asm volatile("" ::"v"(x));
+}
+
 // Wait states between the last AGPR-accumulating MFMA and any vector
 // instruction that reads its accumulator (more than the 8-pass MFMA needs).
 __device__ __forceinline__ void mfma_drain()
@@ -90,6 +102,35 @@ __device__ __forceinline__ void mfma_drain()
 __device__ __forceinline__ void mfma_settle(f32x16 &acc)
 {
     asm volatile("" : "+a"(acc));
+}
+
+// Direct global->LDS loads (each lane's 16 or 4 bytes land at
+// lds_block + lane * size, lds_block wave-uniform), issued as asm. The
+// compiler's wait-count pass treats its own direct-load builtin as a write
+// to all of LDS and waits for it before the next LDS read of any buffer,
+// which exposes the full load latency right after a prefetch is issued;
+// asm loads are not tracked, so the caller waits (lds_dma_wait) before the
+// barrier that hands the filled buffer to the other waves.
+__device__ __forceinline__ uint32_t lds_byte_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_dma_b128(const void *gsrc, uint32_t lds_block)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+__device__ __forceinline__ void lds_dma_b32(const void *gsrc, uint32_t lds_block)
+{
+    asm volatile("global_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+// Waits until at most N of this wave's vector memory operations (the
+// direct loads included) are outstanding.
+template <int N>
+__device__ __forceinline__ void lds_dma_wait()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Eight consecutive bf16 values from LDS (16-byte aligned address).

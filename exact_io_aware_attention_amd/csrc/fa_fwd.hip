@@ -161,9 +161,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             const int r = b * (64 / CPR) + lane / CPR;
             const int lc = (lane % CPR) ^ (is_k ? k_swz(r) : v_swz(r));
             const int key = min(t * BC + r, N - 1);
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(src + (size_t)key * D + 8 * lc),
-                (__attribute__((address_space(3))) void *)(dst + b * 512), 16, 0, 0);
+            lds_dma_b128(src + (size_t)key * D + 8 * lc, lds_byte_addr(dst) + b * 1024);
         }
     };
     auto issue_k = [&](int t, int buf) { issue_tile(Kh, Ks[buf], t, true); };
@@ -238,7 +236,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     issue_v(t0, 0);
     if (t1 < t_end)
         issue_k(t1, 1);
-    __syncthreads();  // waits for the direct loads, then orders them
+    lds_dma_wait<0>();
+    __syncthreads();
 
     f32x16 s_cur;
     qk_half(Ks[0], 0, s_cur);
@@ -347,6 +346,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                 mask_half(tn * BC, s_nxt);
             s_cur = s_nxt;
         }
+        lds_dma_wait<0>();
         __syncthreads();  // tile j+1's V and tile j+2's K have landed
         t = tn;
         t1 = tnn;
