@@ -89,52 +89,94 @@ __device__ __forceinline__ int tile_swz(int r)
     return 2 * ((r / 2) % 4) + ((r / 8) % 2);  // 8 chunks per 128-byte row
 }
 
-// Issues the direct loads of one 64-row tile (row-major, d contiguous) into
-// LDS: 1 KB blocks spread over the workgroup's waves.
+// Lane-dependent parts of the addresses a wave uses on swizzled 64-row tiles,
+// computed once per kernel.
 template <int D, int W>
-__device__ __forceinline__ void issue_rows_tile(const uint16_t *src, uint16_t *dst, int row0, int N,
-                                                int wave, int lane)
-{
-    constexpr int CPR = D / 8;
-    constexpr int BLOCKS = 64 * D * 2 / 1024;
-    static_assert(BLOCKS % W == 0, "tile blocks per wave");
+struct TileLane {
+    static constexpr int KK = D / 16, DB = D / 32, CPR = D / 8;
+    static constexpr int LPW = 64 * D * 2 / 1024 / W;  // direct-load blocks per wave
+    static_assert(LPW * W * 1024 == 64 * D * 2, "tile blocks per wave");
+    uint32_t b128[KK];    // b128 operand read: row l32, logical chunk 2 kk + hi
+    uint32_t tr[DB][2];   // transpose reads: rows rl and rl + 8, columns 32 db..
+    uint32_t dma[LPW];    // direct-load source offset of block wave * LPW + i
+
+    __device__ __forceinline__ TileLane(int wave, int lane)
+    {
+        const int l32 = lane % 32, hi = lane / 32;
 #pragma unroll
-    for (int i = 0; i < BLOCKS / W; ++i) {
-        const int b = wave * (BLOCKS / W) + i;
-        const int r = b * (64 / CPR) + lane / CPR;
-        const int lc = (lane % CPR) ^ tile_swz<D>(r);
-        const int row = min(row0 + r, N - 1);
-        lds_dma_b128(src + (size_t)row * D + 8 * lc, lds_byte_addr(dst) + b * 1024);
+        for (int kk = 0; kk < KK; ++kk)
+            b128[kk] = 2 * (l32 * D + 8 * ((2 * kk + hi) ^ tile_swz<D>(l32)));
+        // Transpose read of 16 rows x 32 columns (the A operand whose k index
+        // runs over rows): lane 4t+u of 16-lane group g points at row
+        // 4 (g / 2) + t (and 8 rows further for operand slots 4..7),
+        // columns 32 db + 16 (g % 2) + 4u.
+        const int g = lane / 16, sl = lane % 16;
+        const int rl = 4 * (g / 2) + sl / 4;
+        const int cl = 2 * (g % 2) + (sl % 4) / 2, e = 4 * (sl % 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            tr[db][0] = 2 * (rl * D + 8 * ((4 * db + cl) ^ tile_swz<D>(rl)) + e);
+            tr[db][1] = 2 * ((rl + 8) * D + 8 * ((4 * db + cl) ^ tile_swz<D>(rl + 8)) + e);
+        }
+        // Direct loads: 1 KB blocks, lane l of block b writes physical chunk
+        // l % CPR of row b * (64 / CPR) + l / CPR, i.e. its logical chunk
+        // (l % CPR) ^ swz(row).
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int b = wave * LPW + i;
+            const int r = b * (64 / CPR) + lane / CPR;
+            dma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ tile_swz<D>(r)));
+        }
     }
-}
+    // Issues this wave's direct loads of rows row0.. of a row-major [N, D]
+    // matrix into the tile at LDS address `tile`; rows past the end read as
+    // zeros (the resource ends at row N).
+    __device__ __forceinline__ void load(const uint16_t *src, uint32_t tile, int row0, int N, int wave) const
+    {
+        const i32x4 rs = buffer_rsrc(src + (size_t)row0 * D, (uint32_t)(N - row0) * (2 * D));
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            lds_dma_buf_b128(rs, dma[i], tile + (wave * LPW + i) * 1024);
+    }
+};
 
-// Direct load of 64 consecutive floats (one wave): row-vector statistics.
-__device__ __forceinline__ void issue_vec64(const float *src, float *dst, int row0, int N, int lane)
-{
-    const int row = min(row0 + lane, N - 1);
-    lds_dma_b32(src + row, lds_byte_addr(dst));
-}
-
-// b128 operand read: row r, logical chunk c of a swizzled tile.
+// Operand addresses of one tile slot: the slot's LDS base plus the lane
+// offsets, one register per pattern; reads add compile-time row and tensor
+// offsets through the instruction's offset field.
 template <int D>
-__device__ __forceinline__ bf16x8 tile_b128(const uint16_t *t, int r, int c)
-{
-    return lds_read_b128(t + r * D + 8 * (c ^ tile_swz<D>(r)));
-}
+struct SlotAddr {
+    uint32_t b128[D / 16];
+    uint32_t tr[D / 32][2];
+    template <int W>
+    __device__ __forceinline__ void set(const TileLane<D, W> &tl, uint32_t slot)
+    {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            b128[kk] = opaque_addr(slot + tl.b128[kk]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            tr[db][0] = opaque_addr(slot + tl.tr[db][0]);
+            tr[db][1] = opaque_addr(slot + tl.tr[db][1]);
+        }
+    }
+    // b128 operand of row 32 rb + l32 of the tile at byte offset `off` in the slot
+    __device__ __forceinline__ bf16x8 b128_at(uint32_t off, int rb, int kk) const
+    {
+        return lds_b128_at(b128[kk] + off + 2 * 32 * rb * D);
+    }
+    // transpose operand of rows r0.. (a multiple of 16), columns 32 db..
+    __device__ __forceinline__ bf16x8 tr_at(uint32_t off, int r0, int db) const
+    {
+        return lds_tr_pair_at(tr[db][0] + off + 2 * r0 * D, tr[db][1] + off + 2 * r0 * D);
+    }
+};
 
-// Transpose-read operand (32 columns x 16 rows, as the A operand whose k
-// index runs over rows): lane 4t+u of 16-lane group g points at row
-// r0 + 4*(g/2) + t (and r0 + 8 + ... for slots 4..7), columns
-// col0 + 16*(g%2) + 4u.
-template <int D>
-__device__ __forceinline__ bf16x8 tile_tr(const uint16_t *t, int r0, int col0, int lane)
+// Direct load of 64 consecutive floats (one wave): row-vector statistics;
+// entries past the end read as zeros.
+__device__ __forceinline__ void load_vec64(const float *src, uint32_t dst, int row0, int N, int lane)
 {
-    const int g = lane / 16, sl = lane % 16;
-    const int r = r0 + 4 * (g / 2) + sl / 4;
-    const int col = col0 + 16 * (g % 2) + 4 * (sl % 4);
-    const int c = col / 8, e = col % 8;
-    return lds_read_tr_pair(t + r * D + 8 * (c ^ tile_swz<D>(r)) + e,
-                            t + (r + 8) * D + 8 * (c ^ tile_swz<D>(r + 8)) + e);
+    const i32x4 rs = buffer_rsrc(src + row0, (uint32_t)(N - row0) * 4);
+    lds_dma_buf_b32(rs, 4 * lane, dst);
 }
 
 // Stores a 32-row accumulator block (lane = row, registers = 32 columns in
@@ -164,89 +206,92 @@ struct DqParams {
     float c, scale;
 };
 
-// One workgroup owns 256 query rows of one (b, h) (64 per wave, Q and dO
-// rows held as MFMA B operands); key/value tiles of 64 stream through LDS.
-// Per 32 keys: S^T = K Q^T and dP^T = V dO^T (lane = query), then
-// dS^T = P^T o (dP^T - D) with P^T = 2^(c s - lse2), then
-// dQ^T += K^T dS^T with K^T from transpose reads of the K tile.
-// Waves per workgroup and 32-row MFMA blocks per wave. The dK/dV kernel
-// holds K and V operands, two accumulators per block and two pipelined steps
-// of S, dP, P and dS, which only fit the register file with one block per
-// wave; its workgroup then covers 128 keys, one block-mask column.
-template <int D, bool DKDV>
+// Rows per wave and per workgroup of both main kernels: 4 waves (one per
+// SIMD) of 32 rows. Each kernel holds its row operands in registers, a
+// long-lived accumulator pair or single in AGPRs and two pipelined steps of
+// S, dP and dS, which only fit the register file at 32 rows per wave; the
+// workgroup then covers 128 rows, one block-mask row or column, so a tile it
+// visits is kept for all of its waves.
 struct BwdShape {
     static constexpr int W = 4;
-    static constexpr int NB = (D == 128 || DKDV) ? 1 : 2;
-    static constexpr int ROWS = 32 * NB * W;  // rows per workgroup
+    static constexpr int ROWS = 32 * W;  // rows per workgroup
+    static_assert(ROWS == kMaskBlock, "one mask block per workgroup");
 };
 
+// One workgroup owns 128 query rows of one (b, h) (32 per wave, Q and dO
+// rows held as MFMA B operands); key/value tiles of 64 stream through LDS.
+// Per 32 keys (a step):
+//   A: S^T = K Q^T and dP^T = V dO^T (lane = query, MFMA);
+//   B: P^T = 2^(c s - lse2), dS^T = P^T o (dP^T - D) (vector ALU);
+//   C: dQ^T += K^T dS^T (MFMA, K^T by transpose reads; accumulator in
+//      AGPRs).
+// The steps are software-pipelined by hand: step i runs A(i) with B(i-1)
+// spread over its MFMA slots, then C(i-1) (C has half as many MFMAs as A,
+// too few to hide B). C reads the previous step's K tile, so K tiles are
+// triple-buffered.
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
 {
-    static_assert(BwdShape<D, false>::W * 64 == 256, "launch bounds");
-    constexpr int W = BwdShape<D, false>::W;
-    constexpr int NB = BwdShape<D, false>::NB;
-    constexpr int QW = 32 * NB;     // query rows per wave
-    constexpr int BR = W * QW;      // query rows per workgroup
-    constexpr int BC = 64;          // keys per LDS tile
+    static_assert(BwdShape::W * 64 == 256, "launch bounds");
+    constexpr int W = BwdShape::W;
+    constexpr int BR = BwdShape::ROWS;  // query rows per workgroup
+    constexpr int BC = 64;              // keys per LDS tile
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = BC * D;
+    constexpr int NPR = 2 * DB;          // K^T transpose operands per step
+    constexpr int PA = D == 128 ? 3 : 2; // A operand reads issued this many slots ahead
+    constexpr int PD = D == 128 ? 3 : 2; // C operands issued this many slots ahead
+    static_assert(PA <= KK && PD <= KK, "slot plan");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
+    // LDS: three slots of [K tile | V tile].
+    constexpr uint32_t TB = TILE * 2;  // bytes per tile
+    constexpr uint32_t SLOT = 2 * TB, K_OFF = 0, V_OFF = TB;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * SLOT];
+    const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
         return;
     const int bh = item / p.nqb;
     const int qi = item - bh * p.nqb;
-    const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;
+    const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;  // causal: heaviest blocks first
     const int q0 = qblk * BR;
     const int N = p.N;
+    const float c = p.c;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int lane = tid % kWave;
     const int l32 = lane % 32;
     const int hi = lane / 32;
-    const int wr0 = q0 + wave * QW;
+    const int wr0 = q0 + wave * 32;
+    const int row = wr0 + l32;  // this lane's query row
+    const TileLane<D, W> tl(wave, lane);
 
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
 
-    bf16x8 qf[NB][KK], gf[NB][KK];
-    float lse2[NB], nDi[NB];
+    bf16x8 qf[KK], gf[KK];
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-        const int row = wr0 + 32 * qb + l32;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            qf[qb][kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
-                                 : bf16x8{};
-            gf[qb][kk] = row < N ? *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * D + 16 * kk + 8 * hi)
-                                 : bf16x8{};
-        }
-        lse2[qb] = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
-        nDi[qb] = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
+    for (int kk = 0; kk < KK; ++kk) {
+        qf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
+                         : bf16x8{};
+        gf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * D + 16 * kk + 8 * hi)
+                         : bf16x8{};
     }
+    const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
+    const float nDi = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
 
     int t_end = p.nkt;
     if (CAUSAL)
         t_end = min(p.nkt, (q0 + BR - 1) / BC + 1);
-    const int mr_lo = q0 / kMaskBlock;
-    const int mr_hi = min(q0 + BR - 1, N - 1) / kMaskBlock;
-    const int wmr = min(wr0, N - 1) / kMaskBlock;  // <= 64 rows: one mask row per wave
-    auto tile_needed = [&](int t) -> bool {
-        if (!SPARSE)
-            return true;
-        bool keep = false;
-        for (int mr = mr_lo; mr <= mr_hi; ++mr)
-            keep |= p.mask[(size_t)mr * p.nmb + (t * BC) / kMaskBlock] != 0;
-        return keep;
+    const int mrow = q0 / kMaskBlock;
+    auto tile_needed = [&](int t) __attribute__((always_inline)) -> bool {
+        return !SPARSE || p.mask[(size_t)mrow * p.nmb + (t * BC) / kMaskBlock] != 0;
     };
-    auto next_tile = [&](int t) -> int {
+    auto next_tile = [&](int t) __attribute__((always_inline)) -> int {
         ++t;
         if (SPARSE)
             while (t < t_end && !tile_needed(t))
@@ -254,114 +299,178 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         return t;
     };
 
-    f32x16 dq[NB][DB];
+    f32x16 dq[DB];
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb)
+    for (int db = 0; db < DB; ++db)
+        dq[db] = f32x16{};
+
+    // S^T and dP^T of the previous step (fp32), its first key and where its
+    // K rows are. Before the first step: S = -inf, so that its P, dS and
+    // dQ^T update are zero (on valid K data).
+    f32x16 s_prev, dp_prev = f32x16{};
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            dq[qb][db] = f32x16{};
+    for (int r = 0; r < 16; ++r)
+        s_prev[r] = -INFINITY;
+    int key0_prev = 0;
+    // Operand addresses of the current tile's slot and of the previous
+    // step's slot (C reads). The previous step of step kh is step 1 - kh
+    // (before the first step its weights are zero and it reads valid rows
+    // of slot 0).
+    SlotAddr<D> cur, prev;
+    prev.set(tl, lds0);
+
+    // K^T operand pr = (hh, db) of a step: 32 columns x 16 keys starting at
+    // key 32 kh + 16 hh of the tile.
+    auto read_kt = [&](const SlotAddr<D> &sa, int kh, int pr) __attribute__((always_inline)) -> bf16x8 {
+        const int hh = pr / DB, db = pr % DB;
+        return sa.tr_at(K_OFF, 32 * kh + 16 * hh, db);
+    };
+
+    // Softmax element r of the previous step: dS^T = P^T o (dP^T - D).
+    // MASKED applies the element mask: key past the end or above the query
+    // (causal). Packs each 8 finished elements into an MFMA operand.
+    bf16x8 sb[2];
+    float dsm[16];
+    auto softmax_elem = [&](auto mtag, int r) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        float pe = exp2_fast(fmaf(s_prev[r], c, -lse2));
+        if (MASKED) {
+            const int key = key0_prev + 8 * (r / 4) + 4 * hi + (r % 4);
+            if (key >= N || (CAUSAL && key > row))
+                pe = 0.f;
+        }
+        dsm[r] = pe * (dp_prev[r] + nDi);
+        if (r % 8 == 7) {
+            bf16x8 sk;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sk[i] = (__bf16)dsm[8 * (r / 8) + i];
+            sb[r / 8] = sk;
+            slot_done(sk);
+        } else {
+            slot_done(dsm[r]);
+        }
+    };
+
+    // One step: keys 32 kh.. of the tile in the current slot, first key
+    // key0; `ps` holds the previous step's slot addresses. Runs A of this
+    // step with B of the previous step spread
+    // over its MFMA slots, then C of the previous step. B uses the mask
+    // variant of this tile: masked tiles only ever follow masked ones (the
+    // masked tiles, diagonal and ragged end, are the last of the sequence),
+    // and masking an unmasked step changes nothing.
+    auto step = [&](auto mtag, int kh, int key0, const SlotAddr<D> &ps) __attribute__((always_inline)) {
+        constexpr int EPS = 16 / (2 * KK);  // B elements per A slot
+        static_assert(EPS * 2 * KK == 16, "elements per slot");
+        bf16x8 ka[KK], va[KK];
+#pragma unroll
+        for (int kk = 0; kk < PA; ++kk) {
+            ka[kk] = cur.b128_at(K_OFF, kh, kk);
+            va[kk] = cur.b128_at(V_OFF, kh, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- A(i) beside B(i-1), the first C(i-1) operands issued behind
+        f32x16 s, dp;
+        bf16x8 kt[NPR];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            s = mfma32x32x16(ka[kk], qf[kk], kk == 0 ? f32x16{} : s);
+            if (kk + PA < KK)
+                ka[kk + PA] = cur.b128_at(K_OFF, kh, kk + PA);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e)
+                softmax_elem(mtag, (2 * kk) * EPS + e);
+            __builtin_amdgcn_sched_barrier(0);
+            dp = mfma32x32x16(va[kk], gf[kk], kk == 0 ? f32x16{} : dp);
+            if (kk + PA < KK)
+                va[kk + PA] = cur.b128_at(V_OFF, kh, kk + PA);
+            if (kk >= KK - PD)
+                kt[kk - (KK - PD)] = read_kt(ps, 1 - kh, kk - (KK - PD));
+#pragma unroll
+            for (int e = 0; e < EPS; ++e)
+                softmax_elem(mtag, (2 * kk + 1) * EPS + e);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- C(i-1)
+#pragma unroll
+        for (int pr = 0; pr < NPR; ++pr) {
+            mfma_acc_agpr_ordered(dq[pr % DB], kt[pr], sb[pr / DB]);
+            if (pr + PD < NPR)
+                kt[pr + PD] = read_kt(ps, 1 - kh, pr + PD);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        s_prev = s;
+        dp_prev = dp;
+        key0_prev = key0;
+    };
 
     int t = next_tile(-1);
     if (t < t_end) {
-        issue_rows_tile<D, W>(Kh, Ks[0], t * BC, N, wave, lane);
-        issue_rows_tile<D, W>(Vh, Vs[0], t * BC, N, wave, lane);
-    }
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
+        tl.load(Kh, lds0 + K_OFF, t * BC, N, wave);
+        tl.load(Vh, lds0 + V_OFF, t * BC, N, wave);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            wait_loaded(qf[qb][kk]);
-            wait_loaded(gf[qb][kk]);
+            wait_loaded(qf[kk]);
+            wait_loaded(gf[kk]);
         }
-        wait_loaded(lse2[qb]);
-        wait_loaded(nDi[qb]);
-    }
-    lds_dma_wait<0>();
-    __syncthreads();
-    int buf = 0;
-    while (t < t_end) {
-        const int tn = next_tile(t);
-        if (tn < t_end) {
-            issue_rows_tile<D, W>(Kh, Ks[buf ^ 1], tn * BC, N, wave, lane);
-            issue_rows_tile<D, W>(Vh, Vs[buf ^ 1], tn * BC, N, wave, lane);
-        }
-        const int kbase = t * BC;
-        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
-        {
-            const uint16_t *ks = Ks[buf];
-            const uint16_t *vs = Vs[buf];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                f32x16 s[NB], dp[NB];
-#pragma unroll
-                for (int qb = 0; qb < NB; ++qb)
-                    s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 ka = tile_b128<D>(ks, 32 * kh + l32, 2 * kk + hi);
-                    const bf16x8 va = tile_b128<D>(vs, 32 * kh + l32, 2 * kk + hi);
-#pragma unroll
-                    for (int qb = 0; qb < NB; ++qb) {
-                        s[qb] = mfma32x32x16(ka, qf[qb][kk], s[qb]);
-                        dp[qb] = mfma32x32x16(va, gf[qb][kk], dp[qb]);
-                    }
-                }
-                const int k0 = kbase + 32 * kh;
-                const bool need_mask = drop || (k0 + 32 > N) || (CAUSAL && k0 + 31 > wr0);
-                bf16x8 sb[NB][2];
-#pragma unroll
-                for (int qb = 0; qb < NB; ++qb) {
-                    const int row = wr0 + 32 * qb + l32;
-                    f32x16 ds;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float pr = exp2_fast(fmaf(s[qb][r], p.c, -lse2[qb]));
-                        if (need_mask) {
-                            const int key = k0 + 8 * (r / 4) + 4 * hi + (r % 4);
-                            if (drop || key >= N || (CAUSAL && key > row))
-                                pr = 0.f;
-                        }
-                        ds[r] = pr * (dp[qb][r] + nDi[qb]);
-                    }
-                    sb[qb][0] = pack_bf16x8(ds, 0);
-                    sb[qb][1] = pack_bf16x8(ds, 1);
-                }
-                // dQ^T += K^T dS^T: K^T (32 d x 16 keys) by transpose reads,
-                // one read per NB MFMAs.
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 kt = tile_tr<D>(ks, 32 * kh + 16 * hh, 32 * db, lane);
-#pragma unroll
-                        for (int qb = 0; qb < NB; ++qb)
-                            mfma_acc_agpr(dq[qb][db], kt, sb[qb][hh]);
-                    }
-            }
-        }
-        // before the loop edges, where the compiler may move accumulators
-        mfma_drain();
-        lds_dma_wait<0>();  // the next tile has landed (all waves: barrier)
+        wait_loaded(lse2);
+        wait_loaded(nDi);
+        lds_dma_wait<0>();
         __syncthreads();
-        buf ^= 1;
-        t = tn;
+        int j = 0;
+        // Whether this wave's elements of tile t need the element mask.
+        auto tile_masked = [&](int t) __attribute__((always_inline)) -> bool {
+            const int kbase = t * BC;
+            return (kbase + BC > N) || (CAUSAL && kbase + BC - 1 > wr0);
+        };
+        // One tile: its two steps, then the barrier after which tile t+1 has
+        // landed; K buffer (j+2)%3 and V buffer j%2 are then free.
+        auto tile = [&](auto mtag) __attribute__((always_inline)) {
+            const int tn = next_tile(t);
+            if (tn < t_end) {
+                tl.load(Kh, lds0 + ((j + 1) % 3) * SLOT + K_OFF, tn * BC, N, wave);
+                tl.load(Vh, lds0 + ((j + 1) % 3) * SLOT + V_OFF, tn * BC, N, wave);
+            }
+            const int kbase = t * BC;
+            cur.set(tl, lds0 + (j % 3) * SLOT);
+            step(mtag, 0, kbase, prev);
+            step(mtag, 1, kbase + 32, cur);
+            prev = cur;
+            mfma_drain();  // before the loop edges, where accumulators may be moved
+            lds_dma_wait<0>();
+            __syncthreads();
+            t = tn;
+            ++j;
+        };
+        // Runs of masked and unmasked tiles each get a loop of their own, so
+        // the hot loop has no join (causal: the masked tiles are the last
+        // ones, on the diagonal).
+        while (t < t_end) {
+            while (t < t_end && !tile_masked(t))
+                tile(std::false_type{});
+            while (t < t_end && tile_masked(t))
+                tile(std::true_type{});
+        }
+        // B and C of the last step
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            softmax_elem(std::true_type{}, r);
+#pragma unroll
+        for (int pr = 0; pr < NPR; ++pr)
+            mfma_acc_agpr_ordered(dq[pr % DB], read_kt(prev, 1, pr), sb[pr / DB]);
+        mfma_drain();
     }
 
-    mfma_drain();
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb)
+    for (int db = 0; db < DB; ++db)
+        mfma_settle(dq[db]);
+    if (row < N) {
+        uint16_t *dst = p.dQ + head + (size_t)row * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            mfma_settle(dq[qb][db]);
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-        const int row = wr0 + 32 * qb + l32;
-        if (row < N) {
-            uint16_t *dst = p.dQ + head + (size_t)row * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                store_rows_bf16(dst, dq[qb][db], 32 * db, hi, p.scale);
-        }
+            store_rows_bf16(dst, dq[db], 32 * db, hi, p.scale);
     }
 }
 
@@ -392,9 +501,9 @@ struct DkvParams {
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 {
-    static_assert(BwdShape<D, true>::W * 64 == 256, "launch bounds");
-    constexpr int W = BwdShape<D, true>::W;
-    constexpr int NB = BwdShape<D, true>::NB;
+    static_assert(BwdShape::W * 64 == 256, "launch bounds");
+    constexpr int W = BwdShape::W;
+    constexpr int NB = 1;
     constexpr int KW = 32 * NB;     // keys per wave
     constexpr int BK = W * KW;      // keys per workgroup
     constexpr int BQ = 64;          // queries per LDS tile
@@ -402,18 +511,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     constexpr int DB = D / 32;
     constexpr int TILE = BQ * D;
     constexpr int NPR = 2 * DB;          // transpose-operand pairs (dO^T, Q^T) per step
-    constexpr int EPP = 16 * NB / NPR;   // softmax elements per pair slot
-    constexpr int PA = D == 128 ? 3 : 2; // A operand reads issued this many slots ahead
-    constexpr int PD = D == 128 ? 3 : 2; // C operand pairs issued this many slots ahead
+    constexpr int PA = D == 128 ? 3 : 2; // A operand reads issued this many MFMA pairs ahead
+    constexpr int PD = D == 128 ? 3 : 2; // C operand pairs issued this many pairs ahead
     static_assert(2 * NB * NPR == KK * NB * 2, "as many MFMAs in A as in C");
-    static_assert(PA <= KK && PD <= KK && EPP * NPR == 16 * NB && 8 % EPP == 0, "slot plan");
+    static_assert(PA <= KK && PD <= KK, "slot plan");
     // One mask column per workgroup: a tile it visits is kept for all waves.
     static_assert(BK == kMaskBlock, "workgroup keys = one mask block");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs[3][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Gs[3][TILE];
-    __shared__ __attribute__((aligned(256))) float Ls[3][BQ];
-    __shared__ __attribute__((aligned(256))) float Ds[3][BQ];
+    // LDS: three slots of [Q tile | dO tile], then lse2 and -D rows per slot.
+    constexpr uint32_t TB = TILE * 2;  // bytes per tile
+    constexpr uint32_t SLOT = 2 * TB, Q_OFF = 0, G_OFF = TB;
+    constexpr uint32_t L_OFF = 3 * SLOT, D_OFF = L_OFF + 3 * BQ * 4;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[D_OFF + 3 * BQ * 4];
+    const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
@@ -425,11 +535,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const float c = p.c;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int lane = tid % kWave;
     const int l32 = lane % 32;
     const int hi = lane / 32;
     const int wk0 = k0 + wave * KW;
+    const TileLane<D, W> tl(wave, lane);
 
     const size_t head = (size_t)bh * (size_t)N * D;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
@@ -462,12 +573,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         return t;
     };
     auto issue_tile = [&](int t, int b) __attribute__((always_inline)) {
-        issue_rows_tile<D, W>(Qh, Qs[b], t * BQ, N, wave, lane);
-        issue_rows_tile<D, W>(dOh, Gs[b], t * BQ, N, wave, lane);
+        tl.load(Qh, lds0 + b * SLOT + Q_OFF, t * BQ, N, wave);
+        tl.load(dOh, lds0 + b * SLOT + G_OFF, t * BQ, N, wave);
         if (wave == 0)
-            issue_vec64(lse2h, Ls[b], t * BQ, N, lane);
+            load_vec64(lse2h, lds0 + L_OFF + b * BQ * 4, t * BQ, N, lane);
         else if (wave == 1)
-            issue_vec64(ndh, Ds[b], t * BQ, N, lane);
+            load_vec64(ndh, lds0 + D_OFF + b * BQ * 4, t * BQ, N, lane);
     };
 
     f32x16 dk[NB][DB], dv[NB][DB];
@@ -485,14 +596,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
         pb[kb][0] = pb[kb][1] = sb[kb][0] = sb[kb][1] = bf16x8{};
-    int pbuf = 0, pqh = 0;
+    // Operand addresses of the current tile's slot (A reads, C of its first
+    // step) and of the previous step's slot (C reads). The previous step of
+    // step qh is step 1 - qh: the second step of the previous tile, or the
+    // first of this one (before the first step its weights are zero, and it
+    // reads valid rows of slot 0).
+    SlotAddr<D> cur, prev;
+    prev.set(tl, lds0);
 
     // Transpose-read operands of pair pr = (hh, db) of a step: dO^T and Q^T,
     // 32 columns x 16 queries starting at query 32 qh + 16 hh.
-    auto read_pair = [&](int b, int qh, int pr, bf16x8 &g, bf16x8 &q) __attribute__((always_inline)) {
+    auto read_pair = [&](const SlotAddr<D> &sa, int qh, int pr, bf16x8 &g, bf16x8 &q) __attribute__((always_inline)) {
         const int hh = pr / DB, db = pr % DB;
-        g = tile_tr<D>(Gs[b], 32 * qh + 16 * hh, 32 * db, lane);
-        q = tile_tr<D>(Qs[b], 32 * qh + 16 * hh, 32 * db, lane);
+        g = sa.tr_at(G_OFF, 32 * qh + 16 * hh, db);
+        q = sa.tr_at(Q_OFF, 32 * qh + 16 * hh, db);
     };
     auto c_mfmas = [&](int pr, const bf16x8 &g, const bf16x8 &q) __attribute__((always_inline)) {
         const int hh = pr / DB, db = pr % DB;
@@ -503,29 +620,27 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         }
     };
 
-    // One step: 32 queries (rows 32 qh.. of tile buffer b, first query
-    // qrow0). MASKED applies the element mask: query past the end or key
-    // above the query (causal).
-    auto step = [&](auto mtag, int b, int qh, int qrow0) __attribute__((always_inline)) {
+    // One step: 32 queries (rows 32 qh.. of the tile in slot b, first query
+    // qrow0); `ps` holds the operand addresses of the previous step's slot.
+    // MASKED applies the element mask: query past the end or key above the
+    // query (causal).
+    auto step = [&](auto mtag, int b, int qh, int qrow0, const SlotAddr<D> &ps) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
-        const uint16_t *qs = Qs[b];
-        const uint16_t *gs = Gs[b];
         // lse2 and -D of the 16 queries a lane's S/dP registers cover:
         // register r <-> query 8 (r / 4) + 4 hi + r % 4 of the step.
         float lq[16];
         f32x16 nd;
         {
-            const float *ls = Ls[b] + 32 * qh + 4 * hi;
-            const float *ds = Ds[b] + 32 * qh + 4 * hi;
+            const uint32_t st = lds0 + b * BQ * 4 + 4 * (32 * qh + 4 * hi);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 dv4 = *reinterpret_cast<const float4 *>(ds + 8 * j);
+                const f32x4 dv4 = lds_f32x4_at(st + D_OFF + 32 * j);
                 nd[4 * j + 0] = dv4.x; nd[4 * j + 1] = dv4.y;
                 nd[4 * j + 2] = dv4.z; nd[4 * j + 3] = dv4.w;
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 lv = *reinterpret_cast<const float4 *>(ls + 8 * j);
+                const f32x4 lv = lds_f32x4_at(st + L_OFF + 32 * j);
                 lq[4 * j + 0] = lv.x; lq[4 * j + 1] = lv.y;
                 lq[4 * j + 2] = lv.z; lq[4 * j + 3] = lv.w;
             }
@@ -533,12 +648,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         bf16x8 qa[KK], ga[KK];
 #pragma unroll
         for (int kk = 0; kk < PA; ++kk) {
-            qa[kk] = tile_b128<D>(qs, 32 * qh + l32, 2 * kk + hi);
-            ga[kk] = tile_b128<D>(gs, 32 * qh + l32, 2 * kk + hi);
+            qa[kk] = cur.b128_at(Q_OFF, qh, kk);
+            ga[kk] = cur.b128_at(G_OFF, qh, kk);
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- A(i), with the first C(i-1) operand pairs issued behind it
+        // ---- A(i), with the first C(i-1) operand pairs issued behind it.
+        // One MFMA per slot: a second MFMA issued right behind the first
+        // would hold up everything after it until the matrix pipe frees.
         f32x16 s[NB], dp[NB];
         bf16x8 gt[NPR], qt[NPR];
 #pragma unroll
@@ -546,55 +663,65 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb) {
                 s[kb] = mfma32x32x16(qa[kk], kf[kb][kk], kk == 0 ? f32x16{} : s[kb]);
+                if (kb == 0 && kk + PA < KK)
+                    qa[kk + PA] = cur.b128_at(Q_OFF, qh, kk + PA);
+                __builtin_amdgcn_sched_barrier(0);
                 dp[kb] = mfma32x32x16(ga[kk], vf[kb][kk], kk == 0 ? nd : dp[kb]);
+                if (kb == 0 && kk + PA < KK)
+                    ga[kk + PA] = cur.b128_at(G_OFF, qh, kk + PA);
+                if (kb == 0 && kk >= KK - PD)
+                    read_pair(ps, 1 - qh, kk - (KK - PD), gt[kk - (KK - PD)], qt[kk - (KK - PD)]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (kk + PA < KK) {
-                qa[kk + PA] = tile_b128<D>(qs, 32 * qh + l32, 2 * (kk + PA) + hi);
-                ga[kk + PA] = tile_b128<D>(gs, 32 * qh + l32, 2 * (kk + PA) + hi);
-            }
-            if (kk >= KK - PD)
-                read_pair(pbuf, pqh, kk - (KK - PD), gt[kk - (KK - PD)], qt[kk - (KK - PD)]);
-            __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- C(i-1) beside B(i)
+        // ---- C(i-1) beside B(i): one MFMA per slot, each followed by the
+        // next operand reads and its share of the softmax elements.
         bf16x8 pb2[NB][2], sb2[NB][2];
         float pm[NB][16], dsm[NB][16];
-#pragma unroll
-        for (int pr = 0; pr < NPR; ++pr) {
-            c_mfmas(pr, gt[pr], qt[pr]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (pr + PD < NPR)
-                read_pair(pbuf, pqh, pr + PD, gt[pr + PD], qt[pr + PD]);
-#pragma unroll
-            for (int e = pr * EPP; e < (pr + 1) * EPP; ++e) {
-                const int kb = e / 16, r = e % 16;
-                float pe = exp2_fast(fmaf(s[kb][r], c, -lq[r]));
-                if (MASKED) {
-                    const int key = wk0 + 32 * kb + l32;
-                    const int q = qrow0 + 8 * (r / 4) + 4 * hi + (r % 4);
-                    if (q >= N || (CAUSAL && key > q))
-                        pe = 0.f;
-                }
-                pm[kb][r] = pe;
-                dsm[kb][r] = pe * dp[kb][r];
-                if (r % 8 == 7) {
-                    const int h = r / 8;
-                    bf16x8 pk, sk;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        pk[i] = (__bf16)pm[kb][8 * h + i];
-                        sk[i] = (__bf16)dsm[kb][8 * h + i];
-                    }
-                    pb2[kb][h] = pk;
-                    sb2[kb][h] = sk;
-                    slot_done(pk);
-                    slot_done(sk);
-                } else {
-                    slot_done(pe);
-                    slot_done(dsm[kb][r]);
-                }
+        auto softmax_elem = [&](int e) __attribute__((always_inline)) {
+            const int kb = e / 16, r = e % 16;
+            float pe = exp2_fast(fmaf(s[kb][r], c, -lq[r]));
+            if (MASKED) {
+                const int key = wk0 + 32 * kb + l32;
+                const int q = qrow0 + 8 * (r / 4) + 4 * hi + (r % 4);
+                if (q >= N || (CAUSAL && key > q))
+                    pe = 0.f;
             }
+            pm[kb][r] = pe;
+            dsm[kb][r] = pe * dp[kb][r];
+            if (r % 8 == 7) {
+                const int h = r / 8;
+                bf16x8 pk, sk;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    pk[i] = (__bf16)pm[kb][8 * h + i];
+                    sk[i] = (__bf16)dsm[kb][8 * h + i];
+                }
+                pb2[kb][h] = pk;
+                sb2[kb][h] = sk;
+                slot_done(pk);
+                slot_done(sk);
+            } else {
+                slot_done(pe);
+                slot_done(dsm[kb][r]);
+            }
+        };
+        constexpr int NSLOT = 2 * NB * NPR;   // C MFMAs per step
+        constexpr int EPS = 16 * NB / NSLOT;  // softmax elements per slot
+        static_assert(EPS * NSLOT == 16 * NB, "elements per slot");
+#pragma unroll
+        for (int m = 0; m < NSLOT; ++m) {
+            const int pr = m / (2 * NB), kb = (m / 2) % NB, hh = pr / DB, db = pr % DB;
+            if (m % 2 == 0)
+                mfma_acc_agpr_ordered(dv[kb][db], gt[pr], pb[kb][hh]);
+            else
+                mfma_acc_agpr_ordered(dk[kb][db], qt[pr], sb[kb][hh]);
+            if (m % (2 * NB) == 0 && pr + PD < NPR)
+                read_pair(ps, 1 - qh, pr + PD, gt[pr + PD], qt[pr + PD]);
+#pragma unroll
+            for (int e = m * EPS; e < (m + 1) * EPS; ++e)
+                softmax_elem(e);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -604,8 +731,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                 pb[kb][h] = pb2[kb][h];
                 sb[kb][h] = sb2[kb][h];
             }
-        pbuf = b;
-        pqh = qh;
     };
 
     int t = t_begin;
@@ -636,8 +761,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             if (tn < p.nqt)
                 issue_tile(tn, (j + 1) % 3);
             const int qbase = t * BQ;
-            step(mtag, bc, 0, qbase);
-            step(mtag, bc, 1, qbase + 32);
+            cur.set(tl, lds0 + bc * SLOT);
+            step(mtag, bc, 0, qbase, prev);
+            step(mtag, bc, 1, qbase + 32, cur);
+            prev = cur;
             mfma_drain();  // before the loop edges, where accumulators may be moved
             lds_dma_wait<0>();
             __syncthreads();
@@ -658,7 +785,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 #pragma unroll
         for (int pr = 0; pr < NPR; ++pr) {
             bf16x8 g, q;
-            read_pair(pbuf, pqh, pr, g, q);
+            read_pair(prev, 1, pr, g, q);
             c_mfmas(pr, g, q);
         }
         mfma_drain();
@@ -723,7 +850,7 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
     qp.ndelta = b.ndelta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
-    qp.nqb = (pr.N + BwdShape<D, false>::ROWS - 1) / BwdShape<D, false>::ROWS;
+    qp.nqb = (pr.N + BwdShape::ROWS - 1) / BwdShape::ROWS;
     qp.nkt = (pr.N + 63) / 64;
     qp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     qp.items = pr.B * pr.H * qp.nqb;
@@ -742,7 +869,7 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
     kp.ndelta = b.ndelta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
-    kp.nkb = (pr.N + BwdShape<D, true>::ROWS - 1) / BwdShape<D, true>::ROWS;
+    kp.nkb = (pr.N + BwdShape::ROWS - 1) / BwdShape::ROWS;
     kp.nqt = (pr.N + 63) / 64;
     kp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     kp.items = pr.B * pr.H * kp.nkb;

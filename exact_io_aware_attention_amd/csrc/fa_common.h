@@ -125,6 +125,51 @@ __device__ __forceinline__ void lds_dma_b32(const void *gsrc, uint32_t lds_block
     asm volatile("global_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
+// The same with a wave-uniform base (SGPR pair) and a 32-bit per-lane byte
+// offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma_b128_at(const void *gbase, uint32_t off, uint32_t lds_block)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(gbase),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+__device__ __forceinline__ void lds_dma_b32_at(const void *gbase, uint32_t off, uint32_t lds_block)
+{
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(gbase),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+// Buffer resource for `bytes` bytes from `base` (raw, stride 0): a buffer
+// load at or past the end returns zeros instead of touching memory, which
+// lets a tile that runs past the last row be loaded without clamping.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+// Buffer direct loads into LDS (same LDS placement as above); `off` is the
+// per-lane byte offset into the resource.
+__device__ __forceinline__ void lds_dma_buf_b128(i32x4 rsrc, uint32_t off, uint32_t lds_block)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+__device__ __forceinline__ void lds_dma_buf_b32(i32x4 rsrc, uint32_t off, uint32_t lds_block)
+{
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+                 : "memory");
+}
+// An address the compiler must treat as opaque: it keeps one register for it
+// and folds the constants added to it into the LDS instruction's offset
+// field instead of re-deriving an address per read.
+__device__ __forceinline__ uint32_t opaque_addr(uint32_t x)
+{
+    asm("" : "+v"(x));
+    return x;
+}
 // Waits until at most N of this wave's vector memory operations (the
 // direct loads included) are outstanding.
 template <int N>
@@ -137,6 +182,27 @@ __device__ __forceinline__ void lds_dma_wait()
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t *p)
 {
     return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Reads at LDS byte addresses (a constant part of the address is folded into
+// the instruction's offset field).
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+__device__ __forceinline__ bf16x8 lds_b128_at(uint32_t a)
+{
+    return *(const lds_bf16x8 *)(size_t)a;
+}
+__device__ __forceinline__ f32x4 lds_f32x4_at(uint32_t a)
+{
+    return *(const lds_f32x4 *)(size_t)a;
+}
+__device__ __forceinline__ bf16x8 lds_tr_pair_at(uint32_t a0, uint32_t a1)
+{
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)a0);
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(size_t)a1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
 }
 
 // Two transpose reads (4 + 4 values) forming one 8-slot MFMA operand.
