@@ -73,20 +73,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const 
 // accumulators (dQ^T, or dK^T and dV^T) stay in AGPRs; operands, S, dP and
 // the softmax temporaries use the VGPRs.
 //
-// Tiles of 64 rows stream through LDS by direct global->LDS loads (rows past
-// the end of the sequence are loaded from the last row and masked). The
-// row-major tiles are read two ways: b128 operand reads (16 consecutive rows
-// per LDS cycle) and transpose reads (4 consecutive rows x 32 bytes per 16
-// lanes). The swizzle f(r) below stores logical 16-byte chunk c of row r at
-// chunk c ^ f(r); f is a bijection on any 16 consecutive rows (b128 reads
-// conflict-free) and f(r) / 2 differs across any 4 aligned rows (transpose
-// reads conflict-free).
+// Tiles of 64 rows stream through LDS by direct loads (rows past the end of
+// the sequence read as zeros and are masked). The row-major tiles are read
+// two ways: b128 operand reads (16 consecutive rows per LDS cycle) and
+// transpose reads (4 consecutive rows x 64 bytes per 32 lanes). The swizzle
+// f(r) below stores logical 16-byte chunk c of row r at chunk c ^ f(r). For
+// d = 128, f is a bijection on any 16 consecutive rows (b128 reads hit 16
+// distinct 4-bank groups) and f(r) / 4 differs across any 4 aligned rows (the
+// aligned 4-chunk blocks a transpose read touches land in distinct banks);
+// for d = 64 (two rows per 256-byte bank cycle) the same holds with the row
+// parity taking the place of one bit.
 template <int D>
 __device__ __forceinline__ int tile_swz(int r)
 {
     if (D == 128)  // 16 chunks per 256-byte row
-        return 2 * (r % 4) + 8 * ((r / 4) % 2) + ((r / 8) % 2);
-    return 2 * ((r / 2) % 4) + ((r / 8) % 2);  // 8 chunks per 128-byte row
+        return 4 * (r % 4) + (r / 4) % 4;
+    return 4 * ((r / 2) % 2) + (r / 4) % 4;  // 8 chunks per 128-byte row
 }
 
 // Lane-dependent parts of the addresses a wave uses on swizzled 64-row tiles,
@@ -133,10 +135,19 @@ struct TileLane {
     // zeros (the resource ends at row N).
     __device__ __forceinline__ void load(const uint16_t *src, uint32_t tile, int row0, int N, int wave) const
     {
-        const i32x4 rs = buffer_rsrc(src + (size_t)row0 * D, (uint32_t)(N - row0) * (2 * D));
+        const i32x4 rs = rsrc(src, row0, N);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
-            lds_dma_buf_b128(rs, dma[i], tile + (wave * LPW + i) * 1024);
+            load_block(rs, tile, wave, i);
+    }
+    __device__ __forceinline__ static i32x4 rsrc(const uint16_t *src, int row0, int N)
+    {
+        return buffer_rsrc(src + (size_t)row0 * D, (uint32_t)(N - row0) * (2 * D));
+    }
+    // The i-th of this wave's LPW loads of a tile (for spreading them out).
+    __device__ __forceinline__ void load_block(const i32x4 &rs, uint32_t tile, int wave, int i) const
+    {
+        lds_dma_buf_b128(rs, dma[i], tile + (wave * LPW + i) * 1024);
     }
 };
 
@@ -624,7 +635,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     // qrow0); `ps` holds the operand addresses of the previous step's slot.
     // MASKED applies the element mask: query past the end or key above the
     // query (causal).
-    auto step = [&](auto mtag, int b, int qh, int qrow0, const SlotAddr<D> &ps) __attribute__((always_inline)) {
+    auto step = [&](auto mtag, int b, int qh, int qrow0, const SlotAddr<D> &ps, auto &&hook) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
         // lse2 and -D of the 16 queries a lane's S/dP registers cover:
         // register r <-> query 8 (r / 4) + 4 hi + r % 4 of the step.
@@ -665,23 +676,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                 s[kb] = mfma32x32x16(qa[kk], kf[kb][kk], kk == 0 ? f32x16{} : s[kb]);
                 if (kb == 0 && kk + PA < KK)
                     qa[kk + PA] = cur.b128_at(Q_OFF, qh, kk + PA);
+                hook(2 * (kk * NB + kb));
                 __builtin_amdgcn_sched_barrier(0);
                 dp[kb] = mfma32x32x16(ga[kk], vf[kb][kk], kk == 0 ? nd : dp[kb]);
                 if (kb == 0 && kk + PA < KK)
                     ga[kk + PA] = cur.b128_at(G_OFF, qh, kk + PA);
                 if (kb == 0 && kk >= KK - PD)
                     read_pair(ps, 1 - qh, kk - (KK - PD), gt[kk - (KK - PD)], qt[kk - (KK - PD)]);
+                hook(2 * (kk * NB + kb) + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 
         // ---- C(i-1) beside B(i): one MFMA per slot, each followed by the
-        // next operand reads and its share of the softmax elements.
+        // next operand reads and its share of the softmax. The softmax of an
+        // element is itself pipelined over three slots (exponent argument,
+        // exponential, product and packing), so no slot waits on a result
+        // it produced itself.
         bf16x8 pb2[NB][2], sb2[NB][2];
-        float pm[NB][16], dsm[NB][16];
-        auto softmax_elem = [&](int e) __attribute__((always_inline)) {
+        float tx[NB][16], pm[NB][16], dsm[NB][16];
+        auto stage_f = [&](int e) __attribute__((always_inline)) {
             const int kb = e / 16, r = e % 16;
-            float pe = exp2_fast(fmaf(s[kb][r], c, -lq[r]));
+            tx[kb][r] = fmaf(s[kb][r], c, -lq[r]);
+            slot_done(tx[kb][r]);
+        };
+        auto stage_e = [&](int e) __attribute__((always_inline)) {
+            const int kb = e / 16, r = e % 16;
+            float pe = exp2_fast(tx[kb][r]);
             if (MASKED) {
                 const int key = wk0 + 32 * kb + l32;
                 const int q = qrow0 + 8 * (r / 4) + 4 * hi + (r % 4);
@@ -689,7 +710,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                     pe = 0.f;
             }
             pm[kb][r] = pe;
-            dsm[kb][r] = pe * dp[kb][r];
+            slot_done(pe);
+        };
+        auto stage_m = [&](int e) __attribute__((always_inline)) {
+            const int kb = e / 16, r = e % 16;
+            dsm[kb][r] = pm[kb][r] * dp[kb][r];
             if (r % 8 == 7) {
                 const int h = r / 8;
                 bf16x8 pk, sk;
@@ -703,7 +728,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                 slot_done(pk);
                 slot_done(sk);
             } else {
-                slot_done(pe);
                 slot_done(dsm[kb][r]);
             }
         };
@@ -711,17 +735,29 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         constexpr int EPS = 16 * NB / NSLOT;  // softmax elements per slot
         static_assert(EPS * NSLOT == 16 * NB, "elements per slot");
 #pragma unroll
-        for (int m = 0; m < NSLOT; ++m) {
-            const int pr = m / (2 * NB), kb = (m / 2) % NB, hh = pr / DB, db = pr % DB;
-            if (m % 2 == 0)
-                mfma_acc_agpr_ordered(dv[kb][db], gt[pr], pb[kb][hh]);
-            else
-                mfma_acc_agpr_ordered(dk[kb][db], qt[pr], sb[kb][hh]);
-            if (m % (2 * NB) == 0 && pr + PD < NPR)
-                read_pair(ps, 1 - qh, pr + PD, gt[pr + PD], qt[pr + PD]);
+        for (int m = 0; m < NSLOT + 2; ++m) {
+            if (m < NSLOT) {
+                const int pr = m / (2 * NB), kb = (m / 2) % NB, hh = pr / DB, db = pr % DB;
+                if (m % 2 == 0)
+                    mfma_acc_agpr_ordered(dv[kb][db], gt[pr], pb[kb][hh]);
+                else
+                    mfma_acc_agpr_ordered(dk[kb][db], qt[pr], sb[kb][hh]);
+                if (m % (2 * NB) == 0 && pr + PD < NPR)
+                    read_pair(ps, 1 - qh, pr + PD, gt[pr + PD], qt[pr + PD]);
 #pragma unroll
-            for (int e = m * EPS; e < (m + 1) * EPS; ++e)
-                softmax_elem(e);
+                for (int e = m * EPS; e < (m + 1) * EPS; ++e)
+                    stage_f(e);
+            }
+            if (m >= 1 && m - 1 < NSLOT) {
+#pragma unroll
+                for (int e = (m - 1) * EPS; e < m * EPS; ++e)
+                    stage_e(e);
+            }
+            if (m >= 2) {
+#pragma unroll
+                for (int e = (m - 2) * EPS; e < (m - 1) * EPS; ++e)
+                    stage_m(e);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -758,12 +794,29 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         auto tile = [&](auto mtag) __attribute__((always_inline)) {
             const int tn = next_tile(t);
             const int bc = j % 3;
-            if (tn < p.nqt)
-                issue_tile(tn, (j + 1) % 3);
+            // Loads of the next tile into the free slot, one per A slot of
+            // the first step rather than in a burst (without a next tile the
+            // current one is loaded again, into the free slot: no branch).
+            const int tl_next = tn < p.nqt ? tn : t;
+            const uint32_t nslot = lds0 + ((j + 1) % 3) * SLOT;
+            const i32x4 rq = TileLane<D, W>::rsrc(Qh, tl_next * BQ, N);
+            const i32x4 rg = TileLane<D, W>::rsrc(dOh, tl_next * BQ, N);
+            auto dma_hook = [&](int sl) __attribute__((always_inline)) {
+                constexpr int LPW = TileLane<D, W>::LPW;
+                if (sl < LPW)
+                    tl.load_block(rq, nslot + Q_OFF, wave, sl);
+                else if (sl < 2 * LPW)
+                    tl.load_block(rg, nslot + G_OFF, wave, sl - LPW);
+                else if (sl == 2 * LPW)  // lse2 (even waves) or -D (odd waves): same bytes twice
+                    load_vec64((wave & 1) ? ndh : lse2h,
+                               lds0 + ((wave & 1) ? D_OFF : L_OFF) + ((j + 1) % 3) * BQ * 4,
+                               tl_next * BQ, N, lane);
+            };
+            auto no_hook = [](int) {};
             const int qbase = t * BQ;
             cur.set(tl, lds0 + bc * SLOT);
-            step(mtag, bc, 0, qbase, prev);
-            step(mtag, bc, 1, qbase + 32, cur);
+            step(mtag, bc, 0, qbase, prev, dma_hook);
+            step(mtag, bc, 1, qbase + 32, cur, no_hook);
             prev = cur;
             mfma_drain();  // before the loop edges, where accumulators may be moved
             lds_dma_wait<0>();
