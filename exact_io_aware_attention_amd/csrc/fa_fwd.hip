@@ -53,8 +53,10 @@
 // straddle the diagonal or the end of the sequence; block-sparse
 // (lukebest.github.io "Block-Sparse FlashAttention") -- key tiles whose
 // 128 x 128 mask block is zero for every wave of the workgroup are skipped
-// without being loaded. Rows past the end of the sequence are loaded from
-// the last row (so every load stays in bounds) and always masked.
+// without being loaded. Rows past the end of the sequence read as zeros
+// (the tile loads go through buffer resources that end at row N, so no load
+// leaves the tensor) and are always masked. Iterations that need no element
+// mask run in a loop of their own, without any mask arithmetic.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -90,8 +92,11 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     constexpr int LPW = TILE * 2 / 1024 / W;  // 1 KB direct loads per wave per tile
     static_assert(LPW >= 1, "tile too small for the direct-load layout");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks[3][TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][TILE];
+    // LDS: three K tiles, then two V tiles.
+    constexpr uint32_t TB = TILE * 2;  // bytes per tile
+    constexpr uint32_t V_OFF = 3 * TB;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 2 * TB];
+    const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item = xcd_work_item(p.per_xcd);
     if (item >= p.items)
@@ -104,7 +109,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     const float c = p.c;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int lane = tid % kWave;
     const int l32 = lane % 32;
     const int hi = lane / 32;
@@ -149,46 +154,58 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         return t;
     };
 
-    // Direct global->LDS loads: lane `lane` of 1 KB block b writes chunk
-    // `lane` of the block, i.e. row r = b * (64 / CPR) + lane / CPR, physical
-    // chunk lane % CPR, which holds logical chunk (lane % CPR) ^ swz(r).
+    // Lane-dependent byte offsets, computed once. Direct loads: lane `lane`
+    // of 1 KB block b writes chunk `lane` of the block, i.e. row
+    // r = b * (64 / CPR) + lane / CPR, physical chunk lane % CPR, which holds
+    // logical chunk (lane % CPR) ^ swz(r).
     auto k_swz = [](int r) -> int { return CPR == 16 ? (r % 16) : ((r / 2) % 8); };
     auto v_swz = [](int r) -> int { return 2 * (r % 4); };
-    auto issue_tile = [&](const uint16_t *src, uint16_t *dst, int t, bool is_k) {
+    uint32_t kdma[LPW], vdma[LPW];
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int b = wave * LPW + i;
-            const int r = b * (64 / CPR) + lane / CPR;
-            const int lc = (lane % CPR) ^ (is_k ? k_swz(r) : v_swz(r));
-            const int key = min(t * BC + r, N - 1);
-            lds_dma_b128(src + (size_t)key * D + 8 * lc, lds_byte_addr(dst) + b * 1024);
-        }
+    for (int i = 0; i < LPW; ++i) {
+        const int r = (wave * LPW + i) * (64 / CPR) + lane / CPR;
+        kdma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ k_swz(r)));
+        vdma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ v_swz(r)));
+    }
+    // Rows past the end of the sequence read as zeros (the buffer resource
+    // ends at row N) and are masked.
+    auto issue = [&](const uint16_t *src, const uint32_t (&off)[LPW], uint32_t tile, int t)
+                     __attribute__((always_inline)) {
+        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * D, (uint32_t)(N - t * BC) * (2 * D));
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            lds_dma_buf_b128(rs, off[i], tile + (wave * LPW + i) * 1024);
     };
-    auto issue_k = [&](int t, int buf) { issue_tile(Kh, Ks[buf], t, true); };
-    auto issue_v = [&](int t, int buf) { issue_tile(Vh, Vs[buf], t, false); };
+    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TB, t); };
+    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) { issue(Vh, vdma, lds0 + V_OFF + buf * TB, t); };
 
-    // K operand reads: row 32*h + l32 of the tile, logical chunk 2*kk + hi.
-    auto qk_half = [&](const uint16_t *kt, int h, f32x16 &s) {
+    // K operand reads: row 32*h + l32 of the tile, logical chunk 2*kk + hi
+    // (k_swz of row 32 h + l32 equals k_swz of l32).
+    uint32_t koff[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        koff[kk] = 2 * (l32 * D + 8 * ((2 * kk + hi) ^ k_swz(l32)));
+    auto qk_half = [&](uint32_t ktile, int h, f32x16 &s) __attribute__((always_inline)) {
         s = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int r = 32 * h + l32;
-            const int pc = (2 * kk + hi) ^ k_swz(r);
-            s = mfma32x32x16(lds_read_b128(kt + r * D + 8 * pc), qf[kk], s);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+            s = mfma32x32x16(lds_b128_at(ktile + koff[kk] + 2 * 32 * h * D), qf[kk], s);
     };
     // V^T operand (transpose reads): lane 4t+u of 16-lane group g points at
-    // key row 4*(g/2)+t, columns 32*db + 16*(g%2) + 4u, i.e. logical chunk
-    // 4*db + 2*(g%2) + u/2, element offset 4*(u%2) within it.
-    const int g = lane / 16;
-    const int sl = lane % 16;
-    const int v_row = 4 * (g / 2) + sl / 4;
-    const int v_lc = 2 * (g % 2) + (sl % 4) / 2;
-    const int v_in = 4 * (sl % 2);
-    auto v_addr = [&](const uint16_t *vt, int r, int db) -> const uint16_t * {
-        const int pc = (4 * db + v_lc) ^ v_swz(r);
-        return vt + r * D + 8 * pc + v_in;
-    };
+    // key row 4*(g/2)+t (and 8 rows further for operand slots 4..7),
+    // columns 32*db + 16*(g%2) + 4u, i.e. logical chunk 4*db + 2*(g%2) + u/2,
+    // element offset 4*(u%2) within it (v_swz of those rows equals v_swz of
+    // 4*(g/2)+t).
+    uint32_t voff[DB];
+    {
+        const int g = lane / 16, sl = lane % 16;
+        const int v_row = 4 * (g / 2) + sl / 4;
+        const int v_lc = 2 * (g % 2) + (sl % 4) / 2;
+        const int v_in = 4 * (sl % 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voff[db] = 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in);
+    }
 
     // Element mask of 32 keys starting at kbase: keys past the end of the
     // sequence, keys above the diagonal (causal), or all of them when this
@@ -236,17 +253,30 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     issue_v(t0, 0);
     if (t1 < t_end)
         issue_k(t1, 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        wait_loaded(qf[kk]);
     lds_dma_wait<0>();
     __syncthreads();
 
     f32x16 s_cur;
-    qk_half(Ks[0], 0, s_cur);
+    qk_half(lds0, 0, s_cur);
     mask_half(t0 * BC, s_cur);
 
     int t = t0;
     int j = 0;
     int kb_cur = 0, kb_nxt = 1;  // K buffers of tiles j and j+1
-    while (t < t_end) {
+    // Whether the keys the iteration of tile t masks (the second half of t,
+    // the first half of the next tile) need the element mask.
+    auto half_masked = [&](int kbase) __attribute__((always_inline)) -> bool {
+        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
+        return drop || (kbase + 32 > N) || (CAUSAL && kbase + 31 > wr0);
+    };
+    auto tile_masked = [&]() __attribute__((always_inline)) -> bool {
+        return half_masked(t * BC + 32) || (t1 < t_end && half_masked(t1 * BC));
+    };
+    auto tile = [&](auto mtag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
         const int kb_nn = 3 - kb_cur - kb_nxt;               // K buffer of tile j+2
@@ -257,20 +287,28 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         if (tn < t_end)
             issue_v(tn, (j + 1) & 1);
 
-        const uint16_t *vt = Vs[j & 1];
+        // this tile's V^T read addresses (one register per pattern)
+        uint32_t va[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            va[db] = opaque_addr(lds0 + V_OFF + (j & 1) * TB + voff[db]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             // S^T of the next 32 keys: the second half of this tile, then the
             // first half of tile j+1 (on the last tile a stale buffer is read
             // and the result unused). Its first half-depth runs beside the
             // row max, its second beside the exponentials.
-            const uint16_t *kt = (h == 0 ? Ks[kb_cur] : Ks[kb_nxt]) + (32 * (h ^ 1) + l32) * D;
-            const int ksw = k_swz(32 * (h ^ 1) + l32);
+            uint32_t ka[KK];
+            const uint32_t kt = lds0 + (h == 0 ? kb_cur : kb_nxt) * TB;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                ka[kk] = opaque_addr(kt + koff[kk]);
+            const uint32_t krow = 2 * 32 * (h ^ 1) * D;
             f32x16 s_nxt = f32x16{};
             bf16x8 kf[KK];
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
-                kf[kk] = lds_read_b128(kt + 8 * ((2 * kk + hi) ^ ksw));
+                kf[kk] = lds_b128_at(ka[kk] + krow);
             float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
@@ -297,14 +335,14 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             const float mref = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
             for (int kk = KK / 2; kk < KK; ++kk)
-                kf[kk] = lds_read_b128(kt + 8 * ((2 * kk + hi) ^ ksw));
+                kf[kk] = lds_b128_at(ka[kk] + krow);
             bf16x8 vf[2][DB];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int r0 = 32 * h + 16 * hh + v_row;
+                const uint32_t vrow = 2 * (32 * h + 16 * hh) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    vf[hh][db] = lds_read_tr_pair(v_addr(vt, r0, db), v_addr(vt, r0 + 8, db));
+                    vf[hh][db] = lds_tr_pair_at(va[db] + vrow, va[db] + vrow + 2 * 8 * D);
             }
             float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -340,10 +378,12 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                 o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
             sched_interleave<KK / 2 + 2 * DB, 2, 4>();
 
-            if (h == 0)
-                mask_half(t * BC + 32, s_nxt);
-            else if (tn < t_end)
-                mask_half(tn * BC, s_nxt);
+            if (MASKED) {
+                if (h == 0)
+                    mask_half(t * BC + 32, s_nxt);
+                else if (tn < t_end)
+                    mask_half(tn * BC, s_nxt);
+            }
             s_cur = s_nxt;
         }
         lds_dma_wait<0>();
@@ -353,6 +393,15 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         ++j;
         kb_cur = kb_nxt;
         kb_nxt = kb_nn;
+    };
+    // Iterations whose keys need no element mask run in a loop of their own
+    // (causal: the masked ones are the last, on the diagonal; block-sparse:
+    // a wave whose mask row drops a tile another wave keeps).
+    while (t < t_end) {
+        while (t < t_end && !tile_masked())
+            tile(std::false_type{});
+        while (t < t_end && tile_masked())
+            tile(std::true_type{});
     }
 
     // Epilogue: O = O^T / l (transposed back per lane), LSE in natural log.
