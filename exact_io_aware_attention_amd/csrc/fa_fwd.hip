@@ -92,10 +92,10 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     constexpr int LPW = TILE * 2 / 1024 / W;  // 1 KB direct loads per wave per tile
     static_assert(LPW >= 1, "tile too small for the direct-load layout");
 
-    // LDS: three K tiles, then two V tiles.
+    // LDS: three K tiles, then three V tiles.
     constexpr uint32_t TB = TILE * 2;  // bytes per tile
     constexpr uint32_t V_OFF = 3 * TB;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 3 * TB];
     const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item = xcd_work_item(p.per_xcd);
@@ -251,21 +251,37 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     int t1 = next_tile(t0);
     issue_k(t0, 0);
     issue_v(t0, 0);
-    if (t1 < t_end)
+    if (t1 < t_end) {
         issue_k(t1, 1);
+        issue_v(t1, 1);
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
         wait_loaded(qf[kk]);
     lds_dma_wait<0>();
     __syncthreads();
 
+    // Row max of a 32-key score block, times c: lane-local over the 16
+    // registers, then across the two 32-lane halves (both hold the row).
+    auto row_max = [&](const f32x16 &sv) __attribute__((always_inline)) -> float {
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            mx0 = fmaxf(mx0, sv[r]);
+            mx1 = fmaxf(mx1, sv[r + 1]);
+        }
+        const float mx = fmaxf(mx0, mx1);
+        return fmaxf(mx, lane_swap32(mx)) * c;
+    };
+
     f32x16 s_cur;
     qk_half(lds0, 0, s_cur);
     mask_half(t0 * BC, s_cur);
+    float mx_cur = row_max(s_cur);
 
     int t = t0;
     int j = 0;
-    int kb_cur = 0, kb_nxt = 1;  // K buffers of tiles j and j+1
+    int kb_cur = 0, kb_nxt = 1;  // K and V buffers of tiles j and j+1
     // Whether the keys the iteration of tile t masks (the second half of t,
     // the first half of the next tile) need the element mask.
     auto half_masked = [&](int kbase) __attribute__((always_inline)) -> bool {
@@ -279,19 +295,20 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         constexpr bool MASKED = decltype(mtag)::value;
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
-        const int kb_nn = 3 - kb_cur - kb_nxt;               // K buffer of tile j+2
-        // K of tile j+2 replaces tile j-1's K; V of tile j+1 replaces tile
-        // j-1's V; both were last read before the previous barrier.
-        if (tnn < t_end)
+        const int kb_nn = 3 - kb_cur - kb_nxt;               // buffers of tile j+2
+        // K and V of tile j+2 replace tile j-1's, last read before the
+        // previous barrier; tile j+1's were issued one iteration ago.
+        const bool more = tnn < t_end;
+        if (more) {
             issue_k(tnn, kb_nn);
-        if (tn < t_end)
-            issue_v(tn, (j + 1) & 1);
+            issue_v(tnn, kb_nn);
+        }
 
         // this tile's V^T read addresses (one register per pattern)
         uint32_t va[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            va[db] = opaque_addr(lds0 + V_OFF + (j & 1) * TB + voff[db]);
+            va[db] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             // S^T of the next 32 keys: the second half of this tile, then the
@@ -304,25 +321,11 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             for (int kk = 0; kk < KK; ++kk)
                 ka[kk] = opaque_addr(kt + koff[kk]);
             const uint32_t krow = 2 * 32 * (h ^ 1) * D;
-            f32x16 s_nxt = f32x16{};
-            bf16x8 kf[KK];
-#pragma unroll
-            for (int kk = 0; kk < KK / 2; ++kk)
-                kf[kk] = lds_b128_at(ka[kk] + krow);
-            float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                mx0 = fmaxf(mx0, s_cur[r]);
-                mx1 = fmaxf(mx1, s_cur[r + 1]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KK / 2; ++kk)
-                s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
-            float mx = fmaxf(mx0, mx1);
-            mx = fmaxf(mx, lane_swap32(mx)) * c;
-            sched_interleave<KK / 2, 0, 2>();
-            if (__any(mx > m + kRescaleSlack)) {
-                const float mnew = fmaxf(m, mx);
+            // Rescale first, so that the rest of the half-step (the next
+            // scores' MFMAs beside this block's exponentials, then P V) is one
+            // straight-line block the scheduler can interleave.
+            if (__any(mx_cur > m + kRescaleSlack)) {
+                const float mnew = fmaxf(m, mx_cur);
                 const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - mnew);
                 m = mnew;
                 l *= alpha;
@@ -332,6 +335,14 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                     for (int r = 0; r < 16; ++r)
                         o[db][r] *= alpha;
             }
+            f32x16 s_nxt = f32x16{};
+            bf16x8 kf[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK / 2; ++kk)
+                kf[kk] = lds_b128_at(ka[kk] + krow);
+#pragma unroll
+            for (int kk = 0; kk < KK / 2; ++kk)
+                s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
             const float mref = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
             for (int kk = KK / 2; kk < KK; ++kk)
@@ -384,10 +395,16 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                 else if (tn < t_end)
                     mask_half(tn * BC, s_nxt);
             }
+            mx_cur = row_max(s_nxt);  // beside the P V MFMAs still in flight
             s_cur = s_nxt;
         }
-        lds_dma_wait<0>();
-        __syncthreads();  // tile j+1's V and tile j+2's K have landed
+        // tile j+1 has landed (this wave's loads of tile j+2, issued after
+        // it, may still be in flight); the barrier extends that to all waves
+        if (more)
+            lds_dma_wait<2 * LPW>();
+        else
+            lds_dma_wait<0>();
+        __syncthreads();
         t = tn;
         t1 = tnn;
         ++j;
