@@ -17,6 +17,7 @@ Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--supp-steps", type=int, default=10,
+                    help="timed steps of the supplementary non-causal run (0: skip)")
     return ap.parse_args()
 
 
@@ -142,11 +145,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    dur = {n: 0.0 for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            dur[n] += ev[j].elapsed_time(ev[j + 1]) * 1e-3  # seconds
-    avg = {n: dur[n] / args.steps for n in names}
+    per = {n: [ev[j].elapsed_time(ev[j + 1]) * 1e-3 for ev in events]  # seconds
+           for j, n in enumerate(names)}
+    avg = {n: sum(per[n]) / args.steps for n in names}
 
     fwd_flops, bwd_flops = flop_counts(cfg, mask)
     step_s = wall / args.steps
@@ -178,8 +179,39 @@ def main():
                 "algorithmic_bytes": kernel_bytes[dominant]}
 
     kernels = {n: {"avg_us": round(avg[n] * 1e6, 2),
+                   "median_us": round(statistics.median(per[n]) * 1e6, 2),
+                   "min_us": round(min(per[n]) * 1e6, 2),
+                   "max_us": round(max(per[n]) * 1e6, 2),
                    "tflops": round(kernel_flops[n] / avg[n] / 1e12, 2) if kernel_flops[n] else None,
                    "gbs": round(kernel_bytes[n] / avg[n] / 1e9, 1)} for n in names}
+
+    # Supplementary: the same shape and inputs without the causal mask (twice
+    # the work), forward and backward times only; never part of `value`.
+    supp = None
+    if causal and mask is None and args.supp_steps > 0:
+        def run_nc():
+            fa.fa_fwd(Q, K, V, O, LSE, scale, causal=False)
+            fa.fa_bwd_prep(dO, O, LSE, ws)
+            fa.fa_bwd_dq(dO, Q, K, V, dQ, scale, ws, causal=False)
+            fa.fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, ws, causal=False)
+        run_nc()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.supp_steps)]
+        for e in ev:
+            e[0].record()
+            fa.fa_fwd(Q, K, V, O, LSE, scale, causal=False)
+            e[1].record()
+            fa.fa_bwd_prep(dO, O, LSE, ws)
+            fa.fa_bwd_dq(dO, Q, K, V, dQ, scale, ws, causal=False)
+            fa.fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, ws, causal=False)
+            e[2].record()
+        torch.cuda.synchronize()
+        f_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
+        b_s = statistics.median([e[1].elapsed_time(e[2]) * 1e-3 for e in ev])
+        supp = {"workload": cfg.name + " shape without the causal mask (supplementary)",
+                "fwd_ms": round(f_s * 1e3, 4), "fwd_tflops": round(2 * fwd_flops / f_s / 1e12, 2),
+                "bwd_ms": round(b_s * 1e3, 4), "bwd_tflops": round(2 * bwd_flops / b_s / 1e12, 2),
+                "steps": args.supp_steps}
 
     cpu = None
     if args.cpu_heads > 0:
@@ -220,6 +252,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "supplementary": supp,
     }
     print(json.dumps(out), flush=True)
 
