@@ -30,8 +30,8 @@
 // lanes of a b128 read per cycle): K row r, chunk c is stored at chunk
 // c ^ (r % 16) for 256-byte rows (d = 128) or c ^ ((r / 2) % 8) for 128-byte
 // rows (d = 64), so the 16 rows of one b128 read cycle land in 16 different
-// bank groups; V row r, chunk c at c ^ 2 (r % 4) -- the four rows x 32 bytes
-// of one 16-lane transpose read cover 32 different banks.
+// bank groups; V row r, chunk c at c ^ (4 (r % 4) + (r / 4) % 4) (d = 128) --
+// the four rows x 64 bytes of one 32-lane transpose read cover all 64 banks.
 //
 // Online softmax (mstx.cn/posts/485 §三.2 update rule) in base 2, c = scale
 // * log2(e). Each row keeps a reference max m (the exponent offset of its
@@ -159,7 +159,12 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     // r = b * (64 / CPR) + lane / CPR, physical chunk lane % CPR, which holds
     // logical chunk (lane % CPR) ^ swz(r).
     auto k_swz = [](int r) -> int { return CPR == 16 ? (r % 16) : ((r / 2) % 8); };
-    auto v_swz = [](int r) -> int { return 2 * (r % 4); };
+    // V rows are only read by transpose reads: the aligned 4-chunk blocks of
+    // any 4 aligned rows land on distinct banks (f(r) / 4 distinct), for
+    // d = 64 with the row parity taking one bit's place.
+    auto v_swz = [](int r) -> int {
+        return CPR == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
+    };
     uint32_t kdma[LPW], vdma[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -194,17 +199,19 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     // V^T operand (transpose reads): lane 4t+u of 16-lane group g points at
     // key row 4*(g/2)+t (and 8 rows further for operand slots 4..7),
     // columns 32*db + 16*(g%2) + 4u, i.e. logical chunk 4*db + 2*(g%2) + u/2,
-    // element offset 4*(u%2) within it (v_swz of those rows equals v_swz of
-    // 4*(g/2)+t).
-    uint32_t voff[DB];
+    // element offset 4*(u%2) within it (v_swz depends on the row modulo 16,
+    // so the rows 16 and 32 further take the same offsets).
+    uint32_t voff[DB][2];
     {
         const int g = lane / 16, sl = lane % 16;
         const int v_row = 4 * (g / 2) + sl / 4;
         const int v_lc = 2 * (g % 2) + (sl % 4) / 2;
         const int v_in = 4 * (sl % 2);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            voff[db] = 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in);
+        for (int db = 0; db < DB; ++db) {
+            voff[db][0] = 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in);
+            voff[db][1] = 2 * ((v_row + 8) * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row + 8)) + v_in);
+        }
     }
 
     // Element mask of 32 keys starting at kbase: keys past the end of the
@@ -305,10 +312,12 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         }
 
         // this tile's V^T read addresses (one register per pattern)
-        uint32_t va[DB];
+        uint32_t va[DB][2];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            va[db] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db]);
+        for (int db = 0; db < DB; ++db) {
+            va[db][0] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db][0]);
+            va[db][1] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db][1]);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             // S^T of the next 32 keys: the second half of this tile, then the
@@ -353,7 +362,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                 const uint32_t vrow = 2 * (32 * h + 16 * hh) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    vf[hh][db] = lds_tr_pair_at(va[db] + vrow, va[db] + vrow + 2 * 8 * D);
+                    vf[hh][db] = lds_tr_pair_at(va[db][0] + vrow, va[db][1] + vrow);
             }
             float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
