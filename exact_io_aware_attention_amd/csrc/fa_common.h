@@ -235,9 +235,36 @@ __device__ __forceinline__ float exp2_fast(float x)
     return __builtin_amdgcn_exp2f(x);
 }
 
-__device__ __forceinline__ float lane_swap32(float x)
+// Each lane gets {x, x of the lane 32 away} from one v_permlane32_swap (the
+// upper half of the first copy trades places with the lower half of the
+// second), so the reduction over the two halves is one VALU op more and
+// stays out of the LDS queue.
+__device__ __forceinline__ float halves_max(float x)
 {
-    return __shfl_xor(x, 32, kWave);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    float y;
+    asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return y;
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max of three scores without the NaN-quieting copies fmaxf brings in IEEE
+// mode (no operand here is ever NaN; -inf is an ordinary value).
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float y;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(y) : "v"(a), "v"(b), "v"(c));
+    return y;
+}
+__device__ __forceinline__ float vmax2(float a, float b)
+{
+    float y;
+    asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(a), "v"(b));
+    return y;
 }
 
 // Asks the scheduler to interleave, within the current basic block, NM

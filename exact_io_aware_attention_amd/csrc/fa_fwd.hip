@@ -184,24 +184,27 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TB, t); };
     auto issue_v = [&](int t, int buf) __attribute__((always_inline)) { issue(Vh, vdma, lds0 + V_OFF + buf * TB, t); };
 
+    // Operand read addresses are this lane's byte address in buffer 0; the
+    // buffer, which each unrolled iteration fixes, and the row block go into
+    // the read instruction's immediate offset.
     // K operand reads: row 32*h + l32 of the tile, logical chunk 2*kk + hi
     // (k_swz of row 32 h + l32 equals k_swz of l32).
-    uint32_t koff[KK];
+    uint32_t kaddr[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-        koff[kk] = 2 * (l32 * D + 8 * ((2 * kk + hi) ^ k_swz(l32)));
-    auto qk_half = [&](uint32_t ktile, int h, f32x16 &s) __attribute__((always_inline)) {
+        kaddr[kk] = lds0 + 2 * (l32 * D + 8 * ((2 * kk + hi) ^ k_swz(l32)));
+    auto qk_half = [&](uint32_t kofs, f32x16 &s) __attribute__((always_inline)) {
         s = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            s = mfma32x32x16(lds_b128_at(ktile + koff[kk] + 2 * 32 * h * D), qf[kk], s);
+            s = mfma32x32x16(lds_b128_at(kaddr[kk] + kofs), qf[kk], s);
     };
     // V^T operand (transpose reads): lane 4t+u of 16-lane group g points at
     // key row 4*(g/2)+t (and 8 rows further for operand slots 4..7),
     // columns 32*db + 16*(g%2) + 4u, i.e. logical chunk 4*db + 2*(g%2) + u/2,
     // element offset 4*(u%2) within it (v_swz depends on the row modulo 16,
     // so the rows 16 and 32 further take the same offsets).
-    uint32_t voff[DB][2];
+    uint32_t vaddr[DB][2];
     {
         const int g = lane / 16, sl = lane % 16;
         const int v_row = 4 * (g / 2) + sl / 4;
@@ -209,8 +212,10 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         const int v_in = 4 * (sl % 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            voff[db][0] = 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in);
-            voff[db][1] = 2 * ((v_row + 8) * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row + 8)) + v_in);
+            // opaque: the V base stays in the register, so that the buffer
+            // and row offsets (< 64 KB) fit the immediate
+            vaddr[db][0] = opaque_addr(lds0 + V_OFF + 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in));
+            vaddr[db][1] = opaque_addr(lds0 + V_OFF + 2 * ((v_row + 8) * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row + 8)) + v_in));
         }
     }
 
@@ -271,24 +276,30 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     // Row max of a 32-key score block, times c: lane-local over the 16
     // registers, then across the two 32-lane halves (both hold the row).
     auto row_max = [&](const f32x16 &sv) __attribute__((always_inline)) -> float {
-        float mx0 = -INFINITY, mx1 = -INFINITY;
+        // two interleaved chains, so that no max waits on the one before
+        float ma = vmax3(sv[0], sv[1], sv[2]);
+        float mb = vmax3(sv[3], sv[4], sv[5]);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            mx0 = fmaxf(mx0, sv[r]);
-            mx1 = fmaxf(mx1, sv[r + 1]);
+        for (int r = 6; r < 14; r += 4) {
+            ma = vmax3(ma, sv[r], sv[r + 1]);
+            mb = vmax3(mb, sv[r + 2], sv[r + 3]);
         }
-        const float mx = fmaxf(mx0, mx1);
-        return fmaxf(mx, lane_swap32(mx)) * c;
+        ma = vmax3(ma, sv[14], sv[15]);
+        return halves_max(vmax2(ma, mb)) * c;
     };
 
     f32x16 s_cur;
-    qk_half(lds0, 0, s_cur);
+    qk_half(0, s_cur);
     mask_half(t0 * BC, s_cur);
     float mx_cur = row_max(s_cur);
+    // Quantities of the reference max m that change only when it does: the
+    // rescale threshold m + slack, and the exponent offset -m (0 while
+    // m = -inf).
+    float thr = -INFINITY, nmref = 0.f;
 
+    // Tile j's K and V sit in buffer j % 3; the loop below is unrolled three
+    // times so that each copy knows its buffers.
     int t = t0;
-    int j = 0;
-    int kb_cur = 0, kb_nxt = 1;  // K and V buffers of tiles j and j+1
     // Whether the keys the iteration of tile t masks (the second half of t,
     // the first half of the next tile) need the element mask.
     auto half_masked = [&](int kbase) __attribute__((always_inline)) -> bool {
@@ -298,25 +309,20 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     auto tile_masked = [&]() __attribute__((always_inline)) -> bool {
         return half_masked(t * BC + 32) || (t1 < t_end && half_masked(t1 * BC));
     };
-    auto tile = [&](auto mtag) __attribute__((always_inline)) {
+    auto tile = [&](auto mtag, auto ptag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
+        constexpr int P = decltype(ptag)::value;           // j % 3
+        constexpr uint32_t KB_CUR = P * TB;                // tile j's buffer
+        constexpr uint32_t KB_NXT = (P + 1) % 3 * TB;      // tile j+1's
+        constexpr int KB_NN = (P + 2) % 3;                 // tile j+2's
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
-        const int kb_nn = 3 - kb_cur - kb_nxt;               // buffers of tile j+2
         // K and V of tile j+2 replace tile j-1's, last read before the
         // previous barrier; tile j+1's were issued one iteration ago.
         const bool more = tnn < t_end;
         if (more) {
-            issue_k(tnn, kb_nn);
-            issue_v(tnn, kb_nn);
-        }
-
-        // this tile's V^T read addresses (one register per pattern)
-        uint32_t va[DB][2];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            va[db][0] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db][0]);
-            va[db][1] = opaque_addr(lds0 + V_OFF + kb_cur * TB + voff[db][1]);
+            issue_k(tnn, KB_NN);
+            issue_v(tnn, KB_NN);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -324,19 +330,16 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             // first half of tile j+1 (on the last tile a stale buffer is read
             // and the result unused). Its first half-depth runs beside the
             // row max, its second beside the exponentials.
-            uint32_t ka[KK];
-            const uint32_t kt = lds0 + (h == 0 ? kb_cur : kb_nxt) * TB;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                ka[kk] = opaque_addr(kt + koff[kk]);
-            const uint32_t krow = 2 * 32 * (h ^ 1) * D;
+            const uint32_t kofs = (h == 0 ? KB_CUR : KB_NXT) + 2 * 32 * (h ^ 1) * D;
             // Rescale first, so that the rest of the half-step (the next
             // scores' MFMAs beside this block's exponentials, then P V) is one
             // straight-line block the scheduler can interleave.
-            if (__any(mx_cur > m + kRescaleSlack)) {
+            if (__any(mx_cur > thr)) {
                 const float mnew = fmaxf(m, mx_cur);
                 const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - mnew);
                 m = mnew;
+                thr = m + kRescaleSlack;
+                nmref = (m == -INFINITY) ? 0.f : -m;
                 l *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -348,31 +351,30 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             bf16x8 kf[KK];
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
-                kf[kk] = lds_b128_at(ka[kk] + krow);
+                kf[kk] = lds_b128_at(kaddr[kk] + kofs);
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
                 s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
-            const float mref = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
             for (int kk = KK / 2; kk < KK; ++kk)
-                kf[kk] = lds_b128_at(ka[kk] + krow);
+                kf[kk] = lds_b128_at(kaddr[kk] + kofs);
             bf16x8 vf[2][DB];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const uint32_t vrow = 2 * (32 * h + 16 * hh) * D;
+                const uint32_t vofs = KB_CUR + 2 * (32 * h + 16 * hh) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    vf[hh][db] = lds_tr_pair_at(va[db][0] + vrow, va[db][1] + vrow);
+                    vf[hh][db] = lds_tr_pair_at(vaddr[db][0] + vofs, vaddr[db][1] + vofs);
             }
-            float ls0 = 0.f, ls1 = 0.f;
+            float ls0, ls1;
 #pragma unroll
             for (int r = 0; r < 8; r += 2) {
-                const float e0 = exp2_fast(fmaf(s_cur[r], c, -mref));
-                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, -mref));
+                const float e0 = exp2_fast(fmaf(s_cur[r], c, nmref));
+                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, nmref));
                 s_cur[r] = e0;
                 s_cur[r + 1] = e1;
-                ls0 += e0;
-                ls1 += e1;
+                ls0 = r == 0 ? e0 : ls0 + e0;
+                ls1 = r == 0 ? e1 : ls1 + e1;
             }
 #pragma unroll
             for (int kk = KK / 2; kk < KK; ++kk)
@@ -381,8 +383,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             const bf16x8 p0 = pack_bf16x8(s_cur, 0);
 #pragma unroll
             for (int r = 8; r < 16; r += 2) {
-                const float e0 = exp2_fast(fmaf(s_cur[r], c, -mref));
-                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, -mref));
+                const float e0 = exp2_fast(fmaf(s_cur[r], c, nmref));
+                const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, nmref));
                 s_cur[r] = e0;
                 s_cur[r + 1] = e1;
                 ls0 += e0;
@@ -416,22 +418,39 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         __syncthreads();
         t = tn;
         t1 = tnn;
-        ++j;
-        kb_cur = kb_nxt;
-        kb_nxt = kb_nn;
     };
     // Iterations whose keys need no element mask run in a loop of their own
     // (causal: the masked ones are the last, on the diagonal; block-sparse:
     // a wave whose mask row drops a tile another wave keeps).
+    int phase = 0;  // j % 3
+    auto run = [&](auto mtag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        for (;;) {
+            if (phase == 0) {
+                if (t >= t_end || tile_masked() != MASKED)
+                    return;
+                tile(mtag, std::integral_constant<int, 0>{});
+                phase = 1;
+            }
+            if (phase == 1) {
+                if (t >= t_end || tile_masked() != MASKED)
+                    return;
+                tile(mtag, std::integral_constant<int, 1>{});
+                phase = 2;
+            }
+            if (t >= t_end || tile_masked() != MASKED)
+                return;
+            tile(mtag, std::integral_constant<int, 2>{});
+            phase = 0;
+        }
+    };
     while (t < t_end) {
-        while (t < t_end && !tile_masked())
-            tile(std::false_type{});
-        while (t < t_end && tile_masked())
-            tile(std::true_type{});
+        run(std::false_type{});
+        run(std::true_type{});
     }
 
     // Epilogue: O = O^T / l (transposed back per lane), LSE in natural log.
-    const float lt = l + lane_swap32(l);
+    const float lt = halves_sum(l);
     if (row < N) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         uint16_t *Oh = p.O + head + (size_t)row * D;
