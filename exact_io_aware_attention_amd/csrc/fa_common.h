@@ -172,6 +172,14 @@ __device__ __forceinline__ uint32_t opaque_addr(uint32_t x)
 }
 // Waits until at most N of this wave's vector memory operations (the
 // direct loads included) are outstanding.
+// Workgroup barrier that waits for none of this wave's own LDS reads: a
+// caller reading, across it, data that no wave writes until a later barrier
+// keeps those reads in flight. Memory accesses are not moved across it.
+__device__ __forceinline__ void barrier_reads_in_flight()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void lds_dma_wait()
 {

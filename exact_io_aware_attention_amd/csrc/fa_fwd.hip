@@ -296,6 +296,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     // rescale threshold m + slack, and the exponent offset -m (0 while
     // m = -inf).
     float thr = -INFINITY, nmref = 0.f;
+    // The first K^T fragments of each half-step are read one half-step
+    // early, so that its first MFMAs wait for no LDS read: here those of the
+    // first half-step (tile t0's second 32 keys, buffer 0).
+    bf16x8 kpre[KK / 2];
+#pragma unroll
+    for (int kk = 0; kk < KK / 2; ++kk)
+        kpre[kk] = lds_b128_at(kaddr[kk] + 2 * 32 * D);
 
     // Tile j's K and V sit in buffer j % 3; the loop below is unrolled three
     // times so that each copy knows its buffers.
@@ -351,7 +358,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             bf16x8 kf[KK];
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
-                kf[kk] = lds_b128_at(kaddr[kk] + kofs);
+                kf[kk] = kpre[kk];
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
                 s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
@@ -398,7 +405,16 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
+            // the next half-step's first K^T fragments: tile j+1's first 32
+            // keys, then its second 32 (visible since the last barrier)
+            {
+                const uint32_t nofs = h == 0 ? KB_NXT : KB_NXT + 2 * 32 * D;
+#pragma unroll
+                for (int kk = 0; kk < KK / 2; ++kk)
+                    kpre[kk] = lds_b128_at(kaddr[kk] + nofs);
+            }
             sched_interleave<KK / 2 + 2 * DB, 2, 4>();
+            __builtin_amdgcn_sched_group_barrier(0x100, KK / 2, 0);
 
             if (MASKED) {
                 if (h == 0)
@@ -415,7 +431,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             lds_dma_wait<2 * LPW>();
         else
             lds_dma_wait<0>();
-        __syncthreads();
+        barrier_reads_in_flight();
         t = tn;
         t1 = tnn;
     };
