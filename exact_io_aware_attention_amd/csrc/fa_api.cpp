@@ -33,15 +33,16 @@ fa_status check_common(int B, int H, int N, int d, float scale, int causal, bool
 {
     if (B < 0 || H < 0 || N < 0)
         return FA_ERR_SHAPE;
-    if (d != 64 && d != 128)
+    if (d < 8 || d > 128 || d % 8 != 0)
         return FA_ERR_HEADDIM;
     if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1))
         return FA_ERR_SCALE;
     // every element index of a [B][H][N][d] tensor must fit in 63 bits and a
-    // per-head slab in 31 bits of elements
+    // per-head slab in 30 bits of elements (2^31 bytes of bf16: buffer
+    // offsets from 2^31 on are then out of range for every tile load)
     const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
     const unsigned long long head = (unsigned long long)N * (unsigned long long)d;
-    if (head > (unsigned long long)std::numeric_limits<int>::max())
+    if (head >= (1ull << 30))
         return FA_ERR_SHAPE;
     if (bh > 0 && head > 0 && bh > (unsigned long long)std::numeric_limits<long long>::max() / head)
         return FA_ERR_SHAPE;

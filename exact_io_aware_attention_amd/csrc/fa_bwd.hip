@@ -38,15 +38,15 @@ namespace {
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const uint16_t *O,
                                                       const float *LSE, float *ndelta,
-                                                      float *lse2, long rows)
+                                                      float *lse2, long rows, int dh)
 {
-    constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
+    constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each (rows are dh <= D wide)
     const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
     const int part = threadIdx.x % LPR;
     float acc = 0.f;
-    if (row < rows) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(dO + row * D + 8 * part);
-        const uint4 b = *reinterpret_cast<const uint4 *>(O + row * D + 8 * part);
+    if (row < rows && 8 * part < dh) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(dO + row * dh + 8 * part);
+        const uint4 b = *reinterpret_cast<const uint4 *>(O + row * dh + 8 * part);
         const uint32_t av[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -101,8 +101,9 @@ struct TileLane {
     uint32_t b128[KK];    // b128 operand read: row l32, logical chunk 2 kk + hi
     uint32_t tr[DB][2];   // transpose reads: rows rl and rl + 8, columns 32 db..
     uint32_t dma[LPW];    // direct-load source offset of block wave * LPW + i
+    int dh;               // global row width (<= D; the rest reads as zeros)
 
-    __device__ __forceinline__ TileLane(int wave, int lane)
+    __device__ __forceinline__ TileLane(int wave, int lane, int dh_) : dh(dh_)
     {
         const int l32 = lane % 32, hi = lane / 32;
 #pragma unroll
@@ -122,12 +123,14 @@ struct TileLane {
         }
         // Direct loads: 1 KB blocks, lane l of block b writes physical chunk
         // l % CPR of row b * (64 / CPR) + l / CPR, i.e. its logical chunk
-        // (l % CPR) ^ swz(row).
+        // (l % CPR) ^ swz(row); global rows are dh wide and chunks past dh
+        // read as zeros.
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int b = wave * LPW + i;
             const int r = b * (64 / CPR) + lane / CPR;
-            dma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ tile_swz<D>(r)));
+            const int c = (lane % CPR) ^ tile_swz<D>(r);
+            dma[i] = 8 * c < dh ? 2 * (r * dh + 8 * c) : kBufferOutOfRange;
         }
     }
     // Issues this wave's direct loads of rows row0.. of a row-major [N, D]
@@ -135,14 +138,14 @@ struct TileLane {
     // zeros (the resource ends at row N).
     __device__ __forceinline__ void load(const uint16_t *src, uint32_t tile, int row0, int N, int wave) const
     {
-        const i32x4 rs = rsrc(src, row0, N);
+        const i32x4 rs = rsrc(src, row0, N, dh);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             load_block(rs, tile, wave, i);
     }
-    __device__ __forceinline__ static i32x4 rsrc(const uint16_t *src, int row0, int N)
+    __device__ __forceinline__ static i32x4 rsrc(const uint16_t *src, int row0, int N, int dh)
     {
-        return buffer_rsrc(src + (size_t)row0 * D, (uint32_t)(N - row0) * (2 * D));
+        return buffer_rsrc(src + (size_t)row0 * dh, (uint32_t)(N - row0) * (2 * dh));
     }
     // The i-th of this wave's LPW loads of a tile (for spreading them out).
     __device__ __forceinline__ void load_block(const i32x4 &rs, uint32_t tile, int wave, int i) const
@@ -191,12 +194,15 @@ __device__ __forceinline__ void load_vec64(const float *src, uint32_t dst, int r
 }
 
 // Stores a 32-row accumulator block (lane = row, registers = 32 columns in
-// runs of 4) as bf16, times a factor.
+// runs of 4) as bf16, times a factor; columns from dh on are padding and are
+// not stored.
 __device__ __forceinline__ void store_rows_bf16(uint16_t *dst_row, const f32x16 &acc, int col0, int hi,
-                                                float mul)
+                                                float mul, int dh)
 {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        if (col0 + 8 * j + 4 * hi >= dh)
+            continue;
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16_bits(acc[4 * j + 0] * mul) |
                ((uint32_t)f32_to_bf16_bits(acc[4 * j + 1] * mul) << 16);
@@ -213,7 +219,7 @@ struct DqParams {
     const float *ndelta, *lse2;  // -D and LSE * log2(e) per row
     uint16_t *dQ;
     const uint8_t *mask;
-    int N, nqb, nkt, nmb, items, per_xcd;
+    int N, dh, nqb, nkt, nmb, items, per_xcd;
     float c, scale;
 };
 
@@ -278,19 +284,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     const int hi = lane / 32;
     const int wr0 = q0 + wave * 32;
     const int row = wr0 + l32;  // this lane's query row
-    const TileLane<D, W> tl(wave, lane);
+    const int dh = p.dh;
+    const TileLane<D, W> tl(wave, lane, dh);
 
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const size_t head = (size_t)bh * (size_t)N * dh;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
 
     bf16x8 qf[KK], gf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        qf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
-                         : bf16x8{};
-        gf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * D + 16 * kk + 8 * hi)
-                         : bf16x8{};
+        const bool in = row < N && 16 * kk + 8 * hi < dh;
+        qf[kk] = in ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * dh + 16 * kk + 8 * hi) : bf16x8{};
+        gf[kk] = in ? *reinterpret_cast<const bf16x8 *>(dOh + (size_t)row * dh + 16 * kk + 8 * hi) : bf16x8{};
     }
     const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
     const float nDi = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
@@ -478,10 +484,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     for (int db = 0; db < DB; ++db)
         mfma_settle(dq[db]);
     if (row < N) {
-        uint16_t *dst = p.dQ + head + (size_t)row * D;
+        uint16_t *dst = p.dQ + head + (size_t)row * dh;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            store_rows_bf16(dst, dq[db], 32 * db, hi, p.scale);
+            store_rows_bf16(dst, dq[db], 32 * db, hi, p.scale, dh);
     }
 }
 
@@ -492,7 +498,7 @@ struct DkvParams {
     const float *ndelta, *lse2;  // -D and LSE * log2(e) per row
     uint16_t *dK, *dV;
     const uint8_t *mask;
-    int N, nkb, nqt, nmb, items, per_xcd;
+    int N, dh, nkb, nqt, nmb, items, per_xcd;
     float c, scale;
 };
 
@@ -551,9 +557,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     const int l32 = lane % 32;
     const int hi = lane / 32;
     const int wk0 = k0 + wave * KW;
-    const TileLane<D, W> tl(wave, lane);
+    const int dh = p.dh;
+    const TileLane<D, W> tl(wave, lane, dh);
 
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const size_t head = (size_t)bh * (size_t)N * dh;
     const uint16_t *Qh = p.Q + head, *dOh = p.dO + head;
     const uint16_t *Kh = p.K + head, *Vh = p.V + head;
     const float *lse2h = p.lse2 + (size_t)bh * N;
@@ -565,10 +572,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         const int key = wk0 + 32 * kb + l32;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            kf[kb][kk] = key < N ? *reinterpret_cast<const bf16x8 *>(Kh + (size_t)key * D + 16 * kk + 8 * hi)
-                                 : bf16x8{};
-            vf[kb][kk] = key < N ? *reinterpret_cast<const bf16x8 *>(Vh + (size_t)key * D + 16 * kk + 8 * hi)
-                                 : bf16x8{};
+            const bool in = key < N && 16 * kk + 8 * hi < dh;
+            kf[kb][kk] = in ? *reinterpret_cast<const bf16x8 *>(Kh + (size_t)key * dh + 16 * kk + 8 * hi)
+                            : bf16x8{};
+            vf[kb][kk] = in ? *reinterpret_cast<const bf16x8 *>(Vh + (size_t)key * dh + 16 * kk + 8 * hi)
+                            : bf16x8{};
         }
     }
 
@@ -799,8 +807,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             // current one is loaded again, into the free slot: no branch).
             const int tl_next = tn < p.nqt ? tn : t;
             const uint32_t nslot = lds0 + ((j + 1) % 3) * SLOT;
-            const i32x4 rq = TileLane<D, W>::rsrc(Qh, tl_next * BQ, N);
-            const i32x4 rg = TileLane<D, W>::rsrc(dOh, tl_next * BQ, N);
+            const i32x4 rq = TileLane<D, W>::rsrc(Qh, tl_next * BQ, N, dh);
+            const i32x4 rg = TileLane<D, W>::rsrc(dOh, tl_next * BQ, N, dh);
             auto dma_hook = [&](int sl) __attribute__((always_inline)) {
                 constexpr int LPW = TileLane<D, W>::LPW;
                 if (sl < LPW)
@@ -855,12 +863,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     for (int kb = 0; kb < NB; ++kb) {
         const int key = wk0 + 32 * kb + l32;
         if (key < N) {
-            uint16_t *dKr = p.dK + head + (size_t)key * D;
-            uint16_t *dVr = p.dV + head + (size_t)key * D;
+            uint16_t *dKr = p.dK + head + (size_t)key * dh;
+            uint16_t *dVr = p.dV + head + (size_t)key * dh;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                store_rows_bf16(dKr, dk[kb][db], 32 * db, hi, p.scale);
-                store_rows_bf16(dVr, dv[kb][db], 32 * db, hi, 1.f);
+                store_rows_bf16(dKr, dk[kb][db], 32 * db, hi, p.scale, dh);
+                store_rows_bf16(dVr, dv[kb][db], 32 * db, hi, 1.f, dh);
             }
         }
     }
@@ -892,7 +900,7 @@ hipError_t prep_d(const Problem &pr, const BwdPtrs &b)
     const long rows = (long)pr.B * pr.H * pr.N;
     const long threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       pr.stream, b.dO, b.O, b.LSE, b.ndelta, b.lse2, rows);
+                       pr.stream, b.dO, b.O, b.LSE, b.ndelta, b.lse2, rows, pr.d);
     return hipGetLastError();
 }
 
@@ -903,6 +911,7 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
     qp.ndelta = b.ndelta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
     qp.N = pr.N;
+    qp.dh = pr.d;
     qp.nqb = (pr.N + BwdShape::ROWS - 1) / BwdShape::ROWS;
     qp.nkt = (pr.N + 63) / 64;
     qp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
@@ -922,6 +931,7 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
     kp.ndelta = b.ndelta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;
     kp.N = pr.N;
+    kp.dh = pr.d;
     kp.nkb = (pr.N + BwdShape::ROWS - 1) / BwdShape::ROWS;
     kp.nqt = (pr.N + 63) / 64;
     kp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
@@ -934,9 +944,10 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     return hipGetLastError();
 }
 
-// Dispatch on (d, causal, sparse) for a kernel template taking <D, CAUSAL, SPARSE>.
+// Dispatch on (d, causal, sparse) for a kernel template taking <D, CAUSAL, SPARSE>;
+// head dims up to 64 run in the 64-wide kernels, the others in the 128-wide ones.
 #define FA_DISPATCH(FN, pr, b)                                                              \
-    ((pr).d == 64 ? ((pr).causal ? ((pr).mask ? FN<64, true, true>(pr, b)                  \
+    ((pr).d <= 64 ? ((pr).causal ? ((pr).mask ? FN<64, true, true>(pr, b)                  \
                                               : FN<64, true, false>(pr, b))                \
                                  : ((pr).mask ? FN<64, false, true>(pr, b)                 \
                                               : FN<64, false, false>(pr, b)))              \
@@ -964,7 +975,7 @@ hipError_t launch_bwd_prep_bf16(const Problem &pr, const uint16_t *dO, const uin
 {
     const BwdPtrs b = bwd_ptrs(pr, dO, nullptr, nullptr, nullptr, O, LSE, nullptr, nullptr,
                                nullptr, workspace);
-    return pr.d == 64 ? prep_d<64>(pr, b) : prep_d<128>(pr, b);
+    return pr.d <= 64 ? prep_d<64>(pr, b) : prep_d<128>(pr, b);
 }
 
 hipError_t launch_bwd_dq_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *Q,

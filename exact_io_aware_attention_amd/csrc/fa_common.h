@@ -180,6 +180,18 @@ __device__ __forceinline__ void barrier_reads_in_flight()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Waits until every LDS read this wave has issued has returned; memory
+// accesses are not moved across it.
+__device__ __forceinline__ void lds_reads_wait_all()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// A buffer offset past the end of every resource used here (tensor slabs are
+// below 2^31 bytes): a load from it returns zeros. Used for the columns of a
+// padded head dimension.
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;
+
 template <int N>
 __device__ __forceinline__ void lds_dma_wait()
 {

@@ -3,7 +3,8 @@
 // bf16 rounding anywhere), so that a disagreement with the reference can be
 // told apart from bf16 rounding. One thread owns one query row (forward,
 // dQ) or one key row (dK, dV); key/query tiles are staged in LDS and read by
-// broadcast.
+// broadcast. Head dims below the compiled width (64 or 128) are zero-padded
+// on load and not stored.
 //
 // Forward: mstx.cn/posts/485 §三.2 "Online Softmax" update rule (base 2,
 // c = scale * log2 e), O divided by l once at the end.
@@ -32,17 +33,17 @@ __device__ __forceinline__ bool visible(int i, int j, bool causal, const uint8_t
 
 template <int D>
 __global__ void __launch_bounds__(kT) fwd_f32_kernel(const float *Q, const float *K, const float *V,
-                                                     float *O, float *LSE, int N, float c,
+                                                     float *O, float *LSE, int N, int dh, float c,
                                                      int causal, const uint8_t *mask, int nmb)
 {
     __shared__ float Ks[kT][D];
     __shared__ float Vs[kT][D];
     const int bh = blockIdx.y;
     const int row = blockIdx.x * kT + threadIdx.x;
-    const size_t head = (size_t)bh * N * D;
+    const size_t head = (size_t)bh * N * dh;
     float q[D], o[D];
     for (int x = 0; x < D; ++x) {
-        q[x] = row < N ? Q[head + (size_t)row * D + x] : 0.f;
+        q[x] = row < N && x < dh ? Q[head + (size_t)row * dh + x] : 0.f;
         o[x] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -51,9 +52,9 @@ __global__ void __launch_bounds__(kT) fwd_f32_kernel(const float *Q, const float
         __syncthreads();
         for (int e = threadIdx.x; e < kT * D; e += kT) {
             const int r = e / D, x = e % D;
-            const bool in = k0 + r < N;
-            Ks[r][x] = in ? K[head + (size_t)(k0 + r) * D + x] : 0.f;
-            Vs[r][x] = in ? V[head + (size_t)(k0 + r) * D + x] : 0.f;
+            const bool in = k0 + r < N && x < dh;
+            Ks[r][x] = in ? K[head + (size_t)(k0 + r) * dh + x] : 0.f;
+            Vs[r][x] = in ? V[head + (size_t)(k0 + r) * dh + x] : 0.f;
         }
         __syncthreads();
         if (row >= N)
@@ -84,8 +85,8 @@ __global__ void __launch_bounds__(kT) fwd_f32_kernel(const float *Q, const float
     }
     if (row < N) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        for (int x = 0; x < D; ++x)
-            O[head + (size_t)row * D + x] = o[x] * inv;
+        for (int x = 0; x < dh; ++x)
+            O[head + (size_t)row * dh + x] = o[x] * inv;
         LSE[(size_t)bh * N + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
 }
@@ -95,15 +96,15 @@ __global__ void __launch_bounds__(kT) fwd_f32_kernel(const float *Q, const float
 template <int D>
 __global__ void __launch_bounds__(kT) bwd_pre_f32_kernel(const float *dO, const float *O,
                                                          const float *LSE, float *delta,
-                                                         float *lse2, int N)
+                                                         float *lse2, int N, int dh)
 {
     const int bh = blockIdx.y;
     const int row = blockIdx.x * kT + threadIdx.x;
     if (row >= N)
         return;
-    const size_t base = ((size_t)bh * N + row) * D;
+    const size_t base = ((size_t)bh * N + row) * dh;
     float acc = 0.f;
-    for (int x = 0; x < D; ++x)
+    for (int x = 0; x < dh; ++x)
         acc = fmaf(dO[base + x], O[base + x], acc);
     const size_t r = (size_t)bh * N + row;
     delta[r] = acc;
@@ -116,18 +117,18 @@ template <int D>
 __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const float *Q,
                                                         const float *K, const float *V,
                                                         const float *delta, const float *lse2,
-                                                        float *dQ, int N, float scale, float c,
+                                                        float *dQ, int N, int dh, float scale, float c,
                                                         int causal, const uint8_t *mask, int nmb)
 {
     __shared__ float Ks[kT][D];
     __shared__ float Vs[kT][D];
     const int bh = blockIdx.y;
     const int row = blockIdx.x * kT + threadIdx.x;
-    const size_t head = (size_t)bh * N * D;
+    const size_t head = (size_t)bh * N * dh;
     float q[D], go[D], dq[D];
     for (int x = 0; x < D; ++x) {
-        q[x] = row < N ? Q[head + (size_t)row * D + x] : 0.f;
-        go[x] = row < N ? dO[head + (size_t)row * D + x] : 0.f;
+        q[x] = row < N && x < dh ? Q[head + (size_t)row * dh + x] : 0.f;
+        go[x] = row < N && x < dh ? dO[head + (size_t)row * dh + x] : 0.f;
         dq[x] = 0.f;
     }
     const float Di = row < N ? delta[(size_t)bh * N + row] : 0.f;
@@ -137,9 +138,9 @@ __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const f
         __syncthreads();
         for (int e = threadIdx.x; e < kT * D; e += kT) {
             const int r = e / D, x = e % D;
-            const bool in = k0 + r < N;
-            Ks[r][x] = in ? K[head + (size_t)(k0 + r) * D + x] : 0.f;
-            Vs[r][x] = in ? V[head + (size_t)(k0 + r) * D + x] : 0.f;
+            const bool in = k0 + r < N && x < dh;
+            Ks[r][x] = in ? K[head + (size_t)(k0 + r) * dh + x] : 0.f;
+            Vs[r][x] = in ? V[head + (size_t)(k0 + r) * dh + x] : 0.f;
         }
         __syncthreads();
         if (row >= N)
@@ -160,8 +161,8 @@ __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const f
         }
     }
     if (row < N)
-        for (int x = 0; x < D; ++x)
-            dQ[head + (size_t)row * D + x] = dq[x] * scale;
+        for (int x = 0; x < dh; ++x)
+            dQ[head + (size_t)row * dh + x] = dq[x] * scale;
 }
 
 // One thread per key row. WANT_DK: dK_j = scale * sum_i dS_ij Q_i;
@@ -170,7 +171,7 @@ template <int D, bool WANT_DK>
 __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const float *Q,
                                                          const float *K, const float *V,
                                                          const float *delta, const float *lse2,
-                                                         float *dOut, int N, float scale, float c,
+                                                         float *dOut, int N, int dh, float scale, float c,
                                                          int causal, const uint8_t *mask, int nmb)
 {
     __shared__ float Qs[kT][D];
@@ -178,11 +179,11 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
     __shared__ float Ls[kT], Ds[kT];
     const int bh = blockIdx.y;
     const int key = blockIdx.x * kT + threadIdx.x;
-    const size_t head = (size_t)bh * N * D;
+    const size_t head = (size_t)bh * N * dh;
     float k[D], v[D], acc[D];
     for (int x = 0; x < D; ++x) {
-        k[x] = key < N ? K[head + (size_t)key * D + x] : 0.f;
-        v[x] = (WANT_DK && key < N) ? V[head + (size_t)key * D + x] : 0.f;
+        k[x] = key < N && x < dh ? K[head + (size_t)key * dh + x] : 0.f;
+        v[x] = (WANT_DK && key < N && x < dh) ? V[head + (size_t)key * dh + x] : 0.f;
         acc[x] = 0.f;
     }
     const int qstart = causal ? (int)blockIdx.x * kT : 0;
@@ -190,9 +191,9 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
         __syncthreads();
         for (int e = threadIdx.x; e < kT * D; e += kT) {
             const int r = e / D, x = e % D;
-            const bool in = q0 + r < N;
-            Qs[r][x] = in ? Q[head + (size_t)(q0 + r) * D + x] : 0.f;
-            Gs[r][x] = in ? dO[head + (size_t)(q0 + r) * D + x] : 0.f;
+            const bool in = q0 + r < N && x < dh;
+            Qs[r][x] = in ? Q[head + (size_t)(q0 + r) * dh + x] : 0.f;
+            Gs[r][x] = in ? dO[head + (size_t)(q0 + r) * dh + x] : 0.f;
         }
         {
             const int r = threadIdx.x;
@@ -225,8 +226,8 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
         }
     }
     if (key < N)
-        for (int x = 0; x < D; ++x)
-            dOut[head + (size_t)key * D + x] = WANT_DK ? acc[x] * scale : acc[x];
+        for (int x = 0; x < dh; ++x)
+            dOut[head + (size_t)key * dh + x] = WANT_DK ? acc[x] * scale : acc[x];
 }
 
 template <int D>
@@ -236,7 +237,7 @@ hipError_t fwd_f32_d(const Problem &p, const float *Q, const float *K, const flo
     const dim3 grid((p.N + kT - 1) / kT, p.B * p.H);
     const int nmb = (p.N + kMaskBlock - 1) / kMaskBlock;
     hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, dim3(kT), 0, p.stream, Q, K, V, O, LSE, p.N,
-                       p.scale * kLog2e, p.causal, p.mask, nmb);
+                       p.d, p.scale * kLog2e, p.causal, p.mask, nmb);
     return hipGetLastError();
 }
 
@@ -252,13 +253,13 @@ hipError_t bwd_f32_d(const Problem &p, const float *dO, const float *Q, const fl
     const int nmb = (p.N + kMaskBlock - 1) / kMaskBlock;
     const float c = p.scale * kLog2e;
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), grid, dim3(kT), 0, p.stream, dO, O, LSE, delta,
-                       lse2, p.N);
+                       lse2, p.N, p.d);
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), grid, dim3(kT), 0, p.stream, dO, Q, K, V, delta,
-                       lse2, dQ, p.N, p.scale, c, p.causal, p.mask, nmb);
+                       lse2, dQ, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
     hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, true>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
-                       delta, lse2, dK, p.N, p.scale, c, p.causal, p.mask, nmb);
+                       delta, lse2, dK, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
     hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, false>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
-                       delta, lse2, dV, p.N, p.scale, c, p.causal, p.mask, nmb);
+                       delta, lse2, dV, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
     return hipGetLastError();
 }
 
@@ -267,14 +268,14 @@ hipError_t bwd_f32_d(const Problem &p, const float *dO, const float *Q, const fl
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE)
 {
-    return p.d == 64 ? fwd_f32_d<64>(p, Q, K, V, O, LSE) : fwd_f32_d<128>(p, Q, K, V, O, LSE);
+    return p.d <= 64 ? fwd_f32_d<64>(p, Q, K, V, O, LSE) : fwd_f32_d<128>(p, Q, K, V, O, LSE);
 }
 
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,
                           const float *V, const float *O, const float *LSE, float *dQ,
                           float *dK, float *dV, void *ws)
 {
-    return p.d == 64 ? bwd_f32_d<64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws)
+    return p.d <= 64 ? bwd_f32_d<64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws)
                      : bwd_f32_d<128>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
 }
 

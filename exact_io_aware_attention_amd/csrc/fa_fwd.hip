@@ -68,6 +68,7 @@ struct FwdParams {
     float *LSE;
     const uint8_t *mask;
     int N;
+    int dh;       // head dimension (<= D; columns dh..D-1 are zero padding)
     int nqb;      // query blocks per head
     int nkt;      // 64-key tiles per head
     int nmb;      // mask blocks per mask row
@@ -106,6 +107,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;  // causal: longest rows first
     const int q0 = qblk * BR;
     const int N = p.N;
+    const int dh = p.dh;
     const float c = p.c;
 
     const int tid = threadIdx.x;
@@ -116,7 +118,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     const int wr0 = q0 + wave * RW;
     const int row = wr0 + l32;
 
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const size_t head = (size_t)bh * (size_t)N * dh;
     const uint16_t *Qh = p.Q + head;
     const uint16_t *Kh = p.K + head;
     const uint16_t *Vh = p.V + head;
@@ -125,8 +127,9 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     bf16x8 qf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-        qf[kk] = row < N ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * D + 16 * kk + 8 * hi)
-                         : bf16x8{};
+        qf[kk] = row < N && 16 * kk + 8 * hi < dh
+                     ? *reinterpret_cast<const bf16x8 *>(Qh + (size_t)row * dh + 16 * kk + 8 * hi)
+                     : bf16x8{};
 
     int t_end = p.nkt;
     if (CAUSAL)
@@ -165,18 +168,20 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     auto v_swz = [](int r) -> int {
         return CPR == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
     };
+    // Global rows are dh wide; chunks past dh read as zeros.
     uint32_t kdma[LPW], vdma[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int r = (wave * LPW + i) * (64 / CPR) + lane / CPR;
-        kdma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ k_swz(r)));
-        vdma[i] = 2 * (r * D + 8 * ((lane % CPR) ^ v_swz(r)));
+        const int kc = (lane % CPR) ^ k_swz(r), vc = (lane % CPR) ^ v_swz(r);
+        kdma[i] = 8 * kc < dh ? 2 * (r * dh + 8 * kc) : kBufferOutOfRange;
+        vdma[i] = 8 * vc < dh ? 2 * (r * dh + 8 * vc) : kBufferOutOfRange;
     }
     // Rows past the end of the sequence read as zeros (the buffer resource
     // ends at row N) and are masked.
     auto issue = [&](const uint16_t *src, const uint32_t (&off)[LPW], uint32_t tile, int t)
                      __attribute__((always_inline)) {
-        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * D, (uint32_t)(N - t * BC) * (2 * D));
+        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * dh, (uint32_t)(N - t * BC) * (2 * dh));
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             lds_dma_buf_b128(rs, off[i], tile + (wave * LPW + i) * 1024);
@@ -249,12 +254,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     if (t0 >= t_end) {
         // no visible key tile at all (fully masked rows): O = 0, LSE = -inf
         if (row < N) {
-            uint16_t *Oh = p.O + head + (size_t)row * D;
+            uint16_t *Oh = p.O + head + (size_t)row * dh;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * j + 4 * hi) = uint2{0, 0};
+                    if (32 * db + 8 * j + 4 * hi < dh)
+                        *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * j + 4 * hi) = uint2{0, 0};
             if (hi == 0)
                 p.LSE[(size_t)bh * N + row] = -INFINITY;
         }
@@ -325,7 +331,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
         // K and V of tile j+2 replace tile j-1's, last read before the
-        // previous barrier; tile j+1's were issued one iteration ago.
+        // previous barrier; tile j+1's were issued one iteration ago (its K
+        // has landed, its V may still be in flight).
         const bool more = tnn < t_end;
         if (more) {
             issue_k(tnn, KB_NN);
@@ -406,8 +413,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             for (int db = 0; db < DB; ++db)
                 o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
             // the next half-step's first K^T fragments: tile j+1's first 32
-            // keys, then its second 32 (visible since the last barrier)
+            // keys, then its second 32 (visible since the last barrier). The
+            // latter stay in flight across the barrier below, which then must
+            // find no other read pending: another wave's loads of tile j+3
+            // overwrite tile j's buffer once past it.
             {
+                if (h == 1)
+                    lds_reads_wait_all();
                 const uint32_t nofs = h == 0 ? KB_NXT : KB_NXT + 2 * 32 * D;
 #pragma unroll
                 for (int kk = 0; kk < KK / 2; ++kk)
@@ -425,10 +437,12 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             mx_cur = row_max(s_nxt);  // beside the P V MFMAs still in flight
             s_cur = s_nxt;
         }
-        // tile j+1 has landed (this wave's loads of tile j+2, issued after
-        // it, may still be in flight); the barrier extends that to all waves
+        // Tile j+1's V and tile j+2's K have landed (tile j+2's V, issued
+        // last, may still be in flight); the barrier extends that to all
+        // waves. The next iteration reads tile j+2's K from its second
+        // half-step on and its V one iteration later.
         if (more)
-            lds_dma_wait<2 * LPW>();
+            lds_dma_wait<LPW>();
         else
             lds_dma_wait<0>();
         barrier_reads_in_flight();
@@ -469,11 +483,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     const float lt = halves_sum(l);
     if (row < N) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t *Oh = p.O + head + (size_t)row * D;
+        uint16_t *Oh = p.O + head + (size_t)row * dh;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
+                if (32 * db + 8 * jj + 4 * hi >= dh)
+                    continue;
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16_bits(o[db][4 * jj + 0] * inv) |
                        ((uint32_t)f32_to_bf16_bits(o[db][4 * jj + 1] * inv) << 16);
@@ -519,10 +535,13 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.LSE = LSE;
     fp.mask = pr.mask;
     fp.N = pr.N;
+    fp.dh = pr.d;
     fp.nkt = (pr.N + 63) / 64;
     fp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     fp.c = pr.scale * kLog2e;
-    if (pr.d == 64)
+    // head dims up to 64 run in the 64-wide kernel, the others (up to 128) in
+    // the 128-wide one, zero-padded
+    if (pr.d <= 64)
         return launch_fwd_d<64>(pr, fp);
     return launch_fwd_d<128>(pr, fp);
 }

@@ -37,7 +37,10 @@
  *     block of (query block, key block). One mask serves every (b, h); it is
  *     combined with the causal mask by AND.
  *   - B, H, N >= 0 (any zero means an empty problem: FA_OK, nothing done);
- *     d in {64, 128}; scale finite and > 0; causal is 0 or 1.
+ *     d a multiple of 8 in [8, 128] (d <= 64 runs in the 64-wide kernels and
+ *     64 < d <= 128 in the 128-wide ones, the columns past d taken as zero:
+ *     the cost is that of the padded width); N * d < 2^30; scale finite and
+ *     > 0; causal is 0 or 1.
  *   - stream is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously on it; argument checks happen synchronously, before any
  *     HIP call, and a failed check enqueues nothing.

@@ -62,7 +62,10 @@ def test_forward_validation(fn):
     assert call(LSE=None) == 1
     assert call(N=-1) == 2
     assert call(B=-3) == 2
-    assert call(d=96) == 3
+    assert call(d=100) == 3                     # head dims: multiples of 8 in [8, 128]
+    assert call(d=136) == 3
+    assert call(d=256) == 3
+    assert call(d=4) == 3
     assert call(d=0) == 3
     assert call(O=MIS) == 4
     assert call(scale=0.0) == 5
@@ -70,7 +73,9 @@ def test_forward_validation(fn):
     assert call(scale=float("nan")) == 5
     assert call(scale=float("inf")) == 5
     assert call(causal=2) == 5
-    assert call(N=1 << 30, d=128) == 2          # per-head slab exceeds 31 bits
+    assert call(N=1 << 30, d=128) == 2          # per-head slab exceeds 2^30 elements
+    assert call(N=1 << 23, d=128) == 2
+    assert call(N=(1 << 24) + 8, d=64) == 2
     # empty problems are valid no-ops and touch nothing (even with NULL pointers)
     assert call(B=0, Q=None) == 0
     assert call(H=0) == 0
@@ -81,7 +86,8 @@ def test_backward_validation():
     ws = fa.fa_bwd_workspace_bytes(1, 1, 128, 64)
     assert ws > 0 and ws % 256 == 0
     assert _bwd(dQ=None) == 1
-    assert _bwd(d=32) == 3
+    assert _bwd(d=33) == 3
+    assert _bwd(d=256) == 3
     assert _bwd(dV=MIS) == 4
     assert _bwd(scale=0.0) == 5
     assert _bwd(ws=None) == 6

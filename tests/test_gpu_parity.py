@@ -157,3 +157,58 @@ def test_empty_problem_is_a_no_op():
     fa.fa_fwd(Q, Q, Q, Q, LSE, 0.125)
     fa.fa_bwd(Q, Q, Q, Q, Q, LSE, Q, Q, Q, 0.125)
     torch.cuda.synchronize()
+
+
+HEAD_DIMS = [
+    # (B, H, N, d, causal, sparse): head dims other than 64 and 128 run in the
+    # 64- or 128-wide kernels with the columns past d zero-padded
+    (1, 2, 200, 8, True, False),
+    (1, 1, 130, 40, False, True),
+    (2, 1, 333, 72, True, False),
+    (1, 2, 257, 96, False, False),
+    (1, 1, 190, 120, True, True),
+    (1, 1, 64, 96, True, False),
+]
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor of `shape` at the start of a larger buffer whose tail holds
+    `fill`, to catch stores past the last row."""
+    n = int(np.prod(shape))
+    big = torch.full((n + 4096,), fill, dtype=dtype, device="cuda")
+    return big, big[:n].view(shape)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,N,d,causal,sparse", HEAD_DIMS)
+def test_other_head_dims(precision, B, H, N, d, causal, sparse):
+    seed = 5000 + N + d + 7 * causal + 3 * sparse
+    q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype=precision)
+    nb = (N + 127) // 128
+    mask = None
+    if sparse:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        mask = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(mask, 1)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"{precision} B={B} H={H} N={N} d={d} causal={causal} sparse={sparse}", flush=True)
+    got = _got(*gu.gpu_forward_backward(q, k, v, do, scale, causal, mask, precision))
+    gu.check_outputs(precision, got, _ref_all(q, k, v, do, scale, causal, mask))
+
+    # no store lands past the last row of any output
+    import exact_io_aware_attention_amd as fa
+    dt = torch.bfloat16 if precision == "bf16" else torch.float32
+    Q, K, V, dO = (gu.dev(x, dt) for x in (q, k, v, do))
+    M = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).to("cuda")
+    bufs = {n: _guarded(Q.shape, dt, 7.0) for n in ("O", "dQ", "dK", "dV")}
+    LSE = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    (fa.fa_fwd if precision == "bf16" else fa.fa_fwd_f32)(
+        Q, K, V, bufs["O"][1], LSE, scale, causal=causal, blockmask=M)
+    (fa.fa_bwd if precision == "bf16" else fa.fa_bwd_f32)(
+        dO, Q, K, V, bufs["O"][1], LSE, bufs["dQ"][1], bufs["dK"][1], bufs["dV"][1], scale,
+        causal=causal, blockmask=M)
+    torch.cuda.synchronize()
+    n = Q.numel()
+    for name, (big, view) in bufs.items():
+        assert torch.all(big[n:] == 7.0), f"{name}: store past the end"
+        assert torch.equal(view.float().cpu(), torch.from_numpy(got[name]).float().to(dt).float()), name
