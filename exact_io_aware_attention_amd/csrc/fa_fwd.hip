@@ -47,6 +47,9 @@
 // takes exponents against 0, so no (-inf) - (-inf) arises; it ends with
 // O = 0, LSE = -inf.
 //
+// Head dims below the kernel width D (64 or 128) are zero-padded: the tile
+// loads read zeros for the columns past dh and only dh columns are stored.
+//
 // Masking: causal (key j visible to query i iff j <= i, nanhubrain.csdn.net
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
 // never loaded, and the per-element mask runs only on 32-key steps that
