@@ -64,6 +64,9 @@ class Oracle:
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = [dp, dp, dp, L, L, L, L, ctypes.c_double,
                                               ctypes.c_int, up, L, lp, lp, L, dp, dp]
+        lib.oracle_attention_kv.restype = ctypes.c_int
+        lib.oracle_attention_kv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L,
+                                            ctypes.c_double, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self.lib = lib
@@ -118,6 +121,24 @@ class Oracle:
             raise RuntimeError(f"oracle_attention_rows failed with code {rc}")
         return O, LSE
 
+    def attention_kv(self, q, k, v, scale, causal=False):
+        """Forward of Nq queries against Nk keys per head (decode shape):
+        q [B,H,Nq,d], k and v [B,H,Nk,d]. causal: query i is at position
+        Nk - Nq + i and sees keys up to it. Returns (O [B,H,Nq,d], LSE [B,H,Nq])."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] \
+                or q.shape[3] != k.shape[3]:
+            raise ValueError("q [B,H,Nq,d] and k, v [B,H,Nk,d] expected")
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        O = np.empty_like(q)
+        LSE = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self.lib.oracle_attention_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(O), _ptr(LSE),
+                                          B, H, Nq, Nk, d, float(scale), int(bool(causal)))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_kv failed with code {rc}")
+        return O, LSE
+
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
@@ -138,6 +159,10 @@ def attention(*args, **kwargs):
 
 def attention_rows(*args, **kwargs):
     return default().attention_rows(*args, **kwargs)
+
+
+def attention_kv(*args, **kwargs):
+    return default().attention_kv(*args, **kwargs)
 
 
 def num_threads() -> int:

@@ -241,6 +241,85 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
     return nomem ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }
 
+/*
+ * Decode-shaped forward: Nq queries against Nk keys of the same head (the
+ * queries are the last Nq positions of a sequence whose first Nk positions
+ * are the keys, as when the key/value cache of earlier steps is attended).
+ * What is computed is the same definition as above, row by row:
+ *   S_ij = scale * q_i . k_j,  P_i = softmax(S_i),  O_i = P_i V,
+ *   LSE_i = max_j S_ij + ln sum_j exp(S_ij - max_j S_ij)
+ * (mstx.cn/posts/485 §二.1 and §三.2), with the causal rule P_ij = 0 for
+ * keys after the query's own position: query i sits at position
+ * Nk - Nq + i, so key j is allowed iff j <= Nk - Nq + i (nanhubrain.csdn.net
+ * §三's j > i rule with the query index shifted to its position; for
+ * Nq = Nk it is that rule). No block mask. The split of the keys into chunks
+ * whose partial results are merged afterwards is lukebest.github.io's
+ * FlashDecoding line of the lineage table ("谱系"); this reference does not
+ * split: it is the plain result the merged one must equal.
+ */
+static void decode_row(const double *q, const double *k, const double *v,
+                       long nkeys, long d, double scale, double *srow,
+                       double *orow, double *lse)
+{
+    for (long c = 0; c < d; ++c)
+        orow[c] = 0.0;
+    if (nkeys <= 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (long j = 0; j < nkeys; ++j) {
+        double dot = 0.0;
+        for (long c = 0; c < d; ++c)
+            dot += q[c] * k[j * d + c];
+        srow[j] = scale * dot;
+        if (srow[j] > m)
+            m = srow[j];
+    }
+    double l = 0.0;
+    for (long j = 0; j < nkeys; ++j) {
+        srow[j] = exp(srow[j] - m);
+        l += srow[j];
+    }
+    for (long j = 0; j < nkeys; ++j) {
+        const double p = srow[j] / l;
+        for (long c = 0; c < d; ++c)
+            orow[c] += p * v[j * d + c];
+    }
+    *lse = log(l) + m;
+}
+
+int oracle_attention_kv(const double *Q, const double *K, const double *V,
+                        double *O, double *LSE, long B, long H, long Nq, long Nk,
+                        long d, double scale, int causal)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0)
+        return ORACLE_ERR_ARG;
+    int nomem = 0;
+    #pragma omp parallel
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!srow) {
+            #pragma omp atomic write
+            nomem = 1;
+        } else {
+            #pragma omp for collapse(2) schedule(dynamic, 1)
+            for (long bh = 0; bh < B * H; ++bh)
+                for (long i = 0; i < Nq; ++i) {
+                    long nkeys = Nk;
+                    if (causal) {
+                        const long last = Nk - Nq + i;  /* last allowed key */
+                        nkeys = last + 1 < Nk ? last + 1 : Nk;
+                    }
+                    decode_row(Q + (bh * Nq + i) * d, K + bh * Nk * d, V + bh * Nk * d,
+                               nkeys, d, scale, srow, O + (bh * Nq + i) * d, LSE + bh * Nq + i);
+                }
+        }
+        free(srow);
+    }
+    return nomem ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
 int oracle_num_threads(void)
 {
     return omp_get_max_threads();

@@ -28,6 +28,13 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
                           const long *row_bh, const long *row_i, long nrows,
                           double *O_rows, double *LSE_rows);
 
+/* Forward of Nq queries against Nk keys per head: Q, O are [B][H][Nq][d],
+ * K, V are [B][H][Nk][d], LSE is [B][H][Nq]. causal: query i is at position
+ * Nk - Nq + i and sees keys j <= Nk - Nq + i (none when that is negative). */
+int oracle_attention_kv(const double *Q, const double *K, const double *V,
+                        double *O, double *LSE, long B, long H, long Nq, long Nk,
+                        long d, double scale, int causal);
+
 /* Number of OpenMP threads the reference runs with. */
 int oracle_num_threads(void);
 

@@ -345,6 +345,99 @@ def pin_rows_match_full(orc):
         _close(Lr, LSE.reshape(B * H, N)[rb, ri], 0.0, "rows LSE")
 
 
+# ------------------------------------------------- decode (Nq != Nk) ---
+
+def _kv_allowed(Nq, Nk, causal):
+    """Brute-force visibility for the decode shape: query i sits at position
+    Nk - Nq + i and, when causal, sees the keys up to that position."""
+    A = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        A &= j <= Nk - Nq + i
+    return A
+
+
+def pin_kv_library_sdpa(orc):
+    """Decode-shaped forward equals torch's CPU fp64 scaled_dot_product_attention
+    with the visibility matrix built from the definition, and LSE equals
+    torch.logsumexp of the masked scores."""
+    B, H, d = 2, 2, 8
+    for Nq, Nk in ((1, 19), (5, 23), (8, 8), (3, 2)):
+        q = _rand((B, H, Nq, d), RNG_SEED + 60 + Nq)
+        k = _rand((B, H, Nk, d), RNG_SEED + 70 + Nk)
+        v = _rand((B, H, Nk, d), RNG_SEED + 80 + Nk)
+        for causal in (False, True):
+            O, LSE = orc.attention_kv(q, k, v, 0.45, causal=causal)
+            A = torch.from_numpy(_kv_allowed(Nq, Nk, causal))
+            S = 0.45 * torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2)
+            S = S.masked_fill(~A, float("-inf"))
+            _close(LSE, torch.logsumexp(S, dim=-1).numpy(), 1e-12, "decode logsumexp")
+            rows = A.any(dim=-1).numpy()
+            if rows.all():
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                    attn_mask=A, scale=0.45)
+                _close(O, ref.numpy(), 1e-13, "decode SDPA O")
+            else:  # rows that see no key: O = 0 by convention
+                _close(O[:, :, ~rows], 0.0, 0.0, "decode O without keys")
+
+
+def pin_kv_identical_keys(orc):
+    """All key rows equal -> O_i is the mean of the visible V rows, and
+    LSE_i = scale*q_i.k + ln(#visible); with the causal rule query i sees
+    Nk - Nq + i + 1 keys."""
+    B, H, Nq, Nk, d = 1, 2, 4, 11, 5
+    q = _rand((B, H, Nq, d), RNG_SEED + 90)
+    k = np.broadcast_to(_rand((B, H, 1, d), RNG_SEED + 91), (B, H, Nk, d)).copy()
+    v = _rand((B, H, Nk, d), RNG_SEED + 92)
+    for causal in (False, True):
+        O, LSE = orc.attention_kv(q, k, v, 0.7, causal=causal)
+        for i in range(Nq):
+            n = Nk - Nq + i + 1 if causal else Nk
+            _close(O[:, :, i], v[:, :, :n].mean(axis=2), 1e-14, "decode identical keys O")
+            dots = 0.7 * np.einsum("bhd,bhd->bh", q[:, :, i], k[:, :, 0])
+            _close(LSE[:, :, i], dots + math.log(n), 1e-13, "decode identical keys LSE")
+
+
+def pin_kv_square_and_suffix(orc):
+    """With Nq = Nk the decode forward is the square forward; with Nq < Nk and
+    the causal rule it gives the last Nq rows of the square causal forward
+    over the whole sequence (queries at the last Nq positions)."""
+    B, H, N, d = 1, 2, 13, 6
+    q = _rand((B, H, N, d), RNG_SEED + 93)
+    k = _rand((B, H, N, d), RNG_SEED + 94)
+    v = _rand((B, H, N, d), RNG_SEED + 95)
+    for causal in (False, True):
+        O, LSE = orc.attention_kv(q, k, v, 0.6, causal=causal)
+        Os, Ls = orc.attention(q, k, v, 0.6, causal=causal)
+        _close(O, Os, 1e-14, "decode square O")
+        _close(LSE, Ls, 1e-14, "decode square LSE")
+    Os, Ls = orc.attention(q, k, v, 0.6, causal=True)
+    for nq in (1, 4):
+        O, LSE = orc.attention_kv(q[:, :, N - nq:], k, v, 0.6, causal=True)
+        _close(O, Os[:, :, N - nq:], 1e-14, "decode suffix O")
+        _close(LSE, Ls[:, :, N - nq:], 1e-14, "decode suffix LSE")
+
+
+def pin_kv_split_merge(orc):
+    """Splitting the keys into two chunks and merging the chunk results with
+    weights exp(LSE_chunk - LSE) gives the unsplit result (mstx.cn/posts/485
+    §三.2 merge of partial softmax sums)."""
+    B, H, Nq, Nk, d = 1, 3, 3, 17, 4
+    q = _rand((B, H, Nq, d), RNG_SEED + 96)
+    k = _rand((B, H, Nk, d), RNG_SEED + 97)
+    v = _rand((B, H, Nk, d), RNG_SEED + 98)
+    O, LSE = orc.attention_kv(q, k, v, 0.9)
+    for a in (1, 8, 16):
+        O1, L1 = orc.attention_kv(q, k[:, :, :a], v[:, :, :a], 0.9)
+        O2, L2 = orc.attention_kv(q, k[:, :, a:], v[:, :, a:], 0.9)
+        L = np.logaddexp(L1, L2)
+        Om = np.exp(L1 - L)[..., None] * O1 + np.exp(L2 - L)[..., None] * O2
+        _close(L, LSE, 1e-13, "split LSE")
+        _close(Om, O, 1e-13, "split O")
+
+
 ALL_PINS = [
     pin_identical_keys_uniform,
     pin_zero_query,
@@ -362,4 +455,8 @@ ALL_PINS = [
     pin_finite_differences,
     pin_backward_invariants,
     pin_rows_match_full,
+    pin_kv_library_sdpa,
+    pin_kv_identical_keys,
+    pin_kv_square_and_suffix,
+    pin_kv_split_merge,
 ]

@@ -36,6 +36,12 @@ MUTANTS = [
     ("dK_operand", "dk[j * d + c] += s * q[i * d + c];", "dk[j * d + c] += s * k[i * d + c];"),
     ("dK_no_scale", "dk[j * d + c] *= scale;", "dk[j * d + c] *= 1.0;"),
     ("dV_uses_dS", "dv[j * d + c] += pij * dout[i * d + c];", "dv[j * d + c] += s * dout[i * d + c];"),
+    ("kv_top_left", "const long last = Nk - Nq + i;", "const long last = i;"),
+    ("kv_no_normalise", "const double p = srow[j] / l;", "const double p = srow[j];"),
+    ("kv_lse_no_max", "*lse = log(l) + m;", "*lse = log(l);"),
+    ("kv_qk_index", "dot += q[c] * k[j * d + c];", "dot += q[c] * k[c];"),
+    ("kv_pv_operand", "orow[c] += p * v[j * d + c];", "orow[c] += p * v[c];"),
+    ("kv_no_scale", "srow[j] = scale * dot;", "srow[j] = dot;"),
     ("dV_transposed", "double pij = P[i * N + j];\n                if (s != 0.0)",
      "double pij = P[j * N + i];\n                if (s != 0.0)"),
 ]
