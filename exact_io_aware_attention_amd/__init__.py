@@ -11,9 +11,13 @@ Functions carry the C names:
            blockmask=None, workspace=None, stream=None)
     fa_fwd_f32(...), fa_bwd_f32(...)  -- the fp32 debug path, same arguments
     fa_bwd_workspace_bytes(B, H, N, d)
+    fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None)
+    fa_decode_workspace_bytes(B, H, Nq, Nk, d)
 Tensors are contiguous CUDA (HIP) tensors of shape [B, H, N, d]: bfloat16 for
 fa_fwd / fa_bwd, float32 for the _f32 entry points; LSE is float32 [B, H, N];
 blockmask is uint8 [ceil(N/128), ceil(N/128)] on the same device, or None.
+fa_decode takes Q, O of shape [B, H, Nq, d] and K, V of shape [B, H, Nk, d]
+(bfloat16), LSE float32 [B, H, Nq].
 """
 import ctypes
 import os
@@ -60,6 +64,10 @@ _lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _
                              _sz, _vp]
 _lib.fa_bwd_workspace_bytes.restype = _sz
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.fa_decode.restype = _i
+_lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+_lib.fa_decode_workspace_bytes.restype = _sz
+_lib.fa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 _lib.fa_status_str.restype = ctypes.c_char_p
 _lib.fa_status_str.argtypes = [_i]
 _lib.fa_last_hip_error.restype = ctypes.c_char_p
@@ -69,8 +77,8 @@ _lib.fa_version.argtypes = []
 
 # Symbols declared in include/fa.h (checked by the ABI test).
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_f32",
-            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_status_str", "fa_last_hip_error",
-            "fa_version")
+            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
+            "fa_status_str", "fa_last_hip_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -235,3 +243,27 @@ def new_workspace(B, H, N, d, device="cuda"):
     """A device buffer of fa_bwd_workspace_bytes (torch allocates it)."""
     return torch.empty(max(fa_bwd_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
                        device=device)
+
+
+def fa_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(_lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None):
+    """Decode-shaped forward, bf16: Q, O [B, H, Nq, d]; K, V [B, H, Nk, d];
+    writes O and LSE [B, H, Nq] in place."""
+    import torch
+    qs, ks = _shape(Q), _shape(K)
+    if qs[:2] != ks[:2] or qs[3] != ks[3]:
+        raise ValueError("Q [B, H, Nq, d] and K, V [B, H, Nk, d] must agree on B, H, d")
+    _require((Q, O), torch.bfloat16, qs)
+    _require((K, V), torch.bfloat16, ks)
+    _require_lse(LSE, qs)
+    B, H, Nq, d = qs
+    Nk = ks[2]
+    if workspace is None:
+        workspace = torch.empty(max(fa_decode_workspace_bytes(B, H, Nq, Nk, d), 1),
+                                dtype=torch.uint8, device=Q.device)
+    _check(_lib.fa_decode(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d,
+                          float(scale), int(bool(causal)), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream_ptr(stream)))

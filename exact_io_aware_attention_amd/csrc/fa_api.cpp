@@ -240,6 +240,53 @@ fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), workspace));
 }
 
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d)
+{
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk < 0 || d <= 0)
+        return 0;
+    return fa::decode_split(B, H, Nq, Nk, d).bytes;
+}
+
+fa_status fa_decode(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                    int H, int Nq, int Nk, int d, float scale, int causal, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    bool empty = false;
+    // the key side and the query side each pass the checks of a [B][H][N][d]
+    // tensor (Nk may be 0: every query then sees no key)
+    fa_status st = check_common(B, H, Nq, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    bool no_keys = false;
+    st = check_common(B, H, Nk, d, scale, causal, &no_keys);
+    if (st != FA_OK)
+        return st;
+    if (empty)
+        return FA_OK;
+    st = check_ptrs({Q, O, LSE});
+    if (st == FA_OK && !no_keys)
+        st = check_ptrs({K, V});
+    if (st != FA_OK)
+        return st;
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk, d);
+    if (workspace == nullptr || workspace_bytes < sp.bytes ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return FA_ERR_WORKSPACE;
+    fa::DecodeProblem p;
+    p.B = B;
+    p.H = H;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.d = d;
+    p.scale = scale;
+    p.causal = causal;
+    p.stream = static_cast<hipStream_t>(stream);
+    return hip_status(fa::launch_decode_bf16(p, static_cast<const uint16_t *>(Q),
+                                             static_cast<const uint16_t *>(K),
+                                             static_cast<const uint16_t *>(V),
+                                             static_cast<uint16_t *>(O), LSE, workspace));
+}
+
 fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE, int B,
                      int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
                      void *stream)
@@ -262,7 +309,7 @@ const char *fa_status_str(fa_status s)
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer";
     case FA_ERR_SHAPE: return "invalid shape";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (d must be a multiple of 8 in [8, 128])";
     case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

@@ -44,6 +44,26 @@ hipError_t launch_bwd_dq_bf16(const Problem &p, const uint16_t *dO, const uint16
 hipError_t launch_bwd_dkdv_bf16(const Problem &p, const uint16_t *dO, const uint16_t *Q,
                                 const uint16_t *K, const uint16_t *V, uint16_t *dK,
                                 uint16_t *dV, const void *workspace);
+// Decode-shaped forward: Nq queries against Nk keys per head.
+struct DecodeProblem {
+    int B, H, Nq, Nk, d;
+    float scale;
+    int causal;  // queries at the last Nq positions: query i sees keys <= Nk - Nq + i
+    hipStream_t stream;
+};
+// How the keys are split (a pure function of the shape) and the workspace it
+// needs: per split, query and column an fp32 O, then per split and query an
+// fp32 LSE (offset lpart_off).
+struct DecodeSplit {
+    int nsplit;        // key chunks per head
+    int chunk;         // keys per chunk
+    size_t lpart_off;  // byte offset of the LSE part
+    size_t bytes;      // total
+};
+DecodeSplit decode_split(int B, int H, int Nq, int Nk, int d);
+hipError_t launch_decode_bf16(const DecodeProblem &p, const uint16_t *Q, const uint16_t *K,
+                              const uint16_t *V, uint16_t *O, float *LSE, void *workspace);
+
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE);
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,

@@ -116,6 +116,33 @@ fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *
                       const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/* Bytes of device scratch fa_decode needs for this shape (0 for an empty
+ * problem). It depends on the shape only. */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/* Decode-shaped forward, bf16: Nq queries per head against Nk keys of the
+ * same head, for the few newest positions of a sequence attending to its
+ * cached keys and values (lukebest.github.io FlashAttention, lineage table
+ * "谱系", the FlashDecoding line: with few queries the keys are split into
+ * chunks processed in parallel, and the chunk results are merged with the
+ * online-softmax rule of mstx.cn/posts/485 §三.2).
+ *   Q, O: [B][H][Nq][d] bf16;  K, V: [B][H][Nk][d] bf16;  LSE: [B][H][Nq]
+ *   float, natural log.  O_i = softmax(scale q_i K^T) V over the keys query
+ *   i sees: all of them, or with causal = 1 the keys j <= Nk - Nq + i (the
+ *   queries are the last Nq positions; for Nq = Nk this is fa_fwd's causal
+ *   rule). A query that sees no key gets O_i = 0, LSE_i = -inf.
+ *   No block mask. Same head-dim, scale and alignment rules as fa_fwd, with
+ *   Nq >= 0 and Nk >= 0 each meeting fa_fwd's limits on N.
+ *   workspace: device memory of at least fa_decode_workspace_bytes(B, H, Nq,
+ *   Nk, d) bytes, 256-byte aligned, owned by the caller; its contents on
+ *   entry do not matter and calls sharing it must be ordered on one stream.
+ *   Meant for small Nq (each 32-query block reads all of K and V once).
+ *   Returns FA_ERR_WORKSPACE when the workspace is missing, misaligned or
+ *   too small. */
+fa_status fa_decode(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                    int H, int Nq, int Nk, int d, float scale, int causal, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* fp32 debug path: the same tiled online-softmax algorithm with every tensor
  * in float and fp32 arithmetic throughout. Same argument rules. */
 fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, float *LSE,

@@ -116,3 +116,45 @@ def test_binding_raises_on_bad_status():
     with pytest.raises(fa.FaError) as e:
         fa._check(3)
     assert "FA_ERR_HEADDIM" in str(e.value)
+
+
+def _dec(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H=2, Nq=4, Nk=1000, d=128, scale=0.1, causal=1,
+             ws=P, wsb=1 << 30)
+    a.update(kw)
+    return fa.lib().fa_decode(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Nq"],
+                              a["Nk"], a["d"], a["scale"], a["causal"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    ws = fa.fa_decode_workspace_bytes(1, 2, 4, 1000, 128)
+    assert ws > 0 and ws % 256 == 0
+    assert _dec(Q=None) == 1
+    assert _dec(LSE=None) == 1
+    assert _dec(K=None) == 1                      # keys present: K and V required
+    assert _dec(Nq=-1) == 2
+    assert _dec(Nk=-1) == 2
+    assert _dec(Nk=1 << 23) == 2                  # key slab exceeds 2^30 elements
+    assert _dec(d=100) == 3
+    assert _dec(d=136) == 3
+    assert _dec(O=MIS) == 4
+    assert _dec(scale=0.0) == 5
+    assert _dec(causal=3) == 5
+    assert _dec(ws=None) == 6
+    assert _dec(wsb=ws - 1) == 6
+    assert _dec(ws=P + 64, wsb=ws) == 6           # workspace must be 256-byte aligned
+    assert _dec(Nq=0, Q=None, O=None) == 0        # empty: nothing done
+    assert _dec(B=0) == 0
+
+
+def test_decode_workspace_bytes():
+    assert fa.fa_decode_workspace_bytes(0, 1, 1, 100, 64) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 0, 100, 64) == 0
+    # one chunk of a short key range: O part (Nq x d fp32) and LSE part, each
+    # 256-byte padded
+    assert fa.fa_decode_workspace_bytes(1, 1, 3, 100, 64) == 768 + 256
+    assert fa.fa_decode_workspace_bytes(1, 1, 3, 100, 40) == 512 + 256
+    # the split count depends on the shape only and grows with Nk
+    a = fa.fa_decode_workspace_bytes(1, 8, 1, 4096, 128)
+    b = fa.fa_decode_workspace_bytes(1, 8, 1, 65536, 128)
+    assert 0 < a < b

@@ -212,3 +212,40 @@ def test_other_head_dims(precision, B, H, N, d, causal, sparse):
     for name, (big, view) in bufs.items():
         assert torch.all(big[n:] == 7.0), f"{name}: store past the end"
         assert torch.equal(view.float().cpu(), torch.from_numpy(got[name]).float().to(dt).float()), name
+
+
+DECODE = [
+    # (B, H, Nq, Nk, d, causal)
+    (1, 2, 1, 1, 128, True),
+    (2, 3, 1, 777, 128, False),
+    (1, 4, 4, 2048, 128, True),
+    (2, 2, 7, 1500, 64, True),
+    (1, 2, 16, 5000, 96, False),
+    (1, 1, 33, 300, 128, True),      # two query blocks
+    (1, 2, 40, 24, 64, True),        # Nq > Nk: the first rows see no key
+    (1, 2, 3, 0, 64, False),         # no keys at all
+    (1, 1, 8, 40000, 128, True),     # many chunks
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", DECODE)
+def test_decode_against_oracle(B, H, Nq, Nk, d, causal):
+    import exact_io_aware_attention_amd as fa
+    seed = 7000 + Nq + Nk + d + causal
+    q = syn.random_inputs(B, H, Nq, d, seed, dtype="bf16")[0]
+    k, v = syn.random_inputs(B, H, Nk, d, seed + 1, dtype="bf16")[1:3] if Nk > 0 else (
+        np.zeros((B, H, 0, d)), np.zeros((B, H, 0, d)))
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"decode B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}", flush=True)
+    Q = gu.dev(q, torch.bfloat16)
+    K, V = gu.dev(k, torch.bfloat16), gu.dev(v, torch.bfloat16)
+    O = torch.full_like(Q, 3.0)
+    LSE = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    # a workspace holding garbage: its contents on entry must not matter
+    ws = torch.full((max(fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d), 1),), 0x7f,
+                    dtype=torch.uint8, device="cuda")
+    fa.fa_decode(Q, K, V, O, LSE, scale, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_kv(q, k, v, scale, causal=causal)
+    gu.check_outputs("bf16", {"O": gu.host(O), "LSE": gu.host(LSE)}, {"O": Or, "LSE": Lr},
+                     fields=("O", "LSE"))
