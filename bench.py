@@ -12,7 +12,10 @@ scaled by the kept-block fraction under a block mask). Per-kernel durations
 come from HIP events recorded on the stream the kernels run on.
 
 Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
---cpu-heads H (heads of the CPU fp64 reference timed as the baseline; 0 skips).
+--cpu-heads H (heads of the CPU fp64 reference timed as the baseline; 0 skips)
+--supp-steps S (the same shape without the causal mask) --decode-steps S (the
+split-KV decode path on its own workload, HBM-bound). The supplementary runs
+are reported beside the headline and never enter `value`.
 """
 import argparse
 import json
@@ -40,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--supp-steps", type=int, default=10,
                     help="timed steps of the supplementary non-causal run (0: skip)")
+    ap.add_argument("--decode-steps", type=int, default=10,
+                    help="timed calls of the supplementary split-KV decode run (0: skip)")
     return ap.parse_args()
 
 
@@ -83,6 +88,50 @@ def flop_counts(cfg, mask):
     if mask is not None:
         fwd *= float(mask.mean())
     return fwd, 2.5 * fwd
+
+
+# Split-KV decode workload: one new query per sequence against a 32K-token
+# cache, 8 sequences x 32 heads, d = 128 (the key/value cache is 4.3 GB, so
+# the path is bound by reading it once from HBM).
+DECODE_SHAPE = dict(B=8, H=32, Nq=1, Nk=32768, d=128)
+
+
+def decode_run(steps):
+    """fa_decode on DECODE_SHAPE with seeded N(0,1) bf16 inputs drawn on the
+    device; median of `steps` calls timed with HIP events on the stream."""
+    import torch
+    import exact_io_aware_attention_amd as fa
+    B, H, Nq, Nk, d = (DECODE_SHAPE[x] for x in ("B", "H", "Nq", "Nk", "d"))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31337)
+    Q = torch.randn((B, H, Nq, d), generator=g, device="cuda").bfloat16()
+    K = torch.randn((B, H, Nk, d), generator=g, device="cuda").bfloat16()
+    V = torch.randn((B, H, Nk, d), generator=g, device="cuda").bfloat16()
+    O = torch.empty_like(Q)
+    LSE = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8,
+                     device="cuda")
+    scale = d ** -0.5
+    for _ in range(3):
+        fa.fa_decode(Q, K, V, O, LSE, scale, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        fa.fa_decode(Q, K, V, O, LSE, scale, causal=True, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    t = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
+    # algorithmic bytes: K and V once, Q and O once, LSE
+    byts = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+    gbs = byts / t / 1e9
+    out = {"workload": "split-KV decode (supplementary)", **DECODE_SHAPE, "causal": True,
+           "us": round(t * 1e6, 1), "gbs": round(gbs, 1), "bound": "hbm",
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": byts,
+           "steps": steps}
+    del Q, K, V, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -213,6 +262,10 @@ def main():
                 "bwd_ms": round(b_s * 1e3, 4), "bwd_tflops": round(2 * bwd_flops / b_s / 1e12, 2),
                 "steps": args.supp_steps}
 
+    decode = None
+    if args.decode_steps > 0:
+        decode = decode_run(args.decode_steps)
+
     cpu = None
     if args.cpu_heads > 0:
         import oracle
@@ -253,6 +306,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "supplementary": supp,
+        "decode": decode,
     }
     print(json.dumps(out), flush=True)
 

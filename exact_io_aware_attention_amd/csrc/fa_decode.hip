@@ -23,8 +23,8 @@
 // normalised O and LSE (fp32) to the workspace. The path is bound by reading
 // K and V from HBM once; the MFMA work per byte is small.
 //
-// Kernel 2, decode_merge_kernel: one wave per (head, query) merges the chunk
-// results and writes O (bf16) and LSE.
+// Kernel 2, decode_merge_kernel: merges the chunk results of each (head,
+// query) and writes O (bf16) and LSE.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -225,45 +225,78 @@ __global__ void __launch_bounds__(kDecWaves * kWave, 1) decode_partial_kernel(De
     }
 }
 
-// One wave per (head, query): LSE = M + ln sum_s exp(LSE_s - M) with
-// M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s; no visible key at all
-// gives O = 0, LSE = -inf.
-__global__ void __launch_bounds__(kWave) decode_merge_kernel(const float *Opart, const float *Lpart,
-                                                            uint16_t *O, float *LSE, int Nq, int dh,
-                                                            int nsplit)
+// Merge of the chunk results: LSE = M + ln sum_s exp(LSE_s - M) with
+// M = max_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s; no visible key at all gives
+// O = 0, LSE = -inf. A workgroup covers 32 columns of one (head, query) row;
+// its 8 groups of 32 threads take every 8th chunk (coalesced 128-byte reads
+// of the chunks' rows, independent of one another) and add up through LDS.
+constexpr int kMergeCols = 32;
+constexpr int kMergeGroups = 8;
+
+__global__ void __launch_bounds__(kMergeCols * kMergeGroups)
+    decode_merge_kernel(const float *Opart, const float *Lpart, uint16_t *O, float *LSE, int Nq,
+                        int dh, int nsplit)
 {
+    __shared__ float red[kMergeGroups][kMergeCols];
+    __shared__ float stat[2][kMergeGroups];
     const long row = blockIdx.x;  // bh * Nq + q
     const long bh = row / Nq;
     const int q = (int)(row % Nq);
-    const int lane = threadIdx.x;
-    const float *L = Lpart + (size_t)bh * nsplit * Nq + q;  // stride Nq over splits
+    const int t = threadIdx.x;
+    const int g = t / kMergeCols;               // group (one wave holds two)
+    const int col = blockIdx.y * kMergeCols + t % kMergeCols;
+    const float *L = Lpart + (size_t)bh * nsplit * Nq + q;  // stride Nq over chunks
+
+    // M and W over all chunks: per thread, then per wave, then per workgroup
     float M = -INFINITY;
-    for (int sp = lane; sp < nsplit; sp += kWave)
+    for (int sp = t; sp < nsplit; sp += kMergeCols * kMergeGroups)
         M = fmaxf(M, L[(size_t)sp * Nq]);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off /= 2)
         M = fmaxf(M, __shfl_xor(M, off, kWave));
+    if (t % kWave == 0)
+        stat[0][t / kWave] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeCols * kMergeGroups / kWave; ++w)
+        M = fmaxf(M, stat[0][w]);
     float W = 0.f;
-    for (int sp = lane; sp < nsplit; sp += kWave) {
-        const float ls = L[(size_t)sp * Nq];
-        W += ls == -INFINITY ? 0.f : __expf(ls - M);
-    }
+    if (M != -INFINITY)
+        for (int sp = t; sp < nsplit; sp += kMergeCols * kMergeGroups) {
+            const float ls = L[(size_t)sp * Nq];
+            W += ls == -INFINITY ? 0.f : __expf(ls - M);
+        }
 #pragma unroll
     for (int off = kWave / 2; off > 0; off /= 2)
         W += __shfl_xor(W, off, kWave);
+    if (t % kWave == 0)
+        stat[1][t / kWave] = W;
+    __syncthreads();
+    W = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeCols * kMergeGroups / kWave; ++w)
+        W += stat[1][w];
     const float lse = M == -INFINITY ? -INFINITY : M + __logf(W);
-    uint16_t *Orow = O + (size_t)row * dh;
-    for (int col = lane; col < dh; col += kWave) {
-        float acc = 0.f;
-        if (M != -INFINITY)
-            for (int sp = 0; sp < nsplit; ++sp) {
-                const float ls = L[(size_t)sp * Nq];
-                if (ls != -INFINITY)
-                    acc = fmaf(__expf(ls - lse), Opart[((size_t)(bh * nsplit + sp) * Nq + q) * dh + col], acc);
-            }
-        Orow[col] = f32_to_bf16_bits(acc);
+
+    float acc = 0.f;
+    if (col < dh && M != -INFINITY) {
+#pragma unroll 4
+        for (int sp = g; sp < nsplit; sp += kMergeGroups) {
+            const float ls = L[(size_t)sp * Nq];
+            const float v = Opart[((size_t)(bh * nsplit + sp) * Nq + q) * dh + col];
+            acc = fmaf(ls == -INFINITY ? 0.f : __expf(ls - lse), v, acc);
+        }
     }
-    if (lane == 0)
+    red[g][t % kMergeCols] = acc;
+    __syncthreads();
+    if (g == 0 && col < dh) {
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMergeGroups; ++k)
+            o += red[k][t];
+        O[(size_t)row * dh + col] = f32_to_bf16_bits(o);
+    }
+    if (blockIdx.y == 0 && t == 0)
         LSE[row] = lse;
 }
 
@@ -296,8 +329,10 @@ hipError_t decode_d(const DecodeProblem &pr, const DecodeSplit &sp, const uint16
     if (e != hipSuccess)
         return e;
     const long rows = (long)pr.B * pr.H * pr.Nq;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)rows), dim3(kWave), 0, pr.stream,
-                       dp.Opart, dp.Lpart, O, LSE, pr.Nq, pr.d, sp.nsplit);
+    const unsigned colblocks = (unsigned)((pr.d + kMergeCols - 1) / kMergeCols);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)rows, colblocks),
+                       dim3(kMergeCols * kMergeGroups), 0, pr.stream, dp.Opart, dp.Lpart, O, LSE,
+                       pr.Nq, pr.d, sp.nsplit);
     return hipGetLastError();
 }
 
