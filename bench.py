@@ -48,14 +48,20 @@ def parse():
     return ap.parse_args()
 
 
+# Sources the forward and backward kernels are built from (the decode path
+# and the host-side ABI layer do not enter them).
+KERNEL_SOURCES = ("csrc/fa_common.h", "csrc/fa_internal.h", "csrc/fa_fwd.hip", "csrc/fa_bwd.hip",
+                  "build.py")
+
+
 def kernel_source_sha256():
-    """sha256 over the kernel sources and their build script (as recorded in
-    the traffic profile when its counters were taken)."""
-    import glob
+    """sha256 over the forward/backward kernel sources and their build script
+    (as recorded in the traffic profile when its counters were taken)."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "exact_io_aware_attention_amd")
-    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
+    for rel in KERNEL_SOURCES:
+        f = os.path.join(pkg, rel)
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()
@@ -70,7 +76,7 @@ def measured_traffic(workload_tag, symbol):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"sha256 \(csrc/\* \+ build\.py\): `([0-9a-f]+)`", text)
+    m = re.search(r"Kernel sources sha256 \([^)]*\): `([0-9a-f]+)`", text)
     if not m or m.group(1) != kernel_source_sha256():
         return None
     for line in text.splitlines():
