@@ -64,6 +64,15 @@ class Oracle:
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = [dp, dp, dp, L, L, L, L, ctypes.c_double,
                                               ctypes.c_int, up, L, lp, lp, L, dp, dp]
+        u32p = ctypes.POINTER(ctypes.c_uint)
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_dropout_keep.restype = ctypes.c_int
+        lib.oracle_dropout_keep.argtypes = [L, L, L, ctypes.c_double, ctypes.c_ulonglong]
+        lib.oracle_attention_dropout.restype = ctypes.c_int
+        lib.oracle_attention_dropout.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                 L, L, L, L, ctypes.c_double, ctypes.c_int, up,
+                                                 L, ctypes.c_double, ctypes.c_ulonglong]
         lib.oracle_attention_kv.restype = ctypes.c_int
         lib.oracle_attention_kv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L,
                                             ctypes.c_double, ctypes.c_int]
@@ -121,6 +130,42 @@ class Oracle:
             raise RuntimeError(f"oracle_attention_rows failed with code {rc}")
         return O, LSE
 
+    def philox4x32_10(self, ctr, key):
+        """Philox4x32-10 of a 4-word counter and 2-word key -> 4 words."""
+        c = (ctypes.c_uint * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+        kk = (ctypes.c_uint * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+        o = (ctypes.c_uint * 4)()
+        self.lib.oracle_philox4x32_10(c, kk, o)
+        return [int(x) for x in o]
+
+    def dropout_keep(self, bh, i, j, p_drop, seed):
+        """1 if element (i, j) of head bh is kept under dropout p_drop, seed."""
+        return int(self.lib.oracle_dropout_keep(bh, i, j, float(p_drop), int(seed)))
+
+    def attention_dropout(self, q, k, v, scale, p_drop, seed, causal=False, blockmask=None,
+                          blk=MASK_BLOCK, do=None):
+        """attention() with dropout on P: returns (O, LSE) or (O, LSE, dQ, dK, dV)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, N, d = _shape(q, k, v)
+        m = _mask(blockmask, N, blk)
+        O = np.empty_like(q)
+        LSE = np.empty((B, H, N), dtype=np.float64)
+        if do is not None:
+            do = _f64(do)
+            dQ, dK, dV = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        else:
+            dQ = dK = dV = None
+        rc = self.lib.oracle_attention_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(O),
+                                               _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                               B, H, N, d, float(scale), int(bool(causal)),
+                                               _ptr(m, ctypes.c_ubyte), blk, float(p_drop),
+                                               int(seed))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_dropout failed with code {rc}")
+        if do is None:
+            return O, LSE
+        return O, LSE, dQ, dK, dV
+
     def attention_kv(self, q, k, v, scale, causal=False):
         """Forward of Nq queries against Nk keys per head (decode shape):
         q [B,H,Nq,d], k and v [B,H,Nk,d]. causal: query i is at position
@@ -163,6 +208,18 @@ def attention_rows(*args, **kwargs):
 
 def attention_kv(*args, **kwargs):
     return default().attention_kv(*args, **kwargs)
+
+
+def attention_dropout(*args, **kwargs):
+    return default().attention_dropout(*args, **kwargs)
+
+
+def dropout_keep(*args, **kwargs):
+    return default().dropout_keep(*args, **kwargs)
+
+
+def philox4x32_10(*args, **kwargs):
+    return default().philox4x32_10(*args, **kwargs)
 
 
 def num_threads() -> int:

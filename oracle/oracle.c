@@ -242,6 +242,180 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
 }
 
 /*
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): a 4 x 32-bit counter and a 2 x 32-bit key give
+ * 4 x 32 random bits. One round multiplies counter words 0 and 2 by the
+ * constants 0xD2511F53 and 0xCD9E8D57 into 64-bit products, and the new
+ * counter is (hi(c2 M1) ^ c1 ^ k0, lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0));
+ * between rounds the key is advanced by (0x9E3779B9, 0xBB67AE85).
+ */
+void oracle_philox4x32_10(const unsigned int ctr_in[4], const unsigned int key_in[2],
+                          unsigned int out[4])
+{
+    unsigned int c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    unsigned int k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned long long p0 = (unsigned long long)0xD2511F53u * c[0];
+        const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c[2];
+        const unsigned int n0 = (unsigned int)(p1 >> 32) ^ c[1] ^ k0;
+        const unsigned int n1 = (unsigned int)p1;
+        const unsigned int n2 = (unsigned int)(p0 >> 32) ^ c[3] ^ k1;
+        const unsigned int n3 = (unsigned int)p0;
+        c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+    }
+    out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
+}
+
+/*
+ * Dropout mask (the drawing rule is this library's, the pages only place
+ * dropout among the fused steps: lukebest.github.io FlashAttention, "Kernel
+ * fusion"): element (i, j) of head bh is dropped iff word j % 4 of
+ * Philox4x32-10(counter = (j / 4, i, bh, 0), key = (seed low, seed high)) is
+ * below floor(p_drop * 2^32); kept weights are scaled by 1 / (1 - p_drop).
+ */
+static unsigned int drop_threshold(double p_drop)
+{
+    const double t = floor(p_drop * 4294967296.0);
+    return t >= 4294967295.0 ? 4294967295u : (unsigned int)t;
+}
+
+int oracle_dropout_keep(long bh, long i, long j, double p_drop, unsigned long long seed)
+{
+    const unsigned int ctr[4] = {(unsigned int)(j / 4), (unsigned int)i, (unsigned int)bh, 0u};
+    const unsigned int key[2] = {(unsigned int)seed, (unsigned int)(seed >> 32)};
+    unsigned int w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    return w[j % 4] >= drop_threshold(p_drop);
+}
+
+/*
+ * Attention with dropout on P, forward and (dO != NULL) backward, written out
+ * with N x N intermediates like oracle_attention:
+ *   P = softmax(S) (S as above, masks included), Z_ij in {0, 1} the mask,
+ *   P~ = P o Z / (1 - p),  O = P~ V,  LSE from P's statistics (no dropout);
+ *   dV = P~^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *   dS = P o (Z o dP / (1 - p) - D 1^T),  dQ = scale dS K,  dK = scale dS^T Q.
+ * (D_i = sum_j P~_ij dP_ij because O_i = sum_j P~_ij V_j; dS is the softmax
+ * Jacobian applied to the gradient reaching P, Z o dP / (1 - p).)
+ */
+int oracle_attention_dropout(const double *Q, const double *K, const double *V,
+                             const double *dO, double *O, double *LSE,
+                             double *dQ, double *dK, double *dV,
+                             long B, long H, long N, long d, double scale, int causal,
+                             const unsigned char *blockmask, long blk,
+                             double p_drop, unsigned long long seed)
+{
+    int rc = check_args(B, H, N, d, blk);
+    if (rc != ORACLE_OK)
+        return rc;
+    if (!(p_drop >= 0.0 && p_drop < 1.0))
+        return ORACLE_ERR_ARG;
+    const int want_bwd = (dO != NULL);
+    if (want_bwd && (dQ == NULL || dK == NULL || dV == NULL))
+        return ORACLE_ERR_ARG;
+    if (N == 0)
+        return ORACLE_OK;
+    const long nb = (N + blk - 1) / blk;
+    const double inv_keep = 1.0 / (1.0 - p_drop);
+    double *P = (double *)malloc(sizeof(double) * (size_t)N * (size_t)N);
+    double *Z = (double *)malloc(sizeof(double) * (size_t)N * (size_t)N);
+    double *D = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    if (!P || !Z || !D) {
+        free(P); free(Z); free(D);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (long bh = 0; bh < B * H; ++bh) {
+        const double *q = Q + bh * N * d, *k = K + bh * N * d, *v = V + bh * N * d;
+        double *o = O + bh * N * d, *lse = LSE + bh * N;
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            /* P_i and LSE_i (O_i from forward_row is replaced below) */
+            forward_row(q, k, v, N, d, scale, causal, blockmask, blk, nb, i,
+                        P + i * N, o + i * d, lse + i);
+            for (long j = 0; j < N; ++j)
+                Z[i * N + j] = oracle_dropout_keep(bh, i, j, p_drop, seed) ? 1.0 : 0.0;
+            for (long c = 0; c < d; ++c)
+                o[i * d + c] = 0.0;
+            for (long j = 0; j < N; ++j) {
+                const double pt = P[i * N + j] * Z[i * N + j] * inv_keep;
+                if (pt != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        o[i * d + c] += pt * v[j * d + c];
+            }
+        }
+        if (!want_bwd)
+            continue;
+        const double *dout = dO + bh * N * d;
+        double *dq = dQ + bh * N * d, *dk = dK + bh * N * d, *dv = dV + bh * N * d;
+        /* overwrite Z with dS row by row once D_i is known */
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            double Di = 0.0;
+            for (long c = 0; c < d; ++c)
+                Di += o[i * d + c] * dout[i * d + c];
+            D[i] = Di;
+        }
+        /* dV_j = sum_i P~_ij dO_i (before Z is overwritten) */
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long j = 0; j < N; ++j) {
+            for (long c = 0; c < d; ++c)
+                dv[j * d + c] = 0.0;
+            for (long i = 0; i < N; ++i) {
+                const double pt = inv_keep * Z[i * N + j] * P[i * N + j];
+                if (pt != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        dv[j * d + c] += pt * dout[i * d + c];
+            }
+        }
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long i = 0; i < N; ++i) {
+            for (long j = 0; j < N; ++j) {
+                const double pij = P[i * N + j];
+                double g = 0.0;
+                if (pij != 0.0) {
+                    double dp = 0.0;
+                    for (long c = 0; c < d; ++c)
+                        dp += v[j * d + c] * dout[i * d + c];
+                    g = pij * (Z[i * N + j] * dp * inv_keep - D[i]);
+                }
+                Z[i * N + j] = g;  /* now dS */
+            }
+            for (long c = 0; c < d; ++c)
+                dq[i * d + c] = 0.0;
+            for (long j = 0; j < N; ++j) {
+                const double ds = Z[i * N + j];
+                if (ds != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        dq[i * d + c] += ds * k[j * d + c];
+            }
+            for (long c = 0; c < d; ++c)
+                dq[i * d + c] = scale * dq[i * d + c];
+        }
+        #pragma omp parallel for schedule(dynamic, 16)
+        for (long j = 0; j < N; ++j) {
+            for (long c = 0; c < d; ++c)
+                dk[j * d + c] = 0.0;
+            for (long i = 0; i < N; ++i) {
+                const double ds = Z[i * N + j];
+                if (ds != 0.0)
+                    for (long c = 0; c < d; ++c)
+                        dk[j * d + c] += ds * q[i * d + c];
+            }
+            for (long c = 0; c < d; ++c)
+                dk[j * d + c] = scale * dk[j * d + c];
+        }
+    }
+    free(P);
+    free(Z);
+    free(D);
+    return ORACLE_OK;
+}
+
+/*
  * Decode-shaped forward: Nq queries against Nk keys of the same head (the
  * queries are the last Nq positions of a sequence whose first Nk positions
  * are the keys, as when the key/value cache of earlier steps is attended).

@@ -35,6 +35,22 @@ int oracle_attention_kv(const double *Q, const double *K, const double *V,
                         double *O, double *LSE, long B, long H, long Nq, long Nk,
                         long d, double scale, int causal);
 
+/* Philox4x32-10: counter ctr[4], key key[2] -> out[4]. */
+void oracle_philox4x32_10(const unsigned int ctr[4], const unsigned int key[2],
+                          unsigned int out[4]);
+
+/* Dropout mask bit (1 = kept) of element (i, j) of head bh: word j % 4 of
+ * Philox4x32-10((j / 4, i, bh, 0), (seed low, seed high)) >= floor(p 2^32). */
+int oracle_dropout_keep(long bh, long i, long j, double p_drop, unsigned long long seed);
+
+/* oracle_attention with dropout on P (kept weights scaled by 1 / (1 - p)). */
+int oracle_attention_dropout(const double *Q, const double *K, const double *V,
+                             const double *dO, double *O, double *LSE,
+                             double *dQ, double *dK, double *dV,
+                             long B, long H, long N, long d, double scale, int causal,
+                             const unsigned char *blockmask, long blk,
+                             double p_drop, unsigned long long seed);
+
 /* Number of OpenMP threads the reference runs with. */
 int oracle_num_threads(void);
 

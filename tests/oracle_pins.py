@@ -438,6 +438,101 @@ def pin_kv_split_merge(orc):
         _close(Om, O, 1e-13, "split O")
 
 
+# ---------------------------------------------------------------- dropout ---
+
+def pin_philox_known_answers(orc):
+    """Philox4x32-10 reproduces the known-answer vectors published with the
+    generator (counter, key -> output): zeros, all ones, and the digits of pi."""
+    kat = [
+        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+    ]
+    for ctr, key, want in kat:
+        got = orc.philox4x32_10(ctr, key)
+        assert got == want, f"philox {ctr} {key}: {[hex(x) for x in got]}"
+
+
+def _drop_mask(orc, BH, N, p, seed):
+    Z = np.zeros((BH, N, N))
+    for bh in range(BH):
+        for i in range(N):
+            for j in range(N):
+                Z[bh, i, j] = orc.dropout_keep(bh, i, j, p, seed)
+    return Z
+
+
+def pin_dropout_zero_is_plain(orc):
+    """Dropout probability 0 gives exactly the plain forward and backward."""
+    B, H, N, d = 1, 2, 9, 4
+    q = _rand((B, H, N, d), RNG_SEED + 100)
+    k = _rand((B, H, N, d), RNG_SEED + 101)
+    v = _rand((B, H, N, d), RNG_SEED + 102)
+    do = _rand((B, H, N, d), RNG_SEED + 103)
+    for causal in (False, True):
+        a = orc.attention(q, k, v, 0.5, causal=causal, do=do)
+        b = orc.attention_dropout(q, k, v, 0.5, 0.0, 77, causal=causal, do=do)
+        for x, y, n in zip(a, b, ("O", "LSE", "dQ", "dK", "dV")):
+            _close(y, x, 0.0, f"p=0 {n}")
+
+
+def pin_dropout_torch_autograd(orc):
+    """With the mask drawn from the oracle's own rule, forward and gradients
+    equal torch's CPU fp64 autograd of O = (softmax(S) o Z / (1 - p)) V
+    (dense, causal, block-masked); LSE is that of S without dropout."""
+    B, H, N, d, blk = 1, 2, 12, 5, 4
+    p, seed = 0.3, 0x1234567890ABCDEF
+    q = _rand((B, H, N, d), RNG_SEED + 104)
+    k = _rand((B, H, N, d), RNG_SEED + 105)
+    v = _rand((B, H, N, d), RNG_SEED + 106)
+    do = _rand((B, H, N, d), RNG_SEED + 107)
+    Z = torch.from_numpy(_drop_mask(orc, B * H, N, p, seed).reshape(B, H, N, N))
+    mask = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], np.uint8)
+    for causal, bm in ((False, None), (True, None), (False, mask)):
+        O, LSE, dQ, dK, dV = orc.attention_dropout(q, k, v, 0.6, p, seed, causal=causal,
+                                                   blockmask=bm, blk=blk, do=do)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        A = torch.from_numpy(_allowed_matrix(N, causal, bm, blk))
+        S = (0.6 * tq @ tk.transpose(-1, -2)).masked_fill(~A, float("-inf"))
+        P = torch.softmax(S, dim=-1)
+        ref = (P * Z / (1 - p)) @ tv
+        ref.backward(torch.from_numpy(do))
+        _close(O, ref.detach().numpy(), 1e-13, "dropout O")
+        _close(dQ, tq.grad.numpy(), 1e-12, "dropout dQ")
+        _close(dK, tk.grad.numpy(), 1e-12, "dropout dK")
+        _close(dV, tv.grad.numpy(), 1e-12, "dropout dV")
+        _close(LSE, torch.logsumexp(S, dim=-1).detach().numpy(), 1e-12, "dropout LSE")
+
+
+def pin_dropout_mask_rule(orc):
+    """The keep bit follows the documented rule (a convention of this library,
+    stated in include/fa.h): element (i, j) of head bh is dropped iff word
+    j % 4 of Philox4x32-10(counter (j // 4, i, bh, 0), key (seed low 32 bits,
+    seed high 32 bits)) is below floor(p * 2^32). Checked with the generator
+    pinned by its known answers above."""
+    seed = 0x0123456789ABCDEF
+    for p in (0.2, 0.75):
+        t = math.floor(p * 2 ** 32)
+        for bh, i, j in ((0, 0, 0), (1, 2, 3), (3, 7, 13), (2, 30, 4), (5, 1, 63)):
+            w = orc.philox4x32_10([j // 4, i, bh, 0], [seed & 0xFFFFFFFF, seed >> 32])[j % 4]
+            assert orc.dropout_keep(bh, i, j, p, seed) == int(w >= t), (bh, i, j, p)
+
+
+def pin_dropout_keep_rate(orc):
+    """The kept fraction is 1 - p within 5 binomial standard deviations, for
+    several p, and different seeds give different masks."""
+    n = 64
+    for p in (0.1, 0.5, 0.9):
+        Z = _drop_mask(orc, 2, n, p, 99)
+        m = Z.size
+        sd = math.sqrt(m * p * (1 - p))
+        assert abs(Z.sum() - m * (1 - p)) <= 5 * sd, f"keep rate {Z.mean()} for p={p}"
+    Z1 = _drop_mask(orc, 1, 16, 0.5, 1)
+    Z2 = _drop_mask(orc, 1, 16, 0.5, 2)
+    assert not np.array_equal(Z1, Z2), "seed has no effect"
+
+
 ALL_PINS = [
     pin_identical_keys_uniform,
     pin_zero_query,
@@ -459,4 +554,9 @@ ALL_PINS = [
     pin_kv_identical_keys,
     pin_kv_square_and_suffix,
     pin_kv_split_merge,
+    pin_philox_known_answers,
+    pin_dropout_zero_is_plain,
+    pin_dropout_torch_autograd,
+    pin_dropout_mask_rule,
+    pin_dropout_keep_rate,
 ]

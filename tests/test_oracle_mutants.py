@@ -42,6 +42,19 @@ MUTANTS = [
     ("kv_qk_index", "dot += q[c] * k[j * d + c];", "dot += q[c] * k[c];"),
     ("kv_pv_operand", "orow[c] += p * v[j * d + c];", "orow[c] += p * v[c];"),
     ("kv_no_scale", "srow[j] = scale * dot;", "srow[j] = dot;"),
+    ("philox_multiplier", "0xD2511F53u", "0xD2511F55u"),
+    ("philox_weyl", "k0 += 0x9E3779B9u;", "k0 += 0x9E3779BBu;"),
+    ("drop_counter_swap",
+     "const unsigned int ctr[4] = {(unsigned int)(j / 4), (unsigned int)i, (unsigned int)bh, 0u};",
+     "const unsigned int ctr[4] = {(unsigned int)i, (unsigned int)(j / 4), (unsigned int)bh, 0u};"),
+    ("drop_keep_flipped", "return w[j % 4] >= drop_threshold(p_drop);",
+     "return w[j % 4] < drop_threshold(p_drop);"),
+    ("drop_O_no_rescale", "const double pt = P[i * N + j] * Z[i * N + j] * inv_keep;",
+     "const double pt = P[i * N + j] * Z[i * N + j];"),
+    ("drop_dV_no_mask", "const double pt = inv_keep * Z[i * N + j] * P[i * N + j];",
+     "const double pt = inv_keep * P[i * N + j];"),
+    ("drop_dS_no_mask", "g = pij * (Z[i * N + j] * dp * inv_keep - D[i]);",
+     "g = pij * (dp * inv_keep - D[i]);"),
     ("dV_transposed", "double pij = P[i * N + j];\n                if (s != 0.0)",
      "double pij = P[j * N + i];\n                if (s != 0.0)"),
 ]
