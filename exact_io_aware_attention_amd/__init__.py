@@ -11,6 +11,10 @@ Functions carry the C names:
            blockmask=None, workspace=None, stream=None)
     fa_fwd_f32(...), fa_bwd_f32(...)  -- the fp32 debug path, same arguments
     fa_bwd_workspace_bytes(B, H, N, d)
+    fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=False, blockmask=None,
+                   stream=None)
+    fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=False,
+                   blockmask=None, workspace=None, stream=None)
     fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None)
     fa_decode_workspace_bytes(B, H, Nq, Nk, d)
 Tensors are contiguous CUDA (HIP) tensors of shape [B, H, N, d]: bfloat16 for
@@ -64,6 +68,12 @@ _lib.fa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _
                              _sz, _vp]
 _lib.fa_bwd_workspace_bytes.restype = _sz
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i]
+_lib.fa_fwd_dropout.restype = _i
+_lib.fa_fwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _f,
+                                ctypes.c_ulonglong, _vp]
+_lib.fa_bwd_dropout.restype = _i
+_lib.fa_bwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                                _i, _vp, _f, ctypes.c_ulonglong, _vp, _sz, _vp]
 _lib.fa_decode.restype = _i
 _lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.fa_decode_workspace_bytes.restype = _sz
@@ -77,7 +87,8 @@ _lib.fa_version.argtypes = []
 
 # Symbols declared in include/fa.h (checked by the ABI test).
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_f32",
-            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
+            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout",
+            "fa_decode", "fa_decode_workspace_bytes",
             "fa_status_str", "fa_last_hip_error", "fa_version")
 
 
@@ -267,3 +278,33 @@ def fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None)
     _check(_lib.fa_decode(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d,
                           float(scale), int(bool(causal)), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+
+
+def fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=False, blockmask=None,
+                   stream=None):
+    """Forward with dropout on P, bf16: writes O and LSE in place."""
+    import torch
+    shape = _shape(Q)
+    _require((Q, K, V, O), torch.bfloat16, shape)
+    _require_lse(LSE, shape)
+    _require_mask(blockmask, shape[2])
+    B, H, N, d = shape
+    _check(_lib.fa_fwd_dropout(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, N, d,
+                               float(scale), int(bool(causal)), _ptr(blockmask), float(p_drop),
+                               int(seed), _stream_ptr(stream)))
+
+
+def fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=False,
+                   blockmask=None, workspace=None, stream=None):
+    """Backward of fa_fwd_dropout, bf16: writes dQ, dK, dV in place."""
+    import torch
+    shape = _shape(Q)
+    _require((dO, Q, K, V, O, dQ, dK, dV), torch.bfloat16, shape)
+    _require_lse(LSE, shape)
+    _require_mask(blockmask, shape[2])
+    ws = _workspace(shape, workspace, Q.device)
+    B, H, N, d = shape
+    _check(_lib.fa_bwd_dropout(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(dQ),
+                               _ptr(dK), _ptr(dV), B, H, N, d, float(scale), int(bool(causal)),
+                               _ptr(blockmask), float(p_drop), int(seed), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream_ptr(stream)))

@@ -79,13 +79,33 @@ fa::Problem make_problem(int B, int H, int N, int d, float scale, int causal,
     return p;
 }
 
+// Dropout probability: finite, in [0, 1). Sets the problem's dropout fields
+// (threshold floor(p 2^32), seed, 1 / (1 - p)).
+fa_status set_dropout(fa::Problem &p, float p_drop, unsigned long long seed)
+{
+    if (!std::isfinite(p_drop) || p_drop < 0.f || p_drop >= 1.f)
+        return FA_ERR_SCALE;
+    if (p_drop > 0.f) {
+        const double t = std::floor((double)p_drop * 4294967296.0);
+        p.dropout = 1;
+        p.drop_threshold = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+        p.drop_seed = seed;
+        p.drop_inv_keep = (float)(1.0 / (1.0 - (double)p_drop));
+    }
+    return FA_OK;
+}
+
 template <typename T>
 fa_status fwd_common(const T *Q, const T *K, const T *V, T *O, float *LSE, int B, int H, int N,
                      int d, float scale, int causal, const uint8_t *blockmask, void *stream,
-                     bool f32)
+                     bool f32, float p_drop = 0.f, unsigned long long seed = 0)
 {
     bool empty = false;
     fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    st = set_dropout(p, p_drop, seed);
     if (st != FA_OK)
         return st;
     if (empty)
@@ -93,7 +113,6 @@ fa_status fwd_common(const T *Q, const T *K, const T *V, T *O, float *LSE, int B
     st = check_ptrs({Q, K, V, O, LSE});
     if (st != FA_OK)
         return st;
-    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
     if (f32)
         return hip_status(fa::launch_fwd_f32(p, reinterpret_cast<const float *>(Q),
                                              reinterpret_cast<const float *>(K),
@@ -111,10 +130,15 @@ template <typename T>
 fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O,
                      const float *LSE, T *dQ, T *dK, T *dV, int B, int H, int N, int d,
                      float scale, int causal, const uint8_t *blockmask, void *workspace,
-                     size_t workspace_bytes, void *stream, bool f32)
+                     size_t workspace_bytes, void *stream, bool f32, float p_drop = 0.f,
+                     unsigned long long seed = 0)
 {
     bool empty = false;
     fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    st = set_dropout(p, p_drop, seed);
     if (st != FA_OK)
         return st;
     if (empty)
@@ -125,7 +149,6 @@ fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O
     st = check_workspace(B, H, N, d, workspace, workspace_bytes);
     if (st != FA_OK)
         return st;
-    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
     if (f32)
         return hip_status(fa::launch_bwd_f32(
             p, reinterpret_cast<const float *>(dO), reinterpret_cast<const float *>(Q),
@@ -240,6 +263,29 @@ fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), workspace));
 }
 
+fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                         int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                         float p_drop, unsigned long long seed, void *stream)
+{
+    return fwd_common<uint16_t>(static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
+                                static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), LSE,
+                                B, H, N, d, scale, causal, blockmask, stream, false, p_drop, seed);
+}
+
+fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const void *V,
+                         const void *O, const float *LSE, void *dQ, void *dK, void *dV, int B,
+                         int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                         float p_drop, unsigned long long seed, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    return bwd_common<uint16_t>(
+        static_cast<const uint16_t *>(dO), static_cast<const uint16_t *>(Q),
+        static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
+        static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
+        static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
+        blockmask, workspace, workspace_bytes, stream, false, p_drop, seed);
+}
+
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d)
 {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk < 0 || d <= 0)
@@ -311,7 +357,7 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_SHAPE: return "invalid shape";
     case FA_ERR_HEADDIM: return "unsupported head dimension (d must be a multiple of 8 in [8, 128])";
     case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1";
+    case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1, dropout probability in [0, 1)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP error";
     }

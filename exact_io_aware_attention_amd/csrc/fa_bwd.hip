@@ -221,6 +221,7 @@ struct DqParams {
     const uint8_t *mask;
     int N, dh, nqb, nkt, nmb, items, per_xcd;
     float c, scale;
+    DropParams drop;  // used by the DROP instances
 };
 
 // Rows per wave and per workgroup of both main kernels: 4 waves (one per
@@ -246,7 +247,7 @@ struct BwdShape {
 // spread over its MFMA slots, then C(i-1) (C has half as many MFMAs as A,
 // too few to hide B). C reads the previous step's K tile, so K tiles are
 // triple-buffered.
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
 {
     static_assert(BwdShape::W * 64 == 256, "launch bounds");
@@ -329,6 +330,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     for (int r = 0; r < 16; ++r)
         s_prev[r] = -INFINITY;
     int key0_prev = 0;
+    uint32_t z_prev = 0;  // dropout keep bits of the previous step's elements
     // Operand addresses of the current tile's slot and of the previous
     // step's slot (C reads). The previous step of step kh is step 1 - kh
     // (before the first step its weights are zero and it reads valid rows
@@ -343,9 +345,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         return sa.tr_at(K_OFF, 32 * kh + 16 * hh, db);
     };
 
-    // Softmax element r of the previous step: dS^T = P^T o (dP^T - D).
-    // MASKED applies the element mask: key past the end or above the query
-    // (causal). Packs each 8 finished elements into an MFMA operand.
+    // Softmax element r of the previous step: dS^T = P^T o (dP^T - D), with
+    // dropout P^T o (Z o dP^T / (1 - p) - D). MASKED applies the element
+    // mask: key past the end or above the query (causal). Packs each 8
+    // finished elements into an MFMA operand.
     bf16x8 sb[2];
     float dsm[16];
     auto softmax_elem = [&](auto mtag, int r) __attribute__((always_inline)) {
@@ -356,7 +359,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
             if (key >= N || (CAUSAL && key > row))
                 pe = 0.f;
         }
-        dsm[r] = pe * (dp_prev[r] + nDi);
+        if constexpr (DROP)
+            dsm[r] = pe * ((((z_prev >> r) & 1u) ? dp_prev[r] * p.drop.inv_keep : 0.f) + nDi);
+        else
+            dsm[r] = pe * (dp_prev[r] + nDi);
         if (r % 8 == 7) {
             bf16x8 sk;
 #pragma unroll
@@ -379,6 +385,15 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     auto step = [&](auto mtag, int kh, int key0, const SlotAddr<D> &ps) __attribute__((always_inline)) {
         constexpr int EPS = 16 / (2 * KK);  // B elements per A slot
         static_assert(EPS * 2 * KK == 16, "elements per slot");
+        // dropout keep bits of this step's elements (keys key0 + 8 g + 4 hi
+        // + 0..3, query `row`), used by B of the next step
+        uint32_t z_cur = 0;
+        if constexpr (DROP) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                z_cur |= drop_keep4(p.drop, (uint32_t)(key0 + 8 * g + 4 * hi), (uint32_t)row,
+                                    (uint32_t)bh) << (4 * g);
+        }
         bf16x8 ka[KK], va[KK];
 #pragma unroll
         for (int kk = 0; kk < PA; ++kk) {
@@ -421,6 +436,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         s_prev = s;
         dp_prev = dp;
         key0_prev = key0;
+        z_prev = z_cur;
     };
 
     int t = next_tile(-1);
@@ -500,6 +516,7 @@ struct DkvParams {
     const uint8_t *mask;
     int N, dh, nkb, nqt, nmb, items, per_xcd;
     float c, scale;
+    DropParams drop;  // used by the DROP instances
 };
 
 // One workgroup owns 128 keys of one (b, h), K and V rows held as MFMA B
@@ -515,7 +532,7 @@ struct DkvParams {
 // then C(i-1) with B(i) spread over its MFMA slots, every LDS operand read
 // issued a few MFMAs ahead of its use. Scheduling fences keep the compiler
 // from regrouping the slots (it cannot see the asm MFMAs' latencies).
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
 {
     static_assert(BwdShape::W * 64 == 256, "launch bounds");
@@ -664,6 +681,22 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
                 lq[4 * j + 2] = lv.z; lq[4 * j + 3] = lv.w;
             }
         }
+        // dropout keep bits of this step's elements (key of this lane,
+        // query qrow0 + 8 (r / 4) + 4 hi + r % 4 for bit r): the key's word
+        // of each query's draw
+        uint32_t zb[NB];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int kb = 0; kb < NB; ++kb) {
+                const uint32_t key = (uint32_t)(wk0 + 32 * kb + l32);
+                zb[kb] = 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t q = (uint32_t)(qrow0 + 8 * (r / 4) + 4 * hi + (r % 4));
+                    zb[kb] |= ((drop_keep4(p.drop, key & ~3u, q, (uint32_t)bh) >> (key & 3u)) & 1u) << r;
+                }
+            }
+        }
         bf16x8 qa[KK], ga[KK];
 #pragma unroll
         for (int kk = 0; kk < PA; ++kk) {
@@ -702,7 +735,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         // exponential, product and packing), so no slot waits on a result
         // it produced itself.
         bf16x8 pb2[NB][2], sb2[NB][2];
-        float tx[NB][16], pm[NB][16], dsm[NB][16];
+        float tx[NB][16], pm[NB][16], dsm[NB][16], pt[NB][16];
         auto stage_f = [&](int e) __attribute__((always_inline)) {
             const int kb = e / 16, r = e % 16;
             tx[kb][r] = fmaf(s[kb][r], c, -lq[r]);
@@ -722,13 +755,24 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
         };
         auto stage_m = [&](int e) __attribute__((always_inline)) {
             const int kb = e / 16, r = e % 16;
-            dsm[kb][r] = pm[kb][r] * dp[kb][r];
+            // dp holds dP - D (its accumulator started from -D); with
+            // dropout dS = P o (Z o dP / (1 - p) - D) and dV takes
+            // P o Z / (1 - p)
+            if constexpr (DROP) {
+                const bool z = (zb[kb] >> r) & 1u;
+                const float ik = p.drop.inv_keep;
+                dsm[kb][r] = pm[kb][r] * (z ? (dp[kb][r] - nd[r]) * ik + nd[r] : nd[r]);
+                pt[kb][r] = z ? pm[kb][r] * ik : 0.f;
+            } else {
+                dsm[kb][r] = pm[kb][r] * dp[kb][r];
+                pt[kb][r] = pm[kb][r];
+            }
             if (r % 8 == 7) {
                 const int h = r / 8;
                 bf16x8 pk, sk;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    pk[i] = (__bf16)pm[kb][8 * h + i];
+                    pk[i] = (__bf16)pt[kb][8 * h + i];
                     sk[i] = (__bf16)dsm[kb][8 * h + i];
                 }
                 pb2[kb][h] = pk;
@@ -904,6 +948,16 @@ hipError_t prep_d(const Problem &pr, const BwdPtrs &b)
     return hipGetLastError();
 }
 
+DropParams drop_params(const Problem &pr)
+{
+    DropParams d;
+    d.threshold = pr.drop_threshold;
+    d.seed_lo = (uint32_t)pr.drop_seed;
+    d.seed_hi = (uint32_t)(pr.drop_seed >> 32);
+    d.inv_keep = pr.drop_inv_keep;
+    return d;
+}
+
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
 {
@@ -919,8 +973,13 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
     qp.per_xcd = (qp.items + kXcds - 1) / kXcds;
     qp.c = pr.scale * kLog2e;
     qp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3(qp.per_xcd * kXcds), dim3(256), 0,
-                       pr.stream, qp);
+    qp.drop = drop_params(pr);
+    if (pr.dropout)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE, true>), dim3(qp.per_xcd * kXcds),
+                           dim3(256), 0, pr.stream, qp);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE, false>), dim3(qp.per_xcd * kXcds),
+                           dim3(256), 0, pr.stream, qp);
     return hipGetLastError();
 }
 
@@ -939,8 +998,13 @@ hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
     kp.per_xcd = (kp.items + kXcds - 1) / kXcds;
     kp.c = pr.scale * kLog2e;
     kp.scale = pr.scale;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(kp.per_xcd * kXcds), dim3(256), 0,
-                       pr.stream, kp);
+    kp.drop = drop_params(pr);
+    if (pr.dropout)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE, true>), dim3(kp.per_xcd * kXcds),
+                           dim3(256), 0, pr.stream, kp);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE, false>), dim3(kp.per_xcd * kXcds),
+                           dim3(256), 0, pr.stream, kp);
     return hipGetLastError();
 }
 

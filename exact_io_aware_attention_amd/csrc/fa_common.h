@@ -187,6 +187,50 @@ __device__ __forceinline__ void lds_reads_wait_all()
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products of
+// counter words 0 and 2 with 0xD2511F53 and 0xCD9E8D57, the new counter being
+// (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)), the key
+// advanced by (0x9E3779B9, 0xBB67AE85) between rounds.
+struct Philox4 {
+    uint32_t w[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    return Philox4{{c0, c1, c2, c3}};
+}
+
+// Dropout parameters: element (i, j) of head bh is kept iff word j % 4 of
+// Philox4x32-10(counter (j / 4, i, bh, 0), key (seed_lo, seed_hi)) is at
+// least `threshold` (floor(p 2^32)); kept weights are scaled by inv_keep.
+struct DropParams {
+    uint32_t threshold;
+    uint32_t seed_lo, seed_hi;
+    float inv_keep;
+};
+// Keep bits of the 4 consecutive keys j0..j0+3 (j0 % 4 == 0) of query i.
+__device__ __forceinline__ uint32_t drop_keep4(const DropParams &dp, uint32_t j0, uint32_t i,
+                                               uint32_t bh)
+{
+    const Philox4 r = philox4x32_10(j0 / 4, i, bh, 0u, dp.seed_lo, dp.seed_hi);
+    return (uint32_t)(r.w[0] >= dp.threshold) | ((uint32_t)(r.w[1] >= dp.threshold) << 1) |
+           ((uint32_t)(r.w[2] >= dp.threshold) << 2) | ((uint32_t)(r.w[3] >= dp.threshold) << 3);
+}
+
 // A buffer offset past the end of every resource used here (tensor slabs are
 // below 2^31 bytes): a load from it returns zeros. Used for the columns of a
 // padded head dimension.

@@ -78,11 +78,12 @@ struct FwdParams {
     int items;    // B * H * nqb
     int per_xcd;  // work items per XCD
     float c;      // scale * log2(e)
+    DropParams drop;  // used by the DROP instances
 };
 
 constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated without rescale
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
 {
     constexpr int W = 8;            // waves
@@ -383,13 +384,28 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                 for (int db = 0; db < DB; ++db)
                     vf[hh][db] = lds_tr_pair_at(vaddr[db][0] + vofs, vaddr[db][1] + vofs);
             }
+            // dropout: keep bits of this block's 16 elements (keys
+            // kb + 8 g + 4 hi + 0..3 for g = 0..3, query `row`); the row sum
+            // takes the weights before dropout, P V the kept ones scaled
+            uint32_t zb = 0;
+            if constexpr (DROP) {
+                const uint32_t kb = (uint32_t)(t * BC + 32 * h + 4 * hi);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    zb |= drop_keep4(p.drop, kb + 8 * g, (uint32_t)row, (uint32_t)bh) << (4 * g);
+            }
+            auto dropped = [&](float e, int r) __attribute__((always_inline)) -> float {
+                if constexpr (DROP)
+                    return ((zb >> r) & 1u) ? e * p.drop.inv_keep : 0.f;
+                return e;
+            };
             float ls0, ls1;
 #pragma unroll
             for (int r = 0; r < 8; r += 2) {
                 const float e0 = exp2_fast(fmaf(s_cur[r], c, nmref));
                 const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, nmref));
-                s_cur[r] = e0;
-                s_cur[r + 1] = e1;
+                s_cur[r] = dropped(e0, r);
+                s_cur[r + 1] = dropped(e1, r + 1);
                 ls0 = r == 0 ? e0 : ls0 + e0;
                 ls1 = r == 0 ? e1 : ls1 + e1;
             }
@@ -402,8 +418,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             for (int r = 8; r < 16; r += 2) {
                 const float e0 = exp2_fast(fmaf(s_cur[r], c, nmref));
                 const float e1 = exp2_fast(fmaf(s_cur[r + 1], c, nmref));
-                s_cur[r] = e0;
-                s_cur[r + 1] = e1;
+                s_cur[r] = dropped(e0, r);
+                s_cur[r + 1] = dropped(e1, r + 1);
                 ls0 += e0;
                 ls1 += e1;
             }
@@ -505,7 +521,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
 {
     FwdParams fp = fp0;
@@ -514,17 +530,25 @@ static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
     fp.items = pr.B * pr.H * fp.nqb;
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3(grid), dim3(512), 0, pr.stream, fp);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(512), 0, pr.stream, fp);
     return hipGetLastError();
+}
+
+template <int D, bool DROP>
+static hipError_t launch_fwd_dd(const Problem &pr, const FwdParams &fp)
+{
+    const bool sparse = pr.mask != nullptr;
+    if (pr.causal)
+        return sparse ? launch_fwd_t<D, true, true, DROP>(pr, fp)
+                      : launch_fwd_t<D, true, false, DROP>(pr, fp);
+    return sparse ? launch_fwd_t<D, false, true, DROP>(pr, fp)
+                  : launch_fwd_t<D, false, false, DROP>(pr, fp);
 }
 
 template <int D>
 static hipError_t launch_fwd_d(const Problem &pr, const FwdParams &fp)
 {
-    const bool sparse = pr.mask != nullptr;
-    if (pr.causal)
-        return sparse ? launch_fwd_t<D, true, true>(pr, fp) : launch_fwd_t<D, true, false>(pr, fp);
-    return sparse ? launch_fwd_t<D, false, true>(pr, fp) : launch_fwd_t<D, false, false>(pr, fp);
+    return pr.dropout ? launch_fwd_dd<D, true>(pr, fp) : launch_fwd_dd<D, false>(pr, fp);
 }
 
 hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t *K,
@@ -542,6 +566,10 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.nkt = (pr.N + 63) / 64;
     fp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     fp.c = pr.scale * kLog2e;
+    fp.drop.threshold = pr.drop_threshold;
+    fp.drop.seed_lo = (uint32_t)pr.drop_seed;
+    fp.drop.seed_hi = (uint32_t)(pr.drop_seed >> 32);
+    fp.drop.inv_keep = pr.drop_inv_keep;
     // head dims up to 64 run in the 64-wide kernel, the others (up to 128) in
     // the 128-wide one, zero-padded
     if (pr.d <= 64)

@@ -15,6 +15,12 @@ struct Problem {
     int causal;
     const uint8_t *mask;  // device pointer or nullptr
     hipStream_t stream;
+    // dropout on P (dropout = 0: none): keep iff the element's Philox word
+    // >= drop_threshold; kept weights times drop_inv_keep
+    int dropout = 0;
+    uint32_t drop_threshold = 0;
+    uint64_t drop_seed = 0;
+    float drop_inv_keep = 1.f;
 };
 
 // Scratch layout of the backward (offsets in bytes from the workspace base).

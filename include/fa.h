@@ -68,7 +68,8 @@ typedef enum {
     FA_ERR_SHAPE = 2,     /* B, H or N negative, or sizes overflow */
     FA_ERR_HEADDIM = 3,   /* d not supported */
     FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
-    FA_ERR_SCALE = 5,     /* scale not finite or not > 0, or causal not 0/1 */
+    FA_ERR_SCALE = 5,     /* scale not finite or not > 0, causal not 0/1, or a
+                             dropout probability outside [0, 1) */
     FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_bwd_workspace_bytes */
     FA_ERR_HIP = 7        /* a HIP call failed; see fa_last_hip_error() */
 } fa_status;
@@ -115,6 +116,30 @@ fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *
                       void *dK, void *dV, int B, int H, int N, int d, float scale, int causal,
                       const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* Forward with dropout on P (lukebest.github.io FlashAttention, "Kernel
+ * fusion", lists dropout among the fused steps; the drawing rule is this
+ * library's): element (i, j) of head bh = b*H + h is dropped iff word j % 4 of
+ * Philox4x32-10(counter (j / 4, i, bh, 0), key (low 32 bits of seed, high 32
+ * bits of seed)) is below floor(p_drop * 2^32) (Philox4x32-10: Salmon et al.,
+ * SC 2011). Then O_i = sum_j P_ij Z_ij / (1 - p_drop) V_j with P the softmax
+ * of the masked scores; LSE is that of P (no dropout), as fa_bwd_dropout
+ * needs. p_drop in [0, 1) (0: same as fa_fwd); the same (p_drop, seed) must
+ * be passed to fa_bwd_dropout. Other arguments and rules as fa_fwd. */
+fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                         int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                         float p_drop, unsigned long long seed, void *stream);
+
+/* Backward of fa_fwd_dropout (O is its output): dV = P~^T dO with
+ * P~ = P o Z / (1 - p), dP = dO V^T, D_i = rowsum(dO o O),
+ * dS = P o (Z o dP / (1 - p) - D), dQ = scale dS K, dK = scale dS^T Q; the
+ * mask Z is drawn again from (p_drop, seed) by the same rule. Other arguments
+ * and rules as fa_bwd (same workspace size). */
+fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const void *V,
+                         const void *O, const float *LSE, void *dQ, void *dK, void *dV, int B,
+                         int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                         float p_drop, unsigned long long seed, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /* Bytes of device scratch fa_decode needs for this shape (0 for an empty
  * problem). It depends on the shape only. */

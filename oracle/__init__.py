@@ -72,7 +72,7 @@ class Oracle:
         lib.oracle_attention_dropout.restype = ctypes.c_int
         lib.oracle_attention_dropout.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                                  L, L, L, L, ctypes.c_double, ctypes.c_int, up,
-                                                 L, ctypes.c_double, ctypes.c_ulonglong]
+                                                 L, ctypes.c_double, ctypes.c_ulonglong, L]
         lib.oracle_attention_kv.restype = ctypes.c_int
         lib.oracle_attention_kv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L,
                                             ctypes.c_double, ctypes.c_int]
@@ -143,8 +143,9 @@ class Oracle:
         return int(self.lib.oracle_dropout_keep(bh, i, j, float(p_drop), int(seed)))
 
     def attention_dropout(self, q, k, v, scale, p_drop, seed, causal=False, blockmask=None,
-                          blk=MASK_BLOCK, do=None):
-        """attention() with dropout on P: returns (O, LSE) or (O, LSE, dQ, dK, dV)."""
+                          blk=MASK_BLOCK, do=None, bh_offset=0):
+        """attention() with dropout on P: returns (O, LSE) or (O, LSE, dQ, dK, dV).
+        Head bh of the arrays draws its mask as head bh + bh_offset."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, H, N, d = _shape(q, k, v)
         m = _mask(blockmask, N, blk)
@@ -159,7 +160,7 @@ class Oracle:
                                                _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
                                                B, H, N, d, float(scale), int(bool(causal)),
                                                _ptr(m, ctypes.c_ubyte), blk, float(p_drop),
-                                               int(seed))
+                                               int(seed), int(bh_offset))
         if rc != 0:
             raise RuntimeError(f"oracle_attention_dropout failed with code {rc}")
         if do is None:

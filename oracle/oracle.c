@@ -294,7 +294,8 @@ int oracle_dropout_keep(long bh, long i, long j, double p_drop, unsigned long lo
 
 /*
  * Attention with dropout on P, forward and (dO != NULL) backward, written out
- * with N x N intermediates like oracle_attention:
+ * with N x N intermediates like oracle_attention (head bh of the arrays draws
+ * its mask as head bh + bh_offset, so a slice of heads can be checked alone):
  *   P = softmax(S) (S as above, masks included), Z_ij in {0, 1} the mask,
  *   P~ = P o Z / (1 - p),  O = P~ V,  LSE from P's statistics (no dropout);
  *   dV = P~^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
@@ -307,7 +308,7 @@ int oracle_attention_dropout(const double *Q, const double *K, const double *V,
                              double *dQ, double *dK, double *dV,
                              long B, long H, long N, long d, double scale, int causal,
                              const unsigned char *blockmask, long blk,
-                             double p_drop, unsigned long long seed)
+                             double p_drop, unsigned long long seed, long bh_offset)
 {
     int rc = check_args(B, H, N, d, blk);
     if (rc != ORACLE_OK)
@@ -337,7 +338,7 @@ int oracle_attention_dropout(const double *Q, const double *K, const double *V,
             forward_row(q, k, v, N, d, scale, causal, blockmask, blk, nb, i,
                         P + i * N, o + i * d, lse + i);
             for (long j = 0; j < N; ++j)
-                Z[i * N + j] = oracle_dropout_keep(bh, i, j, p_drop, seed) ? 1.0 : 0.0;
+                Z[i * N + j] = oracle_dropout_keep(bh + bh_offset, i, j, p_drop, seed) ? 1.0 : 0.0;
             for (long c = 0; c < d; ++c)
                 o[i * d + c] = 0.0;
             for (long j = 0; j < N; ++j) {

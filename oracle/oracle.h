@@ -49,7 +49,7 @@ int oracle_attention_dropout(const double *Q, const double *K, const double *V,
                              double *dQ, double *dK, double *dV,
                              long B, long H, long N, long d, double scale, int causal,
                              const unsigned char *blockmask, long blk,
-                             double p_drop, unsigned long long seed);
+                             double p_drop, unsigned long long seed, long bh_offset);
 
 /* Number of OpenMP threads the reference runs with. */
 int oracle_num_threads(void);

@@ -158,3 +158,32 @@ def test_decode_workspace_bytes():
     a = fa.fa_decode_workspace_bytes(1, 8, 1, 4096, 128)
     b = fa.fa_decode_workspace_bytes(1, 8, 1, 65536, 128)
     assert 0 < a < b
+
+
+def test_dropout_validation():
+    lib = fa.lib()
+
+    def fwd(**kw):
+        a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+                 mask=None, p=0.1, seed=1)
+        a.update(kw)
+        return lib.fa_fwd_dropout(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"],
+                                  a["N"], a["d"], a["scale"], a["causal"], a["mask"], a["p"],
+                                  a["seed"], None)
+
+    def bwd(**kw):
+        a = dict(p=0.1, seed=1, ws=P, wsb=1 << 30, N=128, d=64, Q=P)
+        a.update(kw)
+        return lib.fa_bwd_dropout(P, a["Q"], P, P, P, P, P, P, P, 1, 1, a["N"], a["d"], 0.125, 0,
+                                  None, a["p"], a["seed"], a["ws"], a["wsb"], None)
+
+    for f in (fwd, bwd):
+        assert f(p=1.0) == 5
+        assert f(p=-0.25) == 5
+        assert f(p=float("nan")) == 5
+        assert f(p=float("inf")) == 5
+        assert f(Q=None) == 1
+        assert f(d=100) == 3
+        assert f(N=0, p=0.5) == 0        # empty: nothing done
+        assert f(N=0, p=2.0) == 5        # but the probability is still checked
+    assert bwd(ws=None) == 6

@@ -249,3 +249,90 @@ def test_decode_against_oracle(B, H, Nq, Nk, d, causal):
     Or, Lr = oracle.attention_kv(q, k, v, scale, causal=causal)
     gu.check_outputs("bf16", {"O": gu.host(O), "LSE": gu.host(LSE)}, {"O": Or, "LSE": Lr},
                      fields=("O", "LSE"))
+
+
+DROPOUT = [
+    # (B, H, N, d, causal, sparse, p_drop, seed)
+    (1, 2, 200, 64, True, False, 0.1, 7),
+    (1, 1, 333, 128, False, False, 0.5, 0x1234567890AB),
+    (2, 1, 129, 96, True, False, 0.3, 42),
+    (1, 2, 300, 128, True, True, 0.2, 99),
+    (1, 1, 1031, 128, True, False, 0.15, 2 ** 63 + 5),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,sparse,p_drop,seed", DROPOUT)
+def test_dropout_against_oracle(B, H, N, d, causal, sparse, p_drop, seed):
+    import exact_io_aware_attention_amd as fa
+    q, k, v, do = syn.random_inputs(B, H, N, d, 9000 + N + d, dtype="bf16")
+    nb = (N + 127) // 128
+    mask = None
+    if sparse:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        mask = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(mask, 1)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"dropout p={p_drop} seed={seed} B={B} H={H} N={N} d={d} causal={causal} "
+          f"sparse={sparse}", flush=True)
+    Q, K, V, dO = (gu.dev(x, torch.bfloat16) for x in (q, k, v, do))
+    M = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).to("cuda")
+    O = torch.empty_like(Q)
+    LSE = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=causal, blockmask=M)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    fa.fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=causal,
+                      blockmask=M)
+    torch.cuda.synchronize()
+    ref = oracle.attention_dropout(q, k, v, scale, p_drop, seed, causal=causal, blockmask=mask,
+                                   do=do)
+    gu.check_outputs("bf16", _got(O, LSE, dQ, dK, dV),
+                     dict(zip(("O", "LSE", "dQ", "dK", "dV"), ref)))
+
+
+def test_dropout_zero_matches_plain():
+    """p = 0 through the dropout entry points is the plain path, bit for bit."""
+    import exact_io_aware_attention_amd as fa
+    B, H, N, d = 1, 2, 257, 128
+    q, k, v, do = syn.random_inputs(B, H, N, d, 4321, dtype="bf16")
+    Q, K, V, dO = (gu.dev(x, torch.bfloat16) for x in (q, k, v, do))
+    outs = []
+    for drop in (False, True):
+        O = torch.empty_like(Q)
+        LSE = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+        if drop:
+            fa.fa_fwd_dropout(Q, K, V, O, LSE, 0.09, 0.0, 5, causal=True)
+            fa.fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, 0.09, 0.0, 5, causal=True)
+        else:
+            fa.fa_fwd(Q, K, V, O, LSE, 0.09, causal=True)
+            fa.fa_bwd(dO, Q, K, V, O, LSE, dQ, dK, dV, 0.09, causal=True)
+        torch.cuda.synchronize()
+        outs.append((O, LSE, dQ, dK, dV))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_dropout_full_size_one_head():
+    """Config 3 with dropout p = 0.1 on the GPU at full size; one head checked
+    against the reference."""
+    import exact_io_aware_attention_amd as fa
+    cfg = syn.CONFIGS[3]
+    q, k, v, do, _ = syn.config_inputs(cfg)
+    p_drop, seed = 0.1, 20240601
+    print("config 3 with dropout, head (1, 7)", flush=True)
+    Q, K, V, dO = (gu.dev(x, torch.bfloat16) for x in (q, k, v, do))
+    O = torch.empty_like(Q)
+    LSE = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_dropout(Q, K, V, O, LSE, cfg.scale, p_drop, seed, causal=cfg.causal)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(Q), torch.empty_like(Q)
+    fa.fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, cfg.scale, p_drop, seed, causal=cfg.causal)
+    torch.cuda.synchronize()
+    b, h = 1, 7
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    # the one-head slice draws its mask as head b*H + h of the full problem
+    ref = oracle.attention_dropout(q[sl], k[sl], v[sl], cfg.scale, p_drop, seed,
+                                   causal=cfg.causal, do=do[sl], bh_offset=b * cfg.H + h)
+    got = {n: gu.host(t[sl]) for n, t in (("O", O), ("LSE", LSE), ("dQ", dQ), ("dK", dK),
+                                          ("dV", dV))}
+    gu.check_outputs("bf16", got, dict(zip(("O", "LSE", "dQ", "dK", "dV"), ref)))
