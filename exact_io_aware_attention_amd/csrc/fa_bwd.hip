@@ -682,19 +682,31 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             }
         }
         // dropout keep bits of this step's elements (key of this lane,
-        // query qrow0 + 8 (r / 4) + 4 hi + r % 4 for bit r): the key's word
-        // of each query's draw
+        // query qrow0 + 8 (r / 4) + 4 hi + r % 4 for bit r). The four lanes
+        // of a quad hold four consecutive keys, which share one draw per
+        // query: lane u of the quad draws for the queries r = 4 a + u
+        // (bits 4 a + w of its mask: key 4 (key / 4) + w), the quad's masks
+        // are broadcast to every lane, and lane v takes bit 4 a + v of lane
+        // b's mask as its bit 4 a + b.
         uint32_t zb[NB];
         if constexpr (DROP) {
+            const uint32_t u = (uint32_t)(l32 & 3);
 #pragma unroll
             for (int kb = 0; kb < NB; ++kb) {
                 const uint32_t key = (uint32_t)(wk0 + 32 * kb + l32);
-                zb[kb] = 0;
+                uint32_t mine = 0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const uint32_t q = (uint32_t)(qrow0 + 8 * (r / 4) + 4 * hi + (r % 4));
-                    zb[kb] |= ((drop_keep4(p.drop, key & ~3u, q, (uint32_t)bh) >> (key & 3u)) & 1u) << r;
+                for (int a = 0; a < 4; ++a) {
+                    const uint32_t q = (uint32_t)(qrow0 + 8 * a + 4 * hi) + u;
+                    mine |= drop_keep4(p.drop, key & ~3u, q, (uint32_t)bh) << (4 * a);
                 }
+                // quad_perm broadcasts of lanes 0..3 of the quad
+                const uint32_t x0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x00, 0xF, 0xF, false);
+                const uint32_t x1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0x55, 0xF, 0xF, false);
+                const uint32_t x2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xAA, 0xF, 0xF, false);
+                const uint32_t x3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xFF, 0xF, 0xF, false);
+                zb[kb] = ((x0 >> u) & 0x1111u) | (((x1 >> u) & 0x1111u) << 1) |
+                         (((x2 >> u) & 0x1111u) << 2) | (((x3 >> u) & 0x1111u) << 3);
             }
         }
         bf16x8 qa[KK], ga[KK];

@@ -195,6 +195,14 @@ __device__ __forceinline__ void lds_reads_wait_all()
 struct Philox4 {
     uint32_t w[4];
 };
+// 32 x 32 -> 64-bit product in one v_mad_u64_u32 (the compiler otherwise
+// spends a v_mul_hi_u32 and a v_mul_lo_u32 on it); m is wave-uniform.
+__device__ __forceinline__ uint64_t mul_wide_u32(uint32_t a, uint32_t m)
+{
+    uint64_t r, carry;
+    asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(r), "=s"(carry) : "v"(a), "s"(m));
+    return r;
+}
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1)
 {
@@ -204,12 +212,12 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        c0 = hi1 ^ c1 ^ k0;
-        c1 = lo1;
-        c2 = hi0 ^ c3 ^ k1;
-        c3 = lo0;
+        const uint64_t p0 = mul_wide_u32(c0, 0xD2511F53u);
+        const uint64_t p1 = mul_wide_u32(c2, 0xCD9E8D57u);
+        c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        c1 = (uint32_t)p1;
+        c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c3 = (uint32_t)p0;
     }
     return Philox4{{c0, c1, c2, c3}};
 }
