@@ -13,8 +13,9 @@ come from HIP events recorded on the stream the kernels run on.
 
 Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
 --cpu-heads H (heads of the CPU fp64 reference timed as the baseline; 0 skips)
---supp-steps S (the same shape without the causal mask) --decode-steps S (the
-split-KV decode path on its own workload, HBM-bound). The supplementary runs
+--supp-steps S (the same shape without the causal mask) --dropout-steps S (the
+same workload with dropout p=0.1) --decode-steps S (the split-KV decode path on
+its own workload, HBM-bound). The supplementary runs
 are reported beside the headline and never enter `value`.
 """
 import argparse
@@ -45,6 +46,8 @@ def parse():
                     help="timed steps of the supplementary non-causal run (0: skip)")
     ap.add_argument("--decode-steps", type=int, default=10,
                     help="timed calls of the supplementary split-KV decode run (0: skip)")
+    ap.add_argument("--dropout-steps", type=int, default=5,
+                    help="timed steps of the supplementary dropout run (0: skip)")
     return ap.parse_args()
 
 
@@ -223,7 +226,8 @@ def main():
     dominant = max(names, key=lambda n: avg[n])
     ach = kernel_flops[dominant] / avg[dominant] / 1e12
     tf = lambda b: "true" if b else "false"  # noqa: E731
-    flags = f"{cfg.d}, {tf(cfg.causal)}, {tf(mask is not None)}"
+    # kernel template arguments: head width, causal, block-sparse, dropout
+    flags = f"{cfg.d}, {tf(cfg.causal)}, {tf(mask is not None)}, false"
     symbols = {"fwd": f"fwd_bf16_kernel<{flags}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
                "bwd_dq": f"bwd_dq_kernel<{flags}>", "bwd_dkdv": f"bwd_dkdv_kernel<{flags}>"}
     tag = f"{cfg.name.replace('-', '_')}_b{cfg.B}h{cfg.H}n{cfg.N}d{cfg.d}"
@@ -267,6 +271,35 @@ def main():
                 "fwd_ms": round(f_s * 1e3, 4), "fwd_tflops": round(2 * fwd_flops / f_s / 1e12, 2),
                 "bwd_ms": round(b_s * 1e3, 4), "bwd_tflops": round(2 * bwd_flops / b_s / 1e12, 2),
                 "steps": args.supp_steps}
+
+    # Supplementary: the same workload with dropout p = 0.1 on P (fa_fwd_dropout
+    # + fa_bwd_dropout); never part of `value`.
+    dropout = None
+    if args.dropout_steps > 0:
+        p_drop, seed = 0.1, 1234
+        def run_drop():
+            fa.fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=causal, blockmask=M)
+            fa.fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed,
+                              causal=causal, blockmask=M, workspace=ws)
+        run_drop()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.dropout_steps)]
+        for e in ev:
+            e[0].record()
+            fa.fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=causal, blockmask=M)
+            e[1].record()
+            fa.fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed,
+                              causal=causal, blockmask=M, workspace=ws)
+            e[2].record()
+        torch.cuda.synchronize()
+        f_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
+        b_s = statistics.median([e[1].elapsed_time(e[2]) * 1e-3 for e in ev])
+        dropout = {"workload": cfg.name + " with dropout p=0.1 on P (supplementary)",
+                   "p_drop": p_drop, "fwd_ms": round(f_s * 1e3, 4),
+                   "fwd_tflops": round(fwd_flops / f_s / 1e12, 2),
+                   "bwd_ms": round(b_s * 1e3, 4), "bwd_tflops": round(bwd_flops / b_s / 1e12, 2),
+                   "steps": args.dropout_steps}
 
     decode = None
     if args.decode_steps > 0:
@@ -312,6 +345,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "supplementary": supp,
+        "dropout": dropout,
         "decode": decode,
     }
     print(json.dumps(out), flush=True)
