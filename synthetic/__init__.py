@@ -138,3 +138,73 @@ def random_inputs(B, H, N, d, seed, dtype="f32", qk_mult=1.0):
     if dtype == "bf16":
         q, k, v, do = (bf16_round(t) for t in (q, k, v, do))
     return q, k, v, do
+
+
+# ---------------------------------------------------------------- fp8 ---
+#
+# OCP FP8 E4M3 (the "fn" variant gfx950 uses: bias 7, 3 mantissa bits, no
+# infinities, largest finite 448, subnormals down to 2^-9). Inputs of the FP8
+# forward are stored in this format with one fp32 scale per tensor: value =
+# code * descale, descale = max|x| / 448 so that the largest magnitude maps to
+# the largest code.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round_bits(x) -> np.ndarray:
+    """fp32 -> E4M3 codes (uint8), round to nearest even, magnitudes beyond
+    448 saturate to 448."""
+    x = np.asarray(x, dtype=np.float64)
+    s = np.signbit(x).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # exponent of the binade, clamped to the normal range; below 2^-6 the
+    # spacing is that of the subnormals (2^-9)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)
+    q = np.rint(a / step) * step          # numpy rint: half to even
+    q = np.minimum(q, E4M3_MAX)
+    # encode q
+    out = np.zeros(q.shape, dtype=np.uint8)
+    nz = q > 0
+    qe = np.floor(np.log2(np.where(nz, q, 1.0)))
+    normal = nz & (qe >= -6)
+    mant = np.where(normal, q / np.exp2(qe) - 1.0, 0.0)
+    code_n = ((qe + 7).astype(np.int64) << 3) + np.rint(mant * 8).astype(np.int64)
+    code_s = np.rint(q / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, np.where(nz, code_s, 0))
+    out = (code.astype(np.uint8) | s)
+    return out
+
+
+def e4m3_bits_to_f64(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return sign * val
+
+
+def fp8_quantize(x):
+    """(codes uint8, descale float32) for one tensor: descale = max|x| / 448
+    rounded to fp32, codes = E4M3(x / descale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+    codes = e4m3_round_bits(x.astype(np.float64) / np.float64(descale))
+    return codes, float(descale)
+
+
+def fp8_inputs(B, H, N, d, seed, qk_mult=1.0):
+    """Q, K, V drawn as in draw_qkvdo, then stored as E4M3 codes with one
+    descale each. Returns ((q8, k8, v8), (qs, ks, vs), (q, k, v)) where the
+    last triple is the dequantized values (code * descale, exact in fp64)."""
+    q, k, v, _ = draw_qkvdo(B, H, N, d, seed, qk_mult)
+    codes, scales, deq = [], [], []
+    for t in (q, k, v):
+        c, s = fp8_quantize(t)
+        codes.append(c)
+        scales.append(s)
+        deq.append(e4m3_bits_to_f64(c) * np.float64(s))
+    return tuple(codes), tuple(scales), tuple(deq)

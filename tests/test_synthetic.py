@@ -73,3 +73,24 @@ def test_pages_dense_score_memory_figures():
     assert abs(c8["N"] ** 2 - c8["stated_elements"]) / c8["stated_elements"] < 0.01
     assert c8["N"] ** 2 * c8["bytes_per_element"] == 128 * 2 ** 20
     assert c32["N"] ** 2 * c32["bytes_per_element"] == 2 * 2 ** 30
+
+
+def test_e4m3_round_matches_torch():
+    """The E4M3 quantizer of the FP8 inputs equals torch's float8_e4m3fn
+    conversion (round to nearest even) on every value below the saturation
+    point, decodes every finite code as torch does, and saturates at 448."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * s
+                        for s in (1e-3, 3e-2, 1.0, 40.0, 400.0)])
+    x = x[np.abs(x) <= 448]
+    ours = syn.e4m3_round_bits(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    codes = np.arange(256, dtype=np.uint8)
+    tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ok = np.isfinite(tv)
+    assert np.array_equal(syn.e4m3_bits_to_f64(codes)[ok], tv[ok])
+    assert syn.e4m3_bits_to_f64(syn.e4m3_round_bits(np.array([1e6, -1e6])))[0] == 448.0
+    q8, s = syn.fp8_quantize(np.array([0.5, -3.0, 1.5], np.float32))
+    assert s == np.float32(3.0 / 448) and abs(syn.e4m3_bits_to_f64(q8[1]) * s + 3.0) < 1e-6
