@@ -15,6 +15,9 @@ Functions carry the C names:
                    stream=None)
     fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=False,
                    blockmask=None, workspace=None, stream=None)
+    fa_fwd_fp8(Q8, K8, V8, O, LSE, scale, q_descale, k_descale, v_descale,
+               causal=False, workspace=None, stream=None)
+    fa_fwd_fp8_workspace_bytes(B, H, N, d)
     fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None)
     fa_decode_workspace_bytes(B, H, Nq, Nk, d)
 Tensors are contiguous CUDA (HIP) tensors of shape [B, H, N, d]: bfloat16 for
@@ -74,6 +77,11 @@ _lib.fa_fwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i,
 _lib.fa_bwd_dropout.restype = _i
 _lib.fa_bwd_dropout.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
                                 _i, _vp, _f, ctypes.c_ulonglong, _vp, _sz, _vp]
+_lib.fa_fwd_fp8.restype = _i
+_lib.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp,
+                            _sz, _vp]
+_lib.fa_fwd_fp8_workspace_bytes.restype = _sz
+_lib.fa_fwd_fp8_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.fa_decode.restype = _i
 _lib.fa_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.fa_decode_workspace_bytes.restype = _sz
@@ -88,7 +96,7 @@ _lib.fa_version.argtypes = []
 # Symbols declared in include/fa.h (checked by the ABI test).
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_f32",
             "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout",
-            "fa_decode", "fa_decode_workspace_bytes",
+            "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
             "fa_status_str", "fa_last_hip_error", "fa_version")
 
 
@@ -308,3 +316,26 @@ def fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=
                                _ptr(dK), _ptr(dV), B, H, N, d, float(scale), int(bool(causal)),
                                _ptr(blockmask), float(p_drop), int(seed), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream_ptr(stream)))
+
+
+def fa_fwd_fp8_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.fa_fwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd_fp8(Q8, K8, V8, O, LSE, scale, q_descale, k_descale, v_descale, causal=False,
+               workspace=None, stream=None):
+    """FP8 forward: Q8, K8, V8 contiguous uint8 E4M3 codes [B, H, N, d] (value =
+    code * descale); writes O (bfloat16) and LSE in place."""
+    import torch
+    shape = _shape(Q8)
+    _require((Q8, K8, V8), torch.uint8, shape)
+    _require((O,), torch.bfloat16, shape)
+    _require_lse(LSE, shape)
+    B, H, N, d = shape
+    if workspace is None:
+        workspace = torch.empty(max(fa_fwd_fp8_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
+                                device=Q8.device)
+    _check(_lib.fa_fwd_fp8(_ptr(Q8), _ptr(K8), _ptr(V8), _ptr(O), _ptr(LSE), B, H, N, d,
+                           float(scale), float(q_descale), float(k_descale), float(v_descale),
+                           int(bool(causal)), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream_ptr(stream)))

@@ -286,6 +286,52 @@ fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const voi
         blockmask, workspace, workspace_bytes, stream, false, p_drop, seed);
 }
 
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128))
+        return 0;
+    return fa::fp8_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_fwd_fp8(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                     int H, int N, int d, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    bool empty = false;
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    if (st != FA_OK)
+        return st;
+    if (d != 64 && d != 128)
+        return FA_ERR_HEADDIM;
+    for (float s : {q_descale, k_descale, v_descale})
+        if (!std::isfinite(s) || !(s > 0.f))
+            return FA_ERR_SCALE;
+    if (empty)
+        return FA_OK;
+    st = check_ptrs({Q, K, V, O, LSE});
+    if (st != FA_OK)
+        return st;
+    if (workspace == nullptr || workspace_bytes < fa::fp8_workspace_bytes(B, H, N, d) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return FA_ERR_WORKSPACE;
+    fa::Fp8Problem p;
+    p.B = B;
+    p.H = H;
+    p.N = N;
+    p.d = d;
+    p.scale = scale;
+    p.q_descale = q_descale;
+    p.k_descale = k_descale;
+    p.v_descale = v_descale;
+    p.causal = causal;
+    p.stream = static_cast<hipStream_t>(stream);
+    return hip_status(fa::launch_fwd_fp8(p, static_cast<const uint8_t *>(Q),
+                                         static_cast<const uint8_t *>(K),
+                                         static_cast<const uint8_t *>(V),
+                                         static_cast<uint16_t *>(O), LSE, workspace));
+}
+
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d)
 {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk < 0 || d <= 0)

@@ -70,6 +70,18 @@ DecodeSplit decode_split(int B, int H, int Nq, int Nk, int d);
 hipError_t launch_decode_bf16(const DecodeProblem &p, const uint16_t *Q, const uint16_t *K,
                               const uint16_t *V, uint16_t *O, float *LSE, void *workspace);
 
+// FP8 forward: E4M3 Q, K, V with one descale each, bf16 O, fp32 LSE.
+struct Fp8Problem {
+    int B, H, N, d;  // d: 64 or 128
+    float scale, q_descale, k_descale, v_descale;
+    int causal;
+    hipStream_t stream;
+};
+// Workspace of the FP8 forward: V^T tiles, [B*H][ceil(N/64)][d][64] bytes.
+size_t fp8_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_fwd_fp8(const Fp8Problem &p, const uint8_t *Q, const uint8_t *K,
+                          const uint8_t *V, uint16_t *O, float *LSE, void *workspace);
+
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE);
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,

@@ -141,6 +141,28 @@ fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const voi
                          float p_drop, unsigned long long seed, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/* Bytes of device scratch fa_fwd_fp8 needs (0 for an empty problem or an
+ * unsupported d): V^T in 64-key tiles, B*H*ceil(N/64)*64*d bytes. */
+size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
+
+/* FP8 forward (lukebest.github.io FlashAttention, lineage table "谱系": the
+ * third generation adds an FP8 forward). Q, K, V: [B][H][N][d] OCP E4M3 codes
+ * (1 byte each; value = code * descale, one fp32 descale per tensor); O:
+ * [B][H][N][d] bf16; LSE: [B][H][N] float. Computes the forward of the
+ * decoded values: S = scale * Q K^T from the exact fp8 products accumulated
+ * in fp32, fp32 online softmax, P rounded to E4M3 for the P V product, O and
+ * LSE as fa_fwd. The error against exact attention of the decoded inputs is
+ * that of rounding P to a 3-bit mantissa (relative error about 3% per
+ * weight, in O's relative L2 about as much). d: 64 or 128; no block mask;
+ * causal as fa_fwd. workspace: at least fa_fwd_fp8_workspace_bytes(B, H, N,
+ * d) bytes of device memory, 256-byte aligned, owned by the caller (V is
+ * transposed into it first). Descales must be finite and > 0
+ * (FA_ERR_SCALE otherwise). */
+fa_status fa_fwd_fp8(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                     int H, int N, int d, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Bytes of device scratch fa_decode needs for this shape (0 for an empty
  * problem). It depends on the shape only. */
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);

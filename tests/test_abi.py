@@ -187,3 +187,26 @@ def test_dropout_validation():
         assert f(N=0, p=0.5) == 0        # empty: nothing done
         assert f(N=0, p=2.0) == 5        # but the probability is still checked
     assert bwd(ws=None) == 6
+
+
+def test_fp8_validation():
+    lib = fa.lib()
+
+    def call(**kw):
+        a = dict(B=1, H=1, N=128, d=128, qs=0.01, ks=0.01, vs=0.01, ws=P, wsb=1 << 30, Q=P)
+        a.update(kw)
+        return lib.fa_fwd_fp8(a["Q"], P, P, P, P, a["B"], a["H"], a["N"], a["d"], 0.08, a["qs"],
+                              a["ks"], a["vs"], 0, a["ws"], a["wsb"], None)
+
+    assert call(Q=None) == 1
+    assert call(d=96) == 3                       # FP8 forward: d = 64 or 128
+    assert call(d=32) == 3
+    assert call(qs=0.0) == 5
+    assert call(vs=float("nan")) == 5
+    assert call(ks=-1.0) == 5
+    assert call(ws=None) == 6
+    assert call(wsb=fa.fa_fwd_fp8_workspace_bytes(1, 1, 128, 128) - 1) == 6
+    assert call(N=0) == 0
+    # V^T in 64-key tiles: B*H*ceil(N/64)*64*d bytes, 256-byte padded
+    assert fa.fa_fwd_fp8_workspace_bytes(2, 3, 100, 64) == 2 * 3 * 2 * 64 * 64
+    assert fa.fa_fwd_fp8_workspace_bytes(1, 1, 100, 96) == 0

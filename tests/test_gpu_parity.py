@@ -336,3 +336,32 @@ def test_dropout_full_size_one_head():
     got = {n: gu.host(t[sl]) for n, t in (("O", O), ("LSE", LSE), ("dQ", dQ), ("dK", dK),
                                           ("dV", dV))}
     gu.check_outputs("bf16", got, dict(zip(("O", "LSE", "dQ", "dK", "dV"), ref)))
+
+
+FP8 = [
+    # (B, H, N, d, causal, qk_mult)
+    (1, 2, 300, 128, True, 1.0),
+    (2, 1, 129, 64, False, 1.0),
+    (1, 1, 1031, 128, True, 1.0),
+    (1, 2, 64, 64, True, 1.0),
+    (1, 2, 2048, 128, True, 2.0),
+    (1, 1, 1, 128, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,qk_mult", FP8)
+def test_fp8_forward_against_oracle(B, H, N, d, causal, qk_mult):
+    """FP8 forward against exact attention of the decoded E4M3 inputs, to the
+    tolerance derived for rounding P to E4M3."""
+    import exact_io_aware_attention_amd as fa
+    (q8, k8, v8), (qs, ks, vs), (q, k, v) = syn.fp8_inputs(B, H, N, d, 6000 + N + d, qk_mult)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"fp8 B={B} H={H} N={N} d={d} causal={causal} qk={qk_mult}", flush=True)
+    Q8, K8, V8 = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda") for x in (q8, k8, v8))
+    O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    LSE = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_fp8(Q8, K8, V8, O, LSE, scale, qs, ks, vs, causal=causal)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention(q, k, v, scale, causal=causal)
+    gu.check("O", gu.host(O), Or, max_abs=gu.FP8_O_MAX_ABS, rel_l2=gu.FP8_O_REL_L2)
+    gu.check_lse("LSE", gu.host(LSE), Lr, gu.BF16_LSE_MAX_ABS)
