@@ -15,7 +15,8 @@ Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
 --cpu-heads H (heads of the CPU fp64 reference timed as the baseline; 0 skips)
 --supp-steps S (the same shape without the causal mask) --dropout-steps S (the
 same workload with dropout p=0.1) --decode-steps S (the split-KV decode path on
-its own workload, HBM-bound). The supplementary runs
+its own workload, HBM-bound) --fp8-steps S (the FP8 forward on the same
+shape). The supplementary runs
 are reported beside the headline and never enter `value`.
 """
 import argparse
@@ -32,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 METRIC = "attention fwd+bwd TFLOP/s and % of MFMA bf16 peak at N=8192, d=128, 1 GPU"
 
 
@@ -48,6 +50,8 @@ def parse():
                     help="timed calls of the supplementary split-KV decode run (0: skip)")
     ap.add_argument("--dropout-steps", type=int, default=5,
                     help="timed steps of the supplementary dropout run (0: skip)")
+    ap.add_argument("--fp8-steps", type=int, default=10,
+                    help="timed calls of the supplementary FP8 forward run (0: skip)")
     return ap.parse_args()
 
 
@@ -301,6 +305,33 @@ def main():
                    "bwd_ms": round(b_s * 1e3, 4), "bwd_tflops": round(bwd_flops / b_s / 1e12, 2),
                    "steps": args.dropout_steps}
 
+    # Supplementary: the FP8 forward on the same shape (Q, K, V quantized to
+    # E4M3 with per-tensor descales); never part of `value`.
+    fp8 = None
+    if args.fp8_steps > 0 and cfg.d in (64, 128) and mask is None:
+        def q8(t):
+            amax = float(t.float().abs().max())
+            ds = amax / 448.0
+            return (t.float() / ds).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), ds
+        (Q8, qd), (K8, kd), (V8, vd) = q8(Q), q8(K), q8(V)
+        O8 = torch.empty_like(O)
+        ws8 = torch.empty(fa.fa_fwd_fp8_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d),
+                          dtype=torch.uint8, device=dev)
+        fa.fa_fwd_fp8(Q8, K8, V8, O8, LSE, scale, qd, kd, vd, causal=causal, workspace=ws8)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.fp8_steps)]
+        for e in ev:
+            e[0].record()
+            fa.fa_fwd_fp8(Q8, K8, V8, O8, LSE, scale, qd, kd, vd, causal=causal, workspace=ws8)
+            e[1].record()
+        torch.cuda.synchronize()
+        f_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
+        fp8 = {"workload": cfg.name + " forward with E4M3 Q, K, V and P (supplementary)",
+               "fwd_ms": round(f_s * 1e3, 4), "fwd_tflops": round(fwd_flops / f_s / 1e12, 2),
+               "frac_of_fp8_peak": round(fwd_flops / f_s / 1e12 / PEAK_FP8_TFLOPS, 4),
+               "steps": args.fp8_steps}
+        del Q8, K8, V8, O8, ws8
+
     decode = None
     if args.decode_steps > 0:
         decode = decode_run(args.decode_steps)
@@ -346,6 +377,7 @@ def main():
         "cpu_baseline": cpu,
         "supplementary": supp,
         "dropout": dropout,
+        "fp8": fp8,
         "decode": decode,
     }
     print(json.dumps(out), flush=True)
