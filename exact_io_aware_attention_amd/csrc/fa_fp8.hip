@@ -22,8 +22,9 @@
 // writes V^T per 64-key tile as D rows of 64 bytes, key j at position
 // 32 ((j / 4) % 2) + 16 (j / 32) + 4 ((j % 32) / 8) + j % 4, so that each
 // lane's V^T operand is 32 contiguous bytes. Tiles stream into LDS by direct
-// loads (double-buffered); 16-byte chunks are XOR-swizzled so that the b128
-// operand reads of 16 lanes hit 16 different bank groups.
+// loads (three buffers, two tiles ahead; the next tile's S^T MFMAs are issued
+// beside the current softmax); 16-byte chunks are XOR-swizzled so that the
+// b128 operand reads of 16 lanes hit 16 different bank groups.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -101,7 +102,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
     constexpr int KCH = D / 16;  // 16-byte chunks per K row
     constexpr uint32_t TB = 64 * D;   // bytes of a K tile, and of a V^T tile
     constexpr int NBLK = TB / 1024;   // 1 KB direct loads per tile
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];  // K0 K1 V0 V1
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[6 * TB];  // K0 K1 K2 V0 V1 V2
     const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item = xcd_work_item(p.per_xcd);
@@ -149,15 +150,37 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
         const bf16x8 x = lds_b128_at(a);
         return __builtin_bit_cast(uint4, x);
     };
+    // Tile t's K and V^T go to buffers t % 3; per wave the K loads are
+    // issued before the V^T loads, so that waiting for all but the last
+    // LPV loads leaves only V^T in flight.
     auto issue = [&](int t, int slot) __attribute__((always_inline)) {
-        const uint32_t kbuf = lds0 + slot * TB, vbuf = lds0 + (2 + slot) * TB;
+        const uint32_t kbuf = lds0 + slot * TB, vbuf = lds0 + (3 + slot) * TB;
         const i32x4 rk = buffer_rsrc(Kh + (size_t)t * BC * D, (uint32_t)(N - t * BC) * D);
         const i32x4 rv = buffer_rsrc(Vth + (size_t)t * TB, TB);
         for (int b = wave; b < NBLK; b += W) {
             const int kr = b * (1024 / D) + lane / KCH, kc = (lane % KCH) ^ k_swz(kr);
             lds_dma_buf_b128(rk, kr * D + 16 * kc, kbuf + b * 1024);
+        }
+        for (int b = wave; b < NBLK; b += W) {
             const int vr = b * 16 + lane / 4, vc = (lane % 4) ^ v_swz(vr);
             lds_dma_buf_b128(rv, vr * 64 + 16 * vc, vbuf + b * 1024);
+        }
+    };
+    static_assert(NBLK <= W, "one K and one V^T load per wave and tile at most");
+    // S^T of tile t's two 32-key blocks (K in buffer `slot`)
+    auto qk = [&](int slot, f32x16 (&sv)[2]) __attribute__((always_inline)) {
+        const uint32_t kbuf = lds0 + slot * TB;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            sv[blk] = f32x16{};
+            const int r = 32 * blk + l32;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const uint4 a = k_read(kbuf, r, 4 * kk + 2 * hi);
+                const uint4 b = k_read(kbuf, r, 4 * kk + 2 * hi + 1);
+                const i32x8 ka = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+                sv[blk] = mfma_fp8(ka, qf[kk], sv[blk]);
+            }
         }
     };
 
@@ -172,28 +195,25 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
     float m = -INFINITY, l = 0.f, thr = -INFINITY, nmref = 0.f;
     const float c = p.c;
 
+    // Software pipeline: iteration t issues the loads of tile t+2, the S^T
+    // MFMAs of tile t+1 (their results are used one iteration later, so the
+    // matrix pipe works beside this tile's softmax), then tile t's softmax
+    // and P V.
     issue(0, 0);
+    if (t_end > 1)
+        issue(1, 1);
     lds_dma_wait<0>();
     __syncthreads();
+    f32x16 s[2], s_nxt[2];
+    qk(0, s);
     for (int t = 0; t < t_end; ++t) {
-        const int slot = t & 1;
+        const int slot = t % 3;
+        const bool more = t + 2 < t_end;
+        if (more)
+            issue(t + 2, (t + 2) % 3);  // buffers of tile t-1, free since the last barrier
         if (t + 1 < t_end)
-            issue(t + 1, slot ^ 1);  // its buffers were last read before the previous barrier
-        const uint32_t kbuf = lds0 + slot * TB, vbuf = lds0 + (2 + slot) * TB;
-
-        f32x16 s[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x16{};
-            const int r = 32 * blk + l32;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const uint4 a = k_read(kbuf, r, 4 * kk + 2 * hi);
-                const uint4 b = k_read(kbuf, r, 4 * kk + 2 * hi + 1);
-                const i32x8 ka = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-                s[blk] = mfma_fp8(ka, qf[kk], s[blk]);
-            }
-        }
+            qk((t + 1) % 3, s_nxt);
+        const uint32_t vbuf = lds0 + (3 + slot) * TB;
         // keys past the end, above the diagonal (causal)
         const int kb = t * BC;
         if (kb + BC > N || (CAUSAL && kb + BC - 1 > wr0)) {
@@ -263,9 +283,17 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
             for (int r2 = 0; r2 < 16; ++r2)
                 o[db][r2] = fmaf(f, ot[r2], o[db][r2]);
         }
-        // tile t+1 has landed everywhere, and tile t's buffers may be refilled
-        lds_dma_wait<0>();
+        // Tile t+1's V^T and tile t+2's K have landed (the next iteration
+        // computes tile t+2's S^T), tile t+2's V^T may still be in flight;
+        // the barrier extends that to all waves and frees tile t's buffers.
+        if (more)
+            lds_dma_wait<1>();
+        else
+            lds_dma_wait<0>();
         __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+            s[blk] = s_nxt[blk];
     }
 
     const float lt = halves_sum(l);
