@@ -3,10 +3,12 @@
 // are OCP E4M3 codes with one fp32 descale each (value = code * descale); the
 // result is the forward of those values: S = scale (Q K^T) computed from the
 // exact fp8 products in fp32, online softmax in fp32 (mstx.cn/posts/485
-// §三.2, lazy rescale as in the bf16 kernel), P rounded to E4M3 for the P V
-// contraction relative to each tile's own row max (weights <= 1, the largest
-// exactly 1), the tile's P V added to O times 2^(tile max - reference max);
-// O = (P V) * v_descale / l in fp32, stored as bf16; LSE as in fa_fwd.
+// §三.2) whose reference follows the row max exactly, P rounded to E4M3 for
+// the P V contraction (weights <= 1; the one that sets a new max is exactly 1,
+// so rows dominated by few keys keep them exact -- a reference lagging below
+// the max, as the bf16 kernel's lazy rescale allows, would round them with up
+// to 6% error); O = (P V) * v_descale / l in fp32, stored as bf16; LSE as in
+// fa_fwd.
 //
 // Contractions on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales): one
 // MFMA covers 64 of the contraction index, so S^T = K Q^T of a 32-key block
@@ -90,8 +92,6 @@ struct Fp8Params {
     float c;      // scale * q_descale * k_descale * log2(e)
     float o_mul;  // v_descale
 };
-
-constexpr float kFp8Slack = 8.f;  // log2 growth of the row max tolerated without rescale
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         o[db] = f32x16{};
-    float m = -INFINITY, l = 0.f, thr = -INFINITY, nmref = 0.f;
+    float m = -INFINITY, l = 0.f, nmref = 0.f;
     const float c = p.c;
 
     // Software pipeline: iteration t issues the loads of tile t+2, the S^T
@@ -234,11 +234,12 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
         for (int r = 0; r < 16; ++r)
             mx = vmax2(mx, s[1][r]);
         mx = halves_max(mx) * c;
-        if (__any(mx > thr)) {
+        // The reference follows the row max exactly (no slack): every weight
+        // is <= 1 and the one that sets a new max is exactly 1 in E4M3.
+        if (__any(mx > m)) {
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - mnew);
             m = mnew;
-            thr = m + kFp8Slack;
             nmref = (m == -INFINITY) ? 0.f : -m;
             l *= alpha;
 #pragma unroll
@@ -247,14 +248,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                 for (int r = 0; r < 16; ++r)
                     o[db][r] *= alpha;
         }
-        // This tile's weights relative to its own row max, pt = 2^(c s - mt)
-        // <= 1: the largest is exactly 1 in E4M3, so a row dominated by few
-        // keys keeps them exact (relative to the running reference m, which
-        // the lazy rescale lets lag up to 2^8 below, it would round with up
-        // to 6% error). The tile's P V goes to fresh accumulators and enters
-        // O and l times 2^(mt - m).
-        const float mt = mx == -INFINITY ? 0.f : mx;
-        const float f = mx == -INFINITY ? 0.f : exp2_fast(mt + nmref);
+        // P = 2^(c s - m) <= 1 in fp32 for the row sum, E4M3 for P V
         i32x8 pp;
         float ls = 0.f;
 #pragma unroll
@@ -264,24 +258,21 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                 float e[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e[i] = exp2_fast(fmaf(s[blk][4 * w + i], c, -mt));
+                    e[i] = exp2_fast(fmaf(s[blk][4 * w + i], c, nmref));
                     ls += e[i];
                 }
                 int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
                 v = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
                 pp[4 * blk + w] = v;
             }
-        l = fmaf(f, ls, l);
+        l += ls;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int r = 32 * db + l32;
             const uint4 a = v_read(vbuf, r, 2 * hi);
             const uint4 b = v_read(vbuf, r, 2 * hi + 1);
             const i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-            const f32x16 ot = mfma_fp8(va, pp, f32x16{});
-#pragma unroll
-            for (int r2 = 0; r2 < 16; ++r2)
-                o[db][r2] = fmaf(f, ot[r2], o[db][r2]);
+            o[db] = mfma_fp8(va, pp, o[db]);
         }
         // Tile t+1's V^T and tile t+2's K have landed (the next iteration
         // computes tile t+2's S^T), tile t+2's V^T may still be in flight;
