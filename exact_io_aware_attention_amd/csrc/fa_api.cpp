@@ -27,13 +27,19 @@ bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// Head dims: multiples of 8 up to 128 everywhere, up to 256 in the plain
+// forward and the fp32 path.
+constexpr int kMaxD = 128;
+constexpr int kMaxDWide = 256;
+
 // Checks common to every entry point, in a fixed order. *empty is set when
 // the problem has no elements (then nothing is launched).
-fa_status check_common(int B, int H, int N, int d, float scale, int causal, bool *empty)
+fa_status check_common(int B, int H, int N, int d, float scale, int causal, bool *empty,
+                       int max_d = kMaxD)
 {
     if (B < 0 || H < 0 || N < 0)
         return FA_ERR_SHAPE;
-    if (d < 8 || d > 128 || d % 8 != 0)
+    if (d < 8 || d > max_d || d % 8 != 0)
         return FA_ERR_HEADDIM;
     if (!std::isfinite(scale) || !(scale > 0.f) || (causal != 0 && causal != 1))
         return FA_ERR_SCALE;
@@ -98,10 +104,10 @@ fa_status set_dropout(fa::Problem &p, float p_drop, unsigned long long seed)
 template <typename T>
 fa_status fwd_common(const T *Q, const T *K, const T *V, T *O, float *LSE, int B, int H, int N,
                      int d, float scale, int causal, const uint8_t *blockmask, void *stream,
-                     bool f32, float p_drop = 0.f, unsigned long long seed = 0)
+                     bool f32, int max_d, float p_drop = 0.f, unsigned long long seed = 0)
 {
     bool empty = false;
-    fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty, max_d);
     if (st != FA_OK)
         return st;
     fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
@@ -130,11 +136,11 @@ template <typename T>
 fa_status bwd_common(const T *dO, const T *Q, const T *K, const T *V, const T *O,
                      const float *LSE, T *dQ, T *dK, T *dV, int B, int H, int N, int d,
                      float scale, int causal, const uint8_t *blockmask, void *workspace,
-                     size_t workspace_bytes, void *stream, bool f32, float p_drop = 0.f,
+                     size_t workspace_bytes, void *stream, bool f32, int max_d, float p_drop = 0.f,
                      unsigned long long seed = 0)
 {
     bool empty = false;
-    fa_status st = check_common(B, H, N, d, scale, causal, &empty);
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty, max_d);
     if (st != FA_OK)
         return st;
     fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
@@ -194,7 +200,7 @@ fa_status fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LS
 {
     return fwd_common<uint16_t>(static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
                                 static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), LSE,
-                                B, H, N, d, scale, causal, blockmask, stream, false);
+                                B, H, N, d, scale, causal, blockmask, stream, false, kMaxDWide);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
@@ -214,7 +220,7 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V, co
         static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
         static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
-        blockmask, workspace, workspace_bytes, stream, false);
+        blockmask, workspace, workspace_bytes, stream, false, kMaxD);
 }
 
 fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE, int B, int H, int N, int d,
@@ -269,7 +275,8 @@ fa_status fa_fwd_dropout(const void *Q, const void *K, const void *V, void *O, f
 {
     return fwd_common<uint16_t>(static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(K),
                                 static_cast<const uint16_t *>(V), static_cast<uint16_t *>(O), LSE,
-                                B, H, N, d, scale, causal, blockmask, stream, false, p_drop, seed);
+                                B, H, N, d, scale, causal, blockmask, stream, false, kMaxD, p_drop,
+                                seed);
 }
 
 fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const void *V,
@@ -283,7 +290,7 @@ fa_status fa_bwd_dropout(const void *dO, const void *Q, const void *K, const voi
         static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
         static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
-        blockmask, workspace, workspace_bytes, stream, false, p_drop, seed);
+        blockmask, workspace, workspace_bytes, stream, false, kMaxD, p_drop, seed);
 }
 
 size_t fa_fwd_fp8_workspace_bytes(int B, int H, int N, int d)
@@ -383,7 +390,8 @@ fa_status fa_fwd_f32(const float *Q, const float *K, const float *V, float *O, f
                      int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
                      void *stream)
 {
-    return fwd_common<float>(Q, K, V, O, LSE, B, H, N, d, scale, causal, blockmask, stream, true);
+    return fwd_common<float>(Q, K, V, O, LSE, B, H, N, d, scale, causal, blockmask, stream, true,
+                             kMaxDWide);
 }
 
 fa_status fa_bwd_f32(const float *dO, const float *Q, const float *K, const float *V,
@@ -392,7 +400,7 @@ fa_status fa_bwd_f32(const float *dO, const float *Q, const float *K, const floa
                      void *workspace, size_t workspace_bytes, void *stream)
 {
     return bwd_common<float>(dO, Q, K, V, O, LSE, dQ, dK, dV, B, H, N, d, scale, causal,
-                             blockmask, workspace, workspace_bytes, stream, true);
+                             blockmask, workspace, workspace_bytes, stream, true, kMaxDWide);
 }
 
 const char *fa_status_str(fa_status s)
@@ -401,7 +409,9 @@ const char *fa_status_str(fa_status s)
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer";
     case FA_ERR_SHAPE: return "invalid shape";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (d must be a multiple of 8 in [8, 128])";
+    case FA_ERR_HEADDIM:
+        return "unsupported head dimension (d must be a multiple of 8 in [8, 128]; in [8, 256] for fa_fwd, "
+               "fa_fwd_f32 and fa_bwd_f32)";
     case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1, dropout probability in [0, 1)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

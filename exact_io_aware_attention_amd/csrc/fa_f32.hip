@@ -3,8 +3,10 @@
 // bf16 rounding anywhere), so that a disagreement with the reference can be
 // told apart from bf16 rounding. One thread owns one query row (forward,
 // dQ) or one key row (dK, dV); key/query tiles are staged in LDS and read by
-// broadcast. Head dims below the compiled width (64 or 128) are zero-padded
-// on load and not stored.
+// broadcast. Head dims below the compiled width (64, 128 or 256) are
+// zero-padded on load and not stored. (At 256 a thread's row vectors exceed
+// the register file and live partly in scratch memory: slow, still exact
+// fp32.)
 //
 // Forward: mstx.cn/posts/485 §三.2 "Online Softmax" update rule (base 2,
 // c = scale * log2 e), O divided by l once at the end.
@@ -268,15 +270,22 @@ hipError_t bwd_f32_d(const Problem &p, const float *dO, const float *Q, const fl
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE)
 {
-    return p.d <= 64 ? fwd_f32_d<64>(p, Q, K, V, O, LSE) : fwd_f32_d<128>(p, Q, K, V, O, LSE);
+    if (p.d <= 64)
+        return fwd_f32_d<64>(p, Q, K, V, O, LSE);
+    if (p.d <= 128)
+        return fwd_f32_d<128>(p, Q, K, V, O, LSE);
+    return fwd_f32_d<256>(p, Q, K, V, O, LSE);
 }
 
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,
                           const float *V, const float *O, const float *LSE, float *dQ,
                           float *dK, float *dV, void *ws)
 {
-    return p.d <= 64 ? bwd_f32_d<64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws)
-                     : bwd_f32_d<128>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+    if (p.d <= 64)
+        return bwd_f32_d<64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+    if (p.d <= 128)
+        return bwd_f32_d<128>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+    return bwd_f32_d<256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
 }
 
 }  // namespace fa

@@ -47,8 +47,13 @@
 // takes exponents against 0, so no (-inf) - (-inf) arises; it ends with
 // O = 0, LSE = -inf.
 //
-// Head dims below the kernel width D (64 or 128) are zero-padded: the tile
-// loads read zeros for the columns past dh and only dh columns are stored.
+// Head dims below the kernel width (64, 128 or 256) are zero-padded: the
+// tile loads read zeros for the columns past dh and only dh columns are
+// stored. Past 128, O^T no longer fits one wave's registers beside the rest:
+// the 256-wide instance reads 256-deep Q and K rows but V and O in column
+// slices of 128, one per workgroup, so the two workgroups of a query block
+// both compute its scores (1.5x the contraction work of one pass), with 128
+// query rows per workgroup (one wave per SIMD).
 //
 // Masking: causal (key j visible to query i iff j <= i, nanhubrain.csdn.net
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
@@ -71,11 +76,11 @@ struct FwdParams {
     float *LSE;
     const uint8_t *mask;
     int N;
-    int dh;       // head dimension (<= D; columns dh..D-1 are zero padding)
+    int dh;       // head dimension (<= DK; columns dh..DK-1 are zero padding)
     int nqb;      // query blocks per head
     int nkt;      // 64-key tiles per head
     int nmb;      // mask blocks per mask row
-    int items;    // B * H * nqb
+    int items;    // B * H * nqb * (DK / DV)
     int per_xcd;  // work items per XCD
     float c;      // scale * log2(e)
     DropParams drop;  // used by the DROP instances
@@ -83,29 +88,48 @@ struct FwdParams {
 
 constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated without rescale
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
+// DK: width of the Q and K rows the kernel reads (the depth of Q K^T); DV:
+// width of the slice of V and O columns one workgroup computes. DV < DK
+// splits the columns of O over DK / DV workgroups per query block, each
+// recomputing the scores: the head dim then grows past what one workgroup's
+// registers hold for O. 256-deep rows run one wave per SIMD (4 waves, 512
+// registers each, the part past 256 in AGPRs) instead of two.
+template <int DK>
+constexpr int fwd_waves()
 {
-    constexpr int W = 8;            // waves
+    return DK > 128 ? 4 : 8;
+}
+template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
+__global__ void __launch_bounds__(64 * fwd_waves<DK>(), 1) fwd_bf16_kernel(FwdParams p)
+{
+    constexpr int W = fwd_waves<DK>();  // waves
     constexpr int RW = 32;          // query rows per wave
     constexpr int BR = RW * W;      // query rows per workgroup
     constexpr int BC = 64;          // keys per LDS tile
-    constexpr int KK = D / 16;      // depth steps of Q K^T
-    constexpr int DB = D / 32;      // 32-row blocks of O^T
-    constexpr int CPR = D / 8;      // 16-byte chunks per row
-    constexpr int TILE = BC * D;    // elements per K or V tile
-    constexpr int LPW = TILE * 2 / 1024 / W;  // 1 KB direct loads per wave per tile
-    static_assert(LPW >= 1, "tile too small for the direct-load layout");
+    constexpr int KK = DK / 16;     // depth steps of Q K^T
+    constexpr int DB = DV / 32;     // 32-row blocks of O^T
+    constexpr int NSPLIT = DK / DV; // workgroups per query block
+    static_assert(NSPLIT * DV == DK && DV >= 64, "column split");
+    constexpr int CPRK = DK / 8;    // 16-byte chunks per K row
+    constexpr int CPRV = DV / 8;    // 16-byte chunks per V tile row
+    constexpr int LPWK = BC * DK * 2 / 1024 / W;  // 1 KB direct loads per wave per K tile
+    constexpr int LPWV = BC * DV * 2 / 1024 / W;  // ... per V tile
+    static_assert(LPWV >= 1, "tile too small for the direct-load layout");
 
     // LDS: three K tiles, then three V tiles.
-    constexpr uint32_t TB = TILE * 2;  // bytes per tile
-    constexpr uint32_t V_OFF = 3 * TB;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 3 * TB];
+    constexpr uint32_t TBK = BC * DK * 2;  // bytes per K tile
+    constexpr uint32_t TBV = BC * DV * 2;  // bytes per V tile
+    constexpr uint32_t V_OFF = 3 * TBK;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 3 * TBV];
     const uint32_t lds0 = lds_byte_addr(smem);
 
-    const int item = xcd_work_item(p.per_xcd);
-    if (item >= p.items)
+    const int item0 = xcd_work_item(p.per_xcd);
+    if (item0 >= p.items)
         return;
+    // the column slices of one query block are consecutive items (same XCD,
+    // sharing the K tiles in its L2)
+    const int item = item0 / NSPLIT;
+    const int col0 = (item0 - item * NSPLIT) * DV;  // first V / O column
     const int bh = item / p.nqb;
     const int qi = item - bh * p.nqb;
     const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;  // causal: longest rows first
@@ -164,34 +188,47 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     // Lane-dependent byte offsets, computed once. Direct loads: lane `lane`
     // of 1 KB block b writes chunk `lane` of the block, i.e. row
     // r = b * (64 / CPR) + lane / CPR, physical chunk lane % CPR, which holds
-    // logical chunk (lane % CPR) ^ swz(r).
-    auto k_swz = [](int r) -> int { return CPR == 16 ? (r % 16) : ((r / 2) % 8); };
+    // logical chunk (lane % CPR) ^ swz(r), CPR the chunks per row. K rows of
+    // 256 or 512 bytes: r % 16 (16 consecutive rows, one logical chunk, 16
+    // distinct bank groups).
+    auto k_swz = [](int r) -> int { return CPRK >= 16 ? (r % 16) : ((r / 2) % 8); };
     // V rows are only read by transpose reads: the aligned 4-chunk blocks of
     // any 4 aligned rows land on distinct banks (f(r) / 4 distinct), for
     // d = 64 with the row parity taking one bit's place.
     auto v_swz = [](int r) -> int {
-        return CPR == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
+        return CPRV == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
     };
-    // Global rows are dh wide; chunks past dh read as zeros.
-    uint32_t kdma[LPW], vdma[LPW];
+    // Global rows are dh wide; chunks past dh read as zeros. V tiles hold
+    // columns col0 .. col0 + DV - 1.
+    uint32_t kdma[LPWK], vdma[LPWV];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int r = (wave * LPW + i) * (64 / CPR) + lane / CPR;
-        const int kc = (lane % CPR) ^ k_swz(r), vc = (lane % CPR) ^ v_swz(r);
+    for (int i = 0; i < LPWK; ++i) {
+        const int r = (wave * LPWK + i) * (64 / CPRK) + lane / CPRK;
+        const int kc = (lane % CPRK) ^ k_swz(r);
         kdma[i] = 8 * kc < dh ? 2 * (r * dh + 8 * kc) : kBufferOutOfRange;
-        vdma[i] = 8 * vc < dh ? 2 * (r * dh + 8 * vc) : kBufferOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < LPWV; ++i) {
+        const int r = (wave * LPWV + i) * (64 / CPRV) + lane / CPRV;
+        const int vc = (lane % CPRV) ^ v_swz(r);
+        vdma[i] = col0 + 8 * vc < dh ? 2 * (r * dh + 8 * vc) : kBufferOutOfRange;
     }
     // Rows past the end of the sequence read as zeros (the buffer resource
-    // ends at row N) and are masked.
-    auto issue = [&](const uint16_t *src, const uint32_t (&off)[LPW], uint32_t tile, int t)
+    // ends at row N; for a column slice starting at col0 it starts col0
+    // elements in and ends as many before, at the end of the tensor's row
+    // N - 1) and are masked.
+    auto issue = [&](const uint16_t *src, auto const &off, uint32_t tile, int t, int c0)
                      __attribute__((always_inline)) {
-        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * dh, (uint32_t)(N - t * BC) * (2 * dh));
+        constexpr int L = sizeof(off) / sizeof(off[0]);
+        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * dh + c0, (uint32_t)(N - t * BC) * (2 * dh) - 2 * c0);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            lds_dma_buf_b128(rs, off[i], tile + (wave * LPW + i) * 1024);
+        for (int i = 0; i < L; ++i)
+            lds_dma_buf_b128(rs, off[i], tile + (wave * L + i) * 1024);
     };
-    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TB, t); };
-    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) { issue(Vh, vdma, lds0 + V_OFF + buf * TB, t); };
+    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TBK, t, 0); };
+    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
+        issue(Vh, vdma, lds0 + V_OFF + buf * TBV, t, col0);
+    };
 
     // Operand read addresses are this lane's byte address in buffer 0; the
     // buffer, which each unrolled iteration fixes, and the row block go into
@@ -201,7 +238,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     uint32_t kaddr[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-        kaddr[kk] = lds0 + 2 * (l32 * D + 8 * ((2 * kk + hi) ^ k_swz(l32)));
+        kaddr[kk] = lds0 + 2 * (l32 * DK + 8 * ((2 * kk + hi) ^ k_swz(l32)));
     auto qk_half = [&](uint32_t kofs, f32x16 &s) __attribute__((always_inline)) {
         s = f32x16{};
 #pragma unroll
@@ -223,8 +260,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         for (int db = 0; db < DB; ++db) {
             // opaque: the V base stays in the register, so that the buffer
             // and row offsets (< 64 KB) fit the immediate
-            vaddr[db][0] = opaque_addr(lds0 + V_OFF + 2 * (v_row * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in));
-            vaddr[db][1] = opaque_addr(lds0 + V_OFF + 2 * ((v_row + 8) * D + 8 * ((4 * db + v_lc) ^ v_swz(v_row + 8)) + v_in));
+            vaddr[db][0] = opaque_addr(lds0 + V_OFF + 2 * (v_row * DV + 8 * ((4 * db + v_lc) ^ v_swz(v_row)) + v_in));
+            vaddr[db][1] = opaque_addr(lds0 + V_OFF + 2 * ((v_row + 8) * DV + 8 * ((4 * db + v_lc) ^ v_swz(v_row + 8)) + v_in));
         }
     }
 
@@ -258,14 +295,14 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     if (t0 >= t_end) {
         // no visible key tile at all (fully masked rows): O = 0, LSE = -inf
         if (row < N) {
-            uint16_t *Oh = p.O + head + (size_t)row * dh;
+            uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (32 * db + 8 * j + 4 * hi < dh)
+                    if (col0 + 32 * db + 8 * j + 4 * hi < dh)
                         *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * j + 4 * hi) = uint2{0, 0};
-            if (hi == 0)
+            if (hi == 0 && col0 == 0)
                 p.LSE[(size_t)bh * N + row] = -INFINITY;
         }
         return;
@@ -283,8 +320,8 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     lds_dma_wait<0>();
     __syncthreads();
 
-    // Row max of a 32-key score block, times c: lane-local over the 16
-    // registers, then across the two 32-lane halves (both hold the row).
+    // Row max of a 32-key score block (unscaled scores): lane-local over the
+    // 16 registers, then across the two 32-lane halves (both hold the row).
     auto row_max = [&](const f32x16 &sv) __attribute__((always_inline)) -> float {
         // two interleaved chains, so that no max waits on the one before
         float ma = vmax3(sv[0], sv[1], sv[2]);
@@ -295,7 +332,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             mb = vmax3(mb, sv[r + 2], sv[r + 3]);
         }
         ma = vmax3(ma, sv[14], sv[15]);
-        return halves_max(vmax2(ma, mb)) * c;
+        return halves_max(vmax2(ma, mb));
     };
 
     f32x16 s_cur;
@@ -303,16 +340,19 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     mask_half(t0 * BC, s_cur);
     float mx_cur = row_max(s_cur);
     // Quantities of the reference max m that change only when it does: the
-    // rescale threshold m + slack, and the exponent offset -m (0 while
-    // m = -inf).
+    // rescale threshold (m + slack) / c on unscaled scores, and the exponent
+    // offset -m (0 while m = -inf).
+    const float inv_c = 1.f / c;
     float thr = -INFINITY, nmref = 0.f;
     // The first K^T fragments of each half-step are read one half-step
     // early, so that its first MFMAs wait for no LDS read: here those of the
-    // first half-step (tile t0's second 32 keys, buffer 0).
-    bf16x8 kpre[KK / 2];
+    // first half-step (tile t0's second 32 keys, buffer 0). Half the depth
+    // steps, at most 4 (256-deep rows: the registers of 8 would spill).
+    constexpr int NPRE = KK / 2 < 4 ? KK / 2 : 4;
+    bf16x8 kpre[NPRE];
 #pragma unroll
-    for (int kk = 0; kk < KK / 2; ++kk)
-        kpre[kk] = lds_b128_at(kaddr[kk] + 2 * 32 * D);
+    for (int kk = 0; kk < NPRE; ++kk)
+        kpre[kk] = lds_b128_at(kaddr[kk] + 2 * 32 * DK);
 
     // Tile j's K and V sit in buffer j % 3; the loop below is unrolled three
     // times so that each copy knows its buffers.
@@ -329,8 +369,9 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     auto tile = [&](auto mtag, auto ptag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
         constexpr int P = decltype(ptag)::value;           // j % 3
-        constexpr uint32_t KB_CUR = P * TB;                // tile j's buffer
-        constexpr uint32_t KB_NXT = (P + 1) % 3 * TB;      // tile j+1's
+        constexpr uint32_t KB_CUR = P * TBK;               // tile j's K buffer
+        constexpr uint32_t KB_NXT = (P + 1) % 3 * TBK;     // tile j+1's
+        constexpr uint32_t VB_CUR = P * TBV;               // tile j's V buffer
         constexpr int KB_NN = (P + 2) % 3;                 // tile j+2's
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
@@ -348,15 +389,15 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             // first half of tile j+1 (on the last tile a stale buffer is read
             // and the result unused). Its first half-depth runs beside the
             // row max, its second beside the exponentials.
-            const uint32_t kofs = (h == 0 ? KB_CUR : KB_NXT) + 2 * 32 * (h ^ 1) * D;
+            const uint32_t kofs = (h == 0 ? KB_CUR : KB_NXT) + 2 * 32 * (h ^ 1) * DK;
             // Rescale first, so that the rest of the half-step (the next
             // scores' MFMAs beside this block's exponentials, then P V) is one
             // straight-line block the scheduler can interleave.
             if (__any(mx_cur > thr)) {
-                const float mnew = fmaxf(m, mx_cur);
+                const float mnew = fmaxf(m, mx_cur * c);
                 const float alpha = (m == -INFINITY) ? 0.f : exp2_fast(m - mnew);
                 m = mnew;
-                thr = m + kRescaleSlack;
+                thr = (m + kRescaleSlack) * inv_c;
                 nmref = (m == -INFINITY) ? 0.f : -m;
                 l *= alpha;
 #pragma unroll
@@ -368,8 +409,11 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             f32x16 s_nxt = f32x16{};
             bf16x8 kf[KK];
 #pragma unroll
-            for (int kk = 0; kk < KK / 2; ++kk)
+            for (int kk = 0; kk < NPRE; ++kk)
                 kf[kk] = kpre[kk];
+#pragma unroll
+            for (int kk = NPRE; kk < KK / 2; ++kk)
+                kf[kk] = lds_b128_at(kaddr[kk] + kofs);
 #pragma unroll
             for (int kk = 0; kk < KK / 2; ++kk)
                 s_nxt = mfma32x32x16(kf[kk], qf[kk], s_nxt);
@@ -379,7 +423,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             bf16x8 vf[2][DB];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const uint32_t vofs = KB_CUR + 2 * (32 * h + 16 * hh) * D;
+                const uint32_t vofs = VB_CUR + 2 * (32 * h + 16 * hh) * DV;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     vf[hh][db] = lds_tr_pair_at(vaddr[db][0] + vofs, vaddr[db][1] + vofs);
@@ -439,13 +483,13 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
             {
                 if (h == 1)
                     lds_reads_wait_all();
-                const uint32_t nofs = h == 0 ? KB_NXT : KB_NXT + 2 * 32 * D;
+                const uint32_t nofs = h == 0 ? KB_NXT : KB_NXT + 2 * 32 * DK;
 #pragma unroll
-                for (int kk = 0; kk < KK / 2; ++kk)
+                for (int kk = 0; kk < NPRE; ++kk)
                     kpre[kk] = lds_b128_at(kaddr[kk] + nofs);
             }
             sched_interleave<KK / 2 + 2 * DB, 2, 4>();
-            __builtin_amdgcn_sched_group_barrier(0x100, KK / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NPRE, 0);
 
             if (MASKED) {
                 if (h == 0)
@@ -461,7 +505,7 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
         // waves. The next iteration reads tile j+2's K from its second
         // half-step on and its V one iteration later.
         if (more)
-            lds_dma_wait<LPW>();
+            lds_dma_wait<LPWV>();
         else
             lds_dma_wait<0>();
         barrier_reads_in_flight();
@@ -502,12 +546,12 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
     const float lt = halves_sum(l);
     if (row < N) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t *Oh = p.O + head + (size_t)row * dh;
+        uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                if (32 * db + 8 * jj + 4 * hi >= dh)
+                if (col0 + 32 * db + 8 * jj + 4 * hi >= dh)
                     continue;
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16_bits(o[db][4 * jj + 0] * inv) |
@@ -516,39 +560,40 @@ __global__ void __launch_bounds__(512, 1) fwd_bf16_kernel(FwdParams p)
                        ((uint32_t)f32_to_bf16_bits(o[db][4 * jj + 3] * inv) << 16);
                 *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * jj + 4 * hi) = pk;
             }
-        if (hi == 0)
+        if (hi == 0 && col0 == 0)
             p.LSE[(size_t)bh * N + row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
 {
     FwdParams fp = fp0;
-    constexpr int BR = 256;
+    constexpr int BR = 32 * fwd_waves<DK>();  // query rows per workgroup
     fp.nqb = (pr.N + BR - 1) / BR;
-    fp.items = pr.B * pr.H * fp.nqb;
+    fp.items = pr.B * pr.H * fp.nqb * (DK / DV);
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(512), 0, pr.stream, fp);
+    hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(64 * fwd_waves<DK>()), 0,
+                       pr.stream, fp);
     return hipGetLastError();
 }
 
-template <int D, bool DROP>
+template <int DK, int DV, bool DROP>
 static hipError_t launch_fwd_dd(const Problem &pr, const FwdParams &fp)
 {
     const bool sparse = pr.mask != nullptr;
     if (pr.causal)
-        return sparse ? launch_fwd_t<D, true, true, DROP>(pr, fp)
-                      : launch_fwd_t<D, true, false, DROP>(pr, fp);
-    return sparse ? launch_fwd_t<D, false, true, DROP>(pr, fp)
-                  : launch_fwd_t<D, false, false, DROP>(pr, fp);
+        return sparse ? launch_fwd_t<DK, DV, true, true, DROP>(pr, fp)
+                      : launch_fwd_t<DK, DV, true, false, DROP>(pr, fp);
+    return sparse ? launch_fwd_t<DK, DV, false, true, DROP>(pr, fp)
+                  : launch_fwd_t<DK, DV, false, false, DROP>(pr, fp);
 }
 
 template <int D>
 static hipError_t launch_fwd_d(const Problem &pr, const FwdParams &fp)
 {
-    return pr.dropout ? launch_fwd_dd<D, true>(pr, fp) : launch_fwd_dd<D, false>(pr, fp);
+    return pr.dropout ? launch_fwd_dd<D, D, true>(pr, fp) : launch_fwd_dd<D, D, false>(pr, fp);
 }
 
 hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t *K,
@@ -570,11 +615,16 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.drop.seed_lo = (uint32_t)pr.drop_seed;
     fp.drop.seed_hi = (uint32_t)(pr.drop_seed >> 32);
     fp.drop.inv_keep = pr.drop_inv_keep;
-    // head dims up to 64 run in the 64-wide kernel, the others (up to 128) in
-    // the 128-wide one, zero-padded
+    // head dims up to 64 run in the 64-wide kernel, up to 128 in the
+    // 128-wide one, zero-padded; up to 256 with 256-deep scores and the O
+    // columns split over two workgroups of 128 (no dropout there)
     if (pr.d <= 64)
         return launch_fwd_d<64>(pr, fp);
-    return launch_fwd_d<128>(pr, fp);
+    if (pr.d <= 128)
+        return launch_fwd_d<128>(pr, fp);
+    if (pr.dropout)
+        return hipErrorInvalidValue;
+    return launch_fwd_dd<256, 128, false>(pr, fp);
 }
 
 }  // namespace fa

@@ -62,9 +62,10 @@ def test_forward_validation(fn):
     assert call(LSE=None) == 1
     assert call(N=-1) == 2
     assert call(B=-3) == 2
-    assert call(d=100) == 3                     # head dims: multiples of 8 in [8, 128]
-    assert call(d=136) == 3
-    assert call(d=256) == 3
+    assert call(d=100) == 3                     # head dims: multiples of 8 in [8, 256]
+    assert call(d=252) == 3
+    assert call(d=264) == 3
+    assert call(d=512) == 3
     assert call(d=4) == 3
     assert call(d=0) == 3
     assert call(O=MIS) == 4
@@ -87,6 +88,7 @@ def test_backward_validation():
     assert ws > 0 and ws % 256 == 0
     assert _bwd(dQ=None) == 1
     assert _bwd(d=33) == 3
+    assert _bwd(d=136) == 3                       # the bf16 backward stops at 128
     assert _bwd(d=256) == 3
     assert _bwd(dV=MIS) == 4
     assert _bwd(scale=0.0) == 5
@@ -94,6 +96,16 @@ def test_backward_validation():
     assert _bwd(wsb=ws - 1) == 6
     assert _bwd(ws=P + 128, wsb=ws) == 6          # workspace must be 256-byte aligned
     assert _bwd(B=0, dO=None) == 0
+
+
+def test_f32_backward_head_dims():
+    def call(d):
+        return fa.lib().fa_bwd_f32(P, P, P, P, P, P, P, P, P, 1, 1, 128, d, 0.125, 0, None, P,
+                                   1 << 30, None)
+
+    assert call(252) == 3                         # the fp32 path takes multiples of 8 up to 256
+    assert call(264) == 3
+    assert call(4) == 3
 
 
 def test_workspace_bytes():
@@ -184,6 +196,7 @@ def test_dropout_validation():
         assert f(p=float("inf")) == 5
         assert f(Q=None) == 1
         assert f(d=100) == 3
+        assert f(d=136) == 3             # dropout stops at d = 128
         assert f(N=0, p=0.5) == 0        # empty: nothing done
         assert f(N=0, p=2.0) == 5        # but the probability is still checked
     assert bwd(ws=None) == 6

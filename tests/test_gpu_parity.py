@@ -214,6 +214,65 @@ def test_other_head_dims(precision, B, H, N, d, causal, sparse):
         assert torch.equal(view.float().cpu(), torch.from_numpy(got[name]).float().to(dt).float()), name
 
 
+WIDE_HEAD_DIMS = [
+    # (B, H, N, d, causal, sparse): 128 < d <= 256 -- the bf16 forward runs
+    # 256-deep scores with O in two column halves of 128 (the second half
+    # zero-padded past d), the fp32 path both directions
+    (1, 2, 300, 256, True, False),
+    (1, 1, 1000, 256, False, False),
+    (1, 1, 260, 192, False, True),
+    (2, 1, 200, 136, True, False),
+    (1, 1, 64, 248, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS)
+def test_wide_head_dims_forward_bf16(B, H, N, d, causal, sparse):
+    import exact_io_aware_attention_amd as fa
+    seed = 6000 + N + d + 7 * causal + 3 * sparse
+    q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype="bf16")
+    nb = (N + 127) // 128
+    mask = None
+    if sparse:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        mask = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(mask, 1)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"bf16 forward B={B} H={H} N={N} d={d} causal={causal} sparse={sparse}", flush=True)
+    Q, K, V = (gu.dev(x, torch.bfloat16) for x in (q, k, v))
+    M = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).to("cuda")
+    big, O = _guarded(Q.shape, torch.bfloat16, 7.0)
+    LSE = torch.full((B, H, N), 7.0, dtype=torch.float32, device="cuda")
+    fa.fa_fwd(Q, K, V, O, LSE, scale, causal=causal, blockmask=M)
+    torch.cuda.synchronize()
+    assert torch.all(big[Q.numel():] == 7.0), "O: store past the end"
+    rO, rL = oracle.attention(q, k, v, scale, causal=causal, blockmask=mask)
+    gu.check_outputs("bf16", {"O": gu.host(O), "LSE": gu.host(LSE)}, {"O": rO, "LSE": rL},
+                     fields=("O", "LSE"))
+    # run to run: bitwise identical
+    O2 = torch.empty_like(O)
+    LSE2 = torch.empty_like(LSE)
+    fa.fa_fwd(Q, K, V, O2, LSE2, scale, causal=causal, blockmask=M)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(LSE, LSE2)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS[:3])
+def test_wide_head_dims_f32(B, H, N, d, causal, sparse):
+    seed = 6100 + N + d + 7 * causal + 3 * sparse
+    q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype="f32")
+    nb = (N + 127) // 128
+    mask = None
+    if sparse:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        mask = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(mask, 1)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"f32 B={B} H={H} N={N} d={d} causal={causal} sparse={sparse}", flush=True)
+    got = _got(*gu.gpu_forward_backward(q, k, v, do, scale, causal, mask, "f32"))
+    gu.check_outputs("f32", got, _ref_all(q, k, v, do, scale, causal, mask))
+
+
 DECODE = [
     # (B, H, Nq, Nk, d, causal)
     (1, 2, 1, 1, 128, True),
