@@ -16,7 +16,8 @@ Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
 --supp-steps S (the same shape without the causal mask) --dropout-steps S (the
 same workload with dropout p=0.1) --decode-steps S (the split-KV decode path on
 its own workload, HBM-bound) --fp8-steps S (the FP8 forward on the same
-shape). The supplementary runs
+shape) --wide-steps S (the forward at head dim 256 on the same B, H, N). The
+supplementary runs
 are reported beside the headline and never enter `value`.
 """
 import argparse
@@ -52,6 +53,8 @@ def parse():
                     help="timed steps of the supplementary dropout run (0: skip)")
     ap.add_argument("--fp8-steps", type=int, default=10,
                     help="timed calls of the supplementary FP8 forward run (0: skip)")
+    ap.add_argument("--wide-steps", type=int, default=10,
+                    help="timed calls of the supplementary head-dim-256 forward run (0: skip)")
     return ap.parse_args()
 
 
@@ -230,9 +233,10 @@ def main():
     dominant = max(names, key=lambda n: avg[n])
     ach = kernel_flops[dominant] / avg[dominant] / 1e12
     tf = lambda b: "true" if b else "false"  # noqa: E731
-    # kernel template arguments: head width, causal, block-sparse, dropout
+    # kernel template arguments: head width (the forward's: score depth and
+    # O column width), causal, block-sparse, dropout
     flags = f"{cfg.d}, {tf(cfg.causal)}, {tf(mask is not None)}, false"
-    symbols = {"fwd": f"fwd_bf16_kernel<{flags}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
+    symbols = {"fwd": f"fwd_bf16_kernel<{cfg.d}, {flags}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
                "bwd_dq": f"bwd_dq_kernel<{flags}>", "bwd_dkdv": f"bwd_dkdv_kernel<{flags}>"}
     tag = f"{cfg.name.replace('-', '_')}_b{cfg.B}h{cfg.H}n{cfg.N}d{cfg.d}"
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
@@ -332,6 +336,34 @@ def main():
                "steps": args.fp8_steps}
         del Q8, K8, V8, O8, ws8
 
+    # Supplementary: the forward at head dim 256 on the same B, H, N and mask
+    # (fresh seeded N(0,1) inputs, Q and K scaled like the workload's);
+    # never part of `value`.
+    wide = None
+    if args.wide_steps > 0 and mask is None:
+        g = torch.Generator(device=dev)
+        g.manual_seed(256)
+        shp = (cfg.B, cfg.H, cfg.N, 256)
+        Qw, Kw, Vw = (torch.randn(shp, generator=g, device=dev).mul_(m).to(torch.bfloat16)
+                      for m in (cfg.qk_mult, cfg.qk_mult, 1.0))
+        Ow = torch.empty_like(Qw)
+        sw = float(np.float32(1.0 / np.sqrt(256.0)))
+        fa.fa_fwd(Qw, Kw, Vw, Ow, LSE, sw, causal=causal)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.wide_steps)]
+        for e in ev:
+            e[0].record()
+            fa.fa_fwd(Qw, Kw, Vw, Ow, LSE, sw, causal=causal)
+            e[1].record()
+        torch.cuda.synchronize()
+        f_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
+        wflops = fwd_flops * 256 / cfg.d
+        wide = {"workload": cfg.name + " forward at head dim 256 (supplementary)", "d": 256,
+                "fwd_ms": round(f_s * 1e3, 4), "fwd_tflops": round(wflops / f_s / 1e12, 2),
+                "frac_of_peak": round(wflops / f_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "mfma_work_factor": 1.5, "steps": args.wide_steps}
+        del Qw, Kw, Vw, Ow
+
     decode = None
     if args.decode_steps > 0:
         decode = decode_run(args.decode_steps)
@@ -378,6 +410,7 @@ def main():
         "supplementary": supp,
         "dropout": dropout,
         "fp8": fp8,
+        "wide_head": wide,
         "decode": decode,
     }
     print(json.dumps(out), flush=True)
