@@ -112,12 +112,14 @@ def flop_counts(cfg, mask):
 DECODE_SHAPE = dict(B=8, H=32, Nq=1, Nk=32768, d=128)
 
 
-def decode_run(steps):
-    """fa_decode on DECODE_SHAPE with seeded N(0,1) bf16 inputs drawn on the
-    device; median of `steps` calls timed with HIP events on the stream."""
+def decode_run(steps, d=None):
+    """fa_decode on DECODE_SHAPE (head dim d if given) with seeded N(0,1) bf16
+    inputs drawn on the device; median of `steps` calls timed with HIP events
+    on the stream."""
     import torch
     import exact_io_aware_attention_amd as fa
-    B, H, Nq, Nk, d = (DECODE_SHAPE[x] for x in ("B", "H", "Nq", "Nk", "d"))
+    B, H, Nq, Nk = (DECODE_SHAPE[x] for x in ("B", "H", "Nq", "Nk"))
+    d = DECODE_SHAPE["d"] if d is None else d
     g = torch.Generator(device="cuda")
     g.manual_seed(31337)
     Q = torch.randn((B, H, Nq, d), generator=g, device="cuda").bfloat16()
@@ -141,7 +143,7 @@ def decode_run(steps):
     # algorithmic bytes: K and V once, Q and O once, LSE
     byts = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
     gbs = byts / t / 1e9
-    out = {"workload": "split-KV decode (supplementary)", **DECODE_SHAPE, "causal": True,
+    out = {"workload": "split-KV decode (supplementary)", **DECODE_SHAPE, "d": d, "causal": True,
            "us": round(t * 1e6, 1), "gbs": round(gbs, 1), "bound": "hbm",
            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": byts,
            "steps": steps}
@@ -364,9 +366,10 @@ def main():
                 "mfma_work_factor": 1.5, "steps": args.wide_steps}
         del Qw, Kw, Vw, Ow
 
-    decode = None
+    decode = decode256 = None
     if args.decode_steps > 0:
         decode = decode_run(args.decode_steps)
+        decode256 = decode_run(args.decode_steps, d=256)
 
     cpu = None
     if args.cpu_heads > 0:
@@ -412,6 +415,7 @@ def main():
         "fp8": fp8,
         "wide_head": wide,
         "decode": decode,
+        "decode_d256": decode256,
     }
     print(json.dumps(out), flush=True)
 

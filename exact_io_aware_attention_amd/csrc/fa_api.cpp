@@ -28,7 +28,7 @@ bool aligned16(const void *p)
 }
 
 // Head dims: multiples of 8 up to 128 everywhere, up to 256 in the plain
-// forward and the fp32 path.
+// forward, the decode path and the fp32 path.
 constexpr int kMaxD = 128;
 constexpr int kMaxDWide = 256;
 
@@ -353,11 +353,11 @@ fa_status fa_decode(const void *Q, const void *K, const void *V, void *O, float 
     bool empty = false;
     // the key side and the query side each pass the checks of a [B][H][N][d]
     // tensor (Nk may be 0: every query then sees no key)
-    fa_status st = check_common(B, H, Nq, d, scale, causal, &empty);
+    fa_status st = check_common(B, H, Nq, d, scale, causal, &empty, kMaxDWide);
     if (st != FA_OK)
         return st;
     bool no_keys = false;
-    st = check_common(B, H, Nk, d, scale, causal, &no_keys);
+    st = check_common(B, H, Nk, d, scale, causal, &no_keys, kMaxDWide);
     if (st != FA_OK)
         return st;
     if (empty)
@@ -411,7 +411,7 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_SHAPE: return "invalid shape";
     case FA_ERR_HEADDIM:
         return "unsupported head dimension (d must be a multiple of 8 in [8, 128]; in [8, 256] for fa_fwd, "
-               "fa_fwd_f32 and fa_bwd_f32)";
+               "fa_decode, fa_fwd_f32 and fa_bwd_f32)";
     case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1, dropout probability in [0, 1)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

@@ -34,7 +34,15 @@ namespace {
 
 constexpr int kDecRows = 32;   // queries per wave
 constexpr int kDecTile = 32;   // keys per LDS tile
-constexpr int kDecWaves = 4;   // waves per workgroup
+
+// Waves per workgroup: four, each with two 32-key K+V buffers in LDS (32 KB
+// per wave, 128 KB per workgroup at d = 128); at d = 256 the buffers are
+// twice as large and two waves fill the same 128 KB.
+template <int D>
+constexpr int dec_waves()
+{
+    return D > 128 ? 2 : 4;
+}
 
 struct DecodeParams {
     const uint16_t *Q, *K, *V;
@@ -48,8 +56,9 @@ struct DecodeParams {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kDecWaves * kWave, 1) decode_partial_kernel(DecodeParams p)
+__global__ void __launch_bounds__(dec_waves<D>() * kWave, 1) decode_partial_kernel(DecodeParams p)
 {
+    constexpr int kDecWaves = dec_waves<D>();
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
     constexpr int CPR = D / 8;
@@ -90,9 +99,11 @@ __global__ void __launch_bounds__(kDecWaves * kWave, 1) decode_partial_kernel(De
     // (chunk c at c ^ (r % 16), or c ^ ((r / 2) % 8) for 128-byte rows), V
     // rows for transpose reads (c ^ (4 (r % 4) + (r / 4) % 4), or with the
     // row parity in one bit's place).
-    auto k_swz = [](int r) -> int { return CPR == 16 ? (r % 16) : ((r / 2) % 8); };
+    // (rows of 256 or 512 bytes take the same swizzles: the bank of a byte
+    // depends on its address modulo 256)
+    auto k_swz = [](int r) -> int { return CPR >= 16 ? (r % 16) : ((r / 2) % 8); };
     auto v_swz = [](int r) -> int {
-        return CPR == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
+        return CPR >= 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
     };
     // Direct loads: lane `lane` of 1 KB block b writes physical chunk
     // lane % CPR of row b * (64 / CPR) + lane / CPR; global rows are dh wide
@@ -318,6 +329,7 @@ hipError_t decode_d(const DecodeProblem &pr, const DecodeSplit &sp, const uint16
     dp.chunk = sp.chunk;
     dp.items = (long)pr.B * pr.H * dp.nqb * sp.nsplit;
     dp.c = pr.scale * kLog2e;
+    constexpr int kDecWaves = dec_waves<D>();
     const unsigned grid = (unsigned)((dp.items + kDecWaves - 1) / kDecWaves);
     if (pr.causal)
         hipLaunchKernelGGL((decode_partial_kernel<D, true>), dim3(grid), dim3(kDecWaves * kWave), 0,
@@ -366,7 +378,9 @@ hipError_t launch_decode_bf16(const DecodeProblem &pr, const uint16_t *Q, const 
     const DecodeSplit sp = decode_split(pr.B, pr.H, pr.Nq, pr.Nk, pr.d);
     if (pr.d <= 64)
         return decode_d<64>(pr, sp, Q, K, V, O, LSE, workspace);
-    return decode_d<128>(pr, sp, Q, K, V, O, LSE, workspace);
+    if (pr.d <= 128)
+        return decode_d<128>(pr, sp, Q, K, V, O, LSE, workspace);
+    return decode_d<256>(pr, sp, Q, K, V, O, LSE, workspace);
 }
 
 }  // namespace fa

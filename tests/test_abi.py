@@ -148,7 +148,8 @@ def test_decode_validation():
     assert _dec(Nk=-1) == 2
     assert _dec(Nk=1 << 23) == 2                  # key slab exceeds 2^30 elements
     assert _dec(d=100) == 3
-    assert _dec(d=136) == 3
+    assert _dec(d=264) == 3
+    assert _dec(d=252) == 3
     assert _dec(O=MIS) == 4
     assert _dec(scale=0.0) == 5
     assert _dec(causal=3) == 5

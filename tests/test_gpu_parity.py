@@ -284,6 +284,8 @@ DECODE = [
     (1, 2, 40, 24, 64, True),        # Nq > Nk: the first rows see no key
     (1, 2, 3, 0, 64, False),         # no keys at all
     (1, 1, 8, 40000, 128, True),     # many chunks
+    (1, 2, 4, 3000, 256, True),      # head dim 256 (two waves per workgroup)
+    (2, 1, 33, 777, 200, False),     # 200: zero-padded to the 256-wide kernel
 ]
 
 
