@@ -301,6 +301,13 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     }
     const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
     const float nDi = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
+    // dP^T accumulates from -D (this lane's row), so that dS^T = P^T o dP^T
+    // takes one multiply; with dropout dP^T needs its own scaling first and
+    // starts from zero
+    f32x16 ndv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        ndv[r] = DROP ? 0.f : nDi;
 
     int t_end = p.nkt;
     if (CAUSAL)
@@ -362,7 +369,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
         if constexpr (DROP)
             dsm[r] = pe * ((((z_prev >> r) & 1u) ? dp_prev[r] * p.drop.inv_keep : 0.f) + nDi);
         else
-            dsm[r] = pe * (dp_prev[r] + nDi);
+            dsm[r] = pe * dp_prev[r];
         if (r % 8 == 7) {
             bf16x8 sk;
 #pragma unroll
@@ -414,7 +421,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
             for (int e = 0; e < EPS; ++e)
                 softmax_elem(mtag, (2 * kk) * EPS + e);
             __builtin_amdgcn_sched_barrier(0);
-            dp = mfma32x32x16(va[kk], gf[kk], kk == 0 ? f32x16{} : dp);
+            dp = mfma32x32x16(va[kk], gf[kk], kk == 0 ? ndv : dp);
             if (kk + PA < KK)
                 va[kk + PA] = cur.b128_at(V_OFF, kh, kk + PA);
             if (kk >= KK - PD)
