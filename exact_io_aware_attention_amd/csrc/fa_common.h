@@ -111,31 +111,38 @@ __device__ __forceinline__ void mfma_settle(f32x16 &acc)
 // which exposes the full load latency right after a prefetch is issued;
 // asm loads are not tracked, so the caller waits (lds_dma_wait) before the
 // barrier that hands the filled buffer to the other waves.
+//
+// Each load is preceded by one wait state (s_nop 0) inside its asm: the LDS
+// address comes from M0, which the compiler writes with an SALU move right
+// before the asm, and the ISA requires one wait state between an SALU write
+// of M0 and a global/buffer load with LDS = 1. The compiler's hazard check
+// does not look inside asm; without the wait a load can take the previous
+// M0 and fill the previous 1 KB block, leaving its own block stale.
 __device__ __forceinline__ uint32_t lds_byte_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 __device__ __forceinline__ void lds_dma_b128(const void *gsrc, uint32_t lds_block)
 {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+    asm volatile("s_nop 0\n\t" "global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
 __device__ __forceinline__ void lds_dma_b32(const void *gsrc, uint32_t lds_block)
 {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
+    asm volatile("s_nop 0\n\t" "global_load_lds_dword %0, off" ::"v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
 // The same with a wave-uniform base (SGPR pair) and a 32-bit per-lane byte
 // offset: no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void lds_dma_b128_at(const void *gbase, uint32_t off, uint32_t lds_block)
 {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(gbase),
+    asm volatile("s_nop 0\n\t" "global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(gbase),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
 __device__ __forceinline__ void lds_dma_b32_at(const void *gbase, uint32_t off, uint32_t lds_block)
 {
-    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(gbase),
+    asm volatile("s_nop 0\n\t" "global_load_lds_dword %0, %1" ::"v"(off), "s"(gbase),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
@@ -152,13 +159,13 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes)
 // per-lane byte offset into the resource.
 __device__ __forceinline__ void lds_dma_buf_b128(i32x4 rsrc, uint32_t off, uint32_t lds_block)
 {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+    asm volatile("s_nop 0\n\t" "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
 __device__ __forceinline__ void lds_dma_buf_b32(i32x4 rsrc, uint32_t off, uint32_t lds_block)
 {
-    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+    asm volatile("s_nop 0\n\t" "buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_block))
                  : "memory");
 }
@@ -324,8 +331,26 @@ __device__ __forceinline__ float halves_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait states between an MFMA's write of an accumulator and the first read of
+// it by inline asm (the row maxima below read freshly computed scores): the
+// ISA requires 12 after v_mfma_f32_32x32x16_bf16 and 20 after
+// v_mfma_scale_f32_32x32x64_f8f6f4 before a vector ALU instruction reads the
+// result. The compiler inserts them before its own instructions but does not
+// look inside asm, so an asm reader it places right behind the MFMA would
+// read the registers' previous contents. Tying the accumulator through this
+// statement orders every later read after the wait.
+__device__ __forceinline__ void mfma_result_wait_bf16(f32x16 &x)
+{
+    asm volatile("s_nop 11" : "+v"(x));
+}
+__device__ __forceinline__ void mfma_result_wait_fp8(f32x16 &x, f32x16 &y)
+{
+    asm volatile("s_nop 15\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
+
 // Max of three scores without the NaN-quieting copies fmaxf brings in IEEE
-// mode (no operand here is ever NaN; -inf is an ordinary value).
+// mode (no operand here is ever NaN; -inf is an ordinary value). An operand
+// fresh from an MFMA must have passed mfma_result_wait_* first.
 __device__ __forceinline__ float vmax3(float a, float b, float c)
 {
     float y;

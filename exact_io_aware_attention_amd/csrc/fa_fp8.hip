@@ -226,6 +226,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                         s[blk][r] = -INFINITY;
                 }
         }
+        mfma_result_wait_fp8(s[0], s[1]);
         float mx = vmax3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
         for (int r = 3; r < 16; ++r)
