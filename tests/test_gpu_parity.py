@@ -195,6 +195,76 @@ def test_full_size_run_to_run_bitwise():
             assert nd == 0, f"{name}: {nd} elements differ between runs"
 
 
+def test_other_paths_run_to_run_bitwise():
+    """Decode (d = 128 and 256), the FP8 forward, the dropout forward and
+    backward and the head-dim-256 forward, each three times on the same
+    sharp inputs (Q and K x 2): every output bit for bit the same."""
+    import exact_io_aware_attention_amd as fa
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+
+    def rnd(*shape, mult=1.0):
+        return (torch.randn(shape, generator=g, device="cuda") * mult).to(torch.bfloat16)
+
+    def same(name, fn):
+        runs = [fn() for _ in range(3)]
+        for r in runs[1:]:
+            for i, (x, y) in enumerate(zip(runs[0], r)):
+                nd = int((_bits(x) != _bits(y)).sum())
+                assert nd == 0, f"{name} output {i}: {nd} elements differ between runs"
+
+    B, H, N = 1, 8, 4096
+    for d in (128, 256):
+        Q, K, V = rnd(2, 8, 4, d, mult=2.0), rnd(2, 8, 6000, d, mult=2.0), rnd(2, 8, 6000, d)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(2, 8, 4, 6000, d), dtype=torch.uint8,
+                         device="cuda")
+
+        def dec():
+            O = torch.empty_like(Q)
+            L = torch.empty((2, 8, 4), dtype=torch.float32, device="cuda")
+            fa.fa_decode(Q, K, V, O, L, d ** -0.5, causal=True, workspace=ws)
+            torch.cuda.synchronize()
+            return O, L
+        same(f"decode d={d}", dec)
+
+    d = 128
+    Q, K, V, dO = rnd(B, H, N, d, mult=2.0), rnd(B, H, N, d, mult=2.0), rnd(B, H, N, d), rnd(B, H, N, d)
+    ws = fa.new_workspace(B, H, N, d)
+
+    def drop():
+        O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+        L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.fa_fwd_dropout(Q, K, V, O, L, d ** -0.5, 0.1, 99, causal=True)
+        fa.fa_bwd_dropout(dO, Q, K, V, O, L, dQ, dK, dV, d ** -0.5, 0.1, 99, causal=True, workspace=ws)
+        torch.cuda.synchronize()
+        return O, L, dQ, dK, dV
+    same("dropout", drop)
+
+    def q8(t):
+        ds = float(t.float().abs().max()) / 448.0
+        return (t.float() / ds).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), ds
+    (Q8, qs), (K8, ks), (V8, vs) = q8(Q), q8(K), q8(V)
+    ws8 = torch.empty(fa.fa_fwd_fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+
+    def fp8():
+        O = torch.empty_like(Q)
+        L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.fa_fwd_fp8(Q8, K8, V8, O, L, d ** -0.5, qs, ks, vs, causal=True, workspace=ws8)
+        torch.cuda.synchronize()
+        return O, L
+    same("fp8", fp8)
+
+    Qw, Kw, Vw = rnd(B, H, N, 256, mult=2.0), rnd(B, H, N, 256, mult=2.0), rnd(B, H, N, 256)
+
+    def wide():
+        O = torch.empty_like(Qw)
+        L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.fa_fwd(Qw, Kw, Vw, O, L, 256 ** -0.5, causal=True)
+        torch.cuda.synchronize()
+        return O, L
+    same("forward d=256", wide)
+
+
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
