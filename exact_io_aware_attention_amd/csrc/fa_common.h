@@ -343,6 +343,15 @@ __device__ __forceinline__ void mfma_result_wait_bf16(f32x16 &x)
 {
     asm volatile("s_nop 11" : "+v"(x));
 }
+// The same ordering without a fixed wait, for an asm chain that starts at one
+// register of a single MFMA's accumulator: a compiler-visible add of +0 (not
+// an identity for -0, so it is kept) before which the compiler inserts just
+// the wait states its own schedule still needs; the chain's first asm reads
+// the result, and every register of the accumulator is written by then.
+__device__ __forceinline__ void mfma_result_touch(f32x16 &x, int i)
+{
+    x[i] += 0.f;
+}
 __device__ __forceinline__ void mfma_result_wait_fp8(f32x16 &x, f32x16 &y)
 {
     asm volatile("s_nop 15\n\ts_nop 3" : "+v"(x), "+v"(y));

@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(dec_waves<D>() * kWave, 1) decode_partial_kern
                     sv[r] = -INFINITY;
             }
         }
-        mfma_result_wait_bf16(sv);
+        mfma_result_touch(sv, 0);  // head of the asm max chain
         float mx = vmax3(sv[0], sv[1], sv[2]);
 #pragma unroll
         for (int r = 3; r < 15; r += 2)

@@ -325,6 +325,8 @@ __global__ void __launch_bounds__(64 * fwd_waves<DK>(), 1) fwd_bf16_kernel(FwdPa
 
     // Row max of a 32-key score block (unscaled scores): lane-local over the
     // 16 registers, then across the two 32-lane halves (both hold the row).
+    // Its two asm chains start at registers 0 and 3, which the caller passes
+    // through mfma_result_touch first.
     auto row_max = [&](const f32x16 &sv) __attribute__((always_inline)) -> float {
         // two interleaved chains, so that no max waits on the one before
         float ma = vmax3(sv[0], sv[1], sv[2]);
@@ -341,7 +343,8 @@ __global__ void __launch_bounds__(64 * fwd_waves<DK>(), 1) fwd_bf16_kernel(FwdPa
     f32x16 s_cur;
     qk_half(0, s_cur);
     mask_half(t0 * BC, s_cur);
-    mfma_result_wait_bf16(s_cur);
+    mfma_result_touch(s_cur, 0);
+    mfma_result_touch(s_cur, 3);
     float mx_cur = row_max(s_cur);
     // Quantities of the reference max m that change only when it does: the
     // rescale threshold (m + slack) / c on unscaled scores, and the exponent
@@ -501,7 +504,8 @@ __global__ void __launch_bounds__(64 * fwd_waves<DK>(), 1) fwd_bf16_kernel(FwdPa
                 else if (tn < t_end)
                     mask_half(tn * BC, s_nxt);
             }
-            mfma_result_wait_bf16(s_nxt);
+            mfma_result_touch(s_nxt, 0);  // heads of row_max's two asm chains
+            mfma_result_touch(s_nxt, 3);
             mx_cur = row_max(s_nxt);  // beside the P V MFMAs still in flight
             s_cur = s_nxt;
         }
