@@ -28,7 +28,7 @@ bool aligned16(const void *p)
 }
 
 // Head dims: multiples of 8 up to 128 everywhere, up to 256 in the plain
-// forward, the decode path and the fp32 path.
+// forward and backward, the decode path and the fp32 path.
 constexpr int kMaxD = 128;
 constexpr int kMaxDWide = 256;
 
@@ -220,7 +220,7 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V, co
         static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
         static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
         static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), B, H, N, d, scale, causal,
-        blockmask, workspace, workspace_bytes, stream, false, kMaxD);
+        blockmask, workspace, workspace_bytes, stream, false, kMaxDWide);
 }
 
 fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE, int B, int H, int N, int d,
@@ -411,7 +411,7 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_SHAPE: return "invalid shape";
     case FA_ERR_HEADDIM:
         return "unsupported head dimension (d must be a multiple of 8 in [8, 128]; in [8, 256] for fa_fwd, "
-               "fa_decode, fa_fwd_f32 and fa_bwd_f32)";
+               "fa_bwd, fa_decode, fa_fwd_f32 and fa_bwd_f32)";
     case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1, dropout probability in [0, 1)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

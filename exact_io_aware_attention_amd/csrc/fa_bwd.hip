@@ -1084,6 +1084,8 @@ hipError_t launch_bwd_bf16(const Problem &pr, const uint16_t *dO, const uint16_t
                            const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                            void *workspace)
 {
+    if (pr.d > 128)
+        return launch_bwd_bf16_scalar(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, workspace);
     hipError_t e = launch_bwd_prep_bf16(pr, dO, O, LSE, workspace);
     if (e != hipSuccess)
         return e;

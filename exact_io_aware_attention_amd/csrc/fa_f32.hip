@@ -3,7 +3,9 @@
 // bf16 rounding anywhere), so that a disagreement with the reference can be
 // told apart from bf16 rounding. One thread owns one query row (forward,
 // dQ) or one key row (dK, dV); key/query tiles are staged in LDS and read by
-// broadcast. Head dims below the compiled width (64, 128 or 256) are
+// broadcast. The backward kernels also run on bf16 tensors (fp32 arithmetic
+// throughout, bf16 only on load and store): they are the bf16 backward for
+// head dims past 128, which the matrix-core kernels do not cover. Head dims below the compiled width (64, 128 or 256) are
 // zero-padded on load and not stored. (At 256 a thread's row vectors exceed
 // the register file and live partly in scratch memory: slow, still exact
 // fp32.)
@@ -23,6 +25,14 @@ namespace fa {
 namespace {
 
 constexpr int kT = 64;  // rows per LDS tile and threads per workgroup
+
+// Element access of the backward kernels, which also serve bf16 tensors
+// (uint16 bit patterns: widened exactly to fp32 on load, rounded to nearest
+// even on store).
+__device__ __forceinline__ float ldf(const float *p) { return *p; }
+__device__ __forceinline__ float ldf(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ void stf(float *p, float x) { *p = x; }
+__device__ __forceinline__ void stf(uint16_t *p, float x) { *p = f32_to_bf16_bits(x); }
 
 __device__ __forceinline__ bool visible(int i, int j, bool causal, const uint8_t *mask, int nmb)
 {
@@ -95,8 +105,8 @@ __global__ void __launch_bounds__(kT) fwd_f32_kernel(const float *Q, const float
 
 // D_i = rowsum(dO o O) and LSE in base 2 (+inf for a row without visible
 // keys, so that 2^(c s - lse2) = 0 there).
-template <int D>
-__global__ void __launch_bounds__(kT) bwd_pre_f32_kernel(const float *dO, const float *O,
+template <typename T, int D>
+__global__ void __launch_bounds__(kT) bwd_pre_f32_kernel(const T *dO, const T *O,
                                                          const float *LSE, float *delta,
                                                          float *lse2, int N, int dh)
 {
@@ -107,7 +117,7 @@ __global__ void __launch_bounds__(kT) bwd_pre_f32_kernel(const float *dO, const 
     const size_t base = ((size_t)bh * N + row) * dh;
     float acc = 0.f;
     for (int x = 0; x < dh; ++x)
-        acc = fmaf(dO[base + x], O[base + x], acc);
+        acc = fmaf(ldf(dO + base + x), ldf(O + base + x), acc);
     const size_t r = (size_t)bh * N + row;
     delta[r] = acc;
     const float L = LSE[r];
@@ -115,11 +125,11 @@ __global__ void __launch_bounds__(kT) bwd_pre_f32_kernel(const float *dO, const 
 }
 
 // dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j, one thread per query row.
-template <int D>
-__global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const float *Q,
-                                                        const float *K, const float *V,
+template <typename T, int D>
+__global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const T *dO, const T *Q,
+                                                        const T *K, const T *V,
                                                         const float *delta, const float *lse2,
-                                                        float *dQ, int N, int dh, float scale, float c,
+                                                        T *dQ, int N, int dh, float scale, float c,
                                                         int causal, const uint8_t *mask, int nmb)
 {
     __shared__ float Ks[kT][D];
@@ -129,8 +139,8 @@ __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const f
     const size_t head = (size_t)bh * N * dh;
     float q[D], go[D], dq[D];
     for (int x = 0; x < D; ++x) {
-        q[x] = row < N && x < dh ? Q[head + (size_t)row * dh + x] : 0.f;
-        go[x] = row < N && x < dh ? dO[head + (size_t)row * dh + x] : 0.f;
+        q[x] = row < N && x < dh ? ldf(Q + head + (size_t)row * dh + x) : 0.f;
+        go[x] = row < N && x < dh ? ldf(dO + head + (size_t)row * dh + x) : 0.f;
         dq[x] = 0.f;
     }
     const float Di = row < N ? delta[(size_t)bh * N + row] : 0.f;
@@ -141,8 +151,8 @@ __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const f
         for (int e = threadIdx.x; e < kT * D; e += kT) {
             const int r = e / D, x = e % D;
             const bool in = k0 + r < N && x < dh;
-            Ks[r][x] = in ? K[head + (size_t)(k0 + r) * dh + x] : 0.f;
-            Vs[r][x] = in ? V[head + (size_t)(k0 + r) * dh + x] : 0.f;
+            Ks[r][x] = in ? ldf(K + head + (size_t)(k0 + r) * dh + x) : 0.f;
+            Vs[r][x] = in ? ldf(V + head + (size_t)(k0 + r) * dh + x) : 0.f;
         }
         __syncthreads();
         if (row >= N)
@@ -164,16 +174,16 @@ __global__ void __launch_bounds__(kT) bwd_dq_f32_kernel(const float *dO, const f
     }
     if (row < N)
         for (int x = 0; x < dh; ++x)
-            dQ[head + (size_t)row * dh + x] = dq[x] * scale;
+            stf(dQ + head + (size_t)row * dh + x, dq[x] * scale);
 }
 
 // One thread per key row. WANT_DK: dK_j = scale * sum_i dS_ij Q_i;
 // otherwise dV_j = sum_i P_ij dO_i.
-template <int D, bool WANT_DK>
-__global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const float *Q,
-                                                         const float *K, const float *V,
+template <typename T, int D, bool WANT_DK>
+__global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const T *dO, const T *Q,
+                                                         const T *K, const T *V,
                                                          const float *delta, const float *lse2,
-                                                         float *dOut, int N, int dh, float scale, float c,
+                                                         T *dOut, int N, int dh, float scale, float c,
                                                          int causal, const uint8_t *mask, int nmb)
 {
     __shared__ float Qs[kT][D];
@@ -184,8 +194,8 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
     const size_t head = (size_t)bh * N * dh;
     float k[D], v[D], acc[D];
     for (int x = 0; x < D; ++x) {
-        k[x] = key < N && x < dh ? K[head + (size_t)key * dh + x] : 0.f;
-        v[x] = (WANT_DK && key < N && x < dh) ? V[head + (size_t)key * dh + x] : 0.f;
+        k[x] = key < N && x < dh ? ldf(K + head + (size_t)key * dh + x) : 0.f;
+        v[x] = (WANT_DK && key < N && x < dh) ? ldf(V + head + (size_t)key * dh + x) : 0.f;
         acc[x] = 0.f;
     }
     const int qstart = causal ? (int)blockIdx.x * kT : 0;
@@ -194,8 +204,8 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
         for (int e = threadIdx.x; e < kT * D; e += kT) {
             const int r = e / D, x = e % D;
             const bool in = q0 + r < N && x < dh;
-            Qs[r][x] = in ? Q[head + (size_t)(q0 + r) * dh + x] : 0.f;
-            Gs[r][x] = in ? dO[head + (size_t)(q0 + r) * dh + x] : 0.f;
+            Qs[r][x] = in ? ldf(Q + head + (size_t)(q0 + r) * dh + x) : 0.f;
+            Gs[r][x] = in ? ldf(dO + head + (size_t)(q0 + r) * dh + x) : 0.f;
         }
         {
             const int r = threadIdx.x;
@@ -229,7 +239,7 @@ __global__ void __launch_bounds__(kT) bwd_dkv_f32_kernel(const float *dO, const 
     }
     if (key < N)
         for (int x = 0; x < dh; ++x)
-            dOut[head + (size_t)key * dh + x] = WANT_DK ? acc[x] * scale : acc[x];
+            stf(dOut + head + (size_t)key * dh + x, WANT_DK ? acc[x] * scale : acc[x]);
 }
 
 template <int D>
@@ -243,10 +253,9 @@ hipError_t fwd_f32_d(const Problem &p, const float *Q, const float *K, const flo
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t bwd_f32_d(const Problem &p, const float *dO, const float *Q, const float *K,
-                     const float *V, const float *O, const float *LSE, float *dQ, float *dK,
-                     float *dV, void *ws)
+template <typename T, int D>
+hipError_t bwd_f32_d(const Problem &p, const T *dO, const T *Q, const T *K, const T *V,
+                     const T *O, const float *LSE, T *dQ, T *dK, T *dV, void *ws)
 {
     const BwdWorkspace L = bwd_workspace_layout(p.B, p.H, p.N, p.d);
     float *delta = reinterpret_cast<float *>(static_cast<char *>(ws) + L.delta_off);
@@ -254,13 +263,13 @@ hipError_t bwd_f32_d(const Problem &p, const float *dO, const float *Q, const fl
     const dim3 grid((p.N + kT - 1) / kT, p.B * p.H);
     const int nmb = (p.N + kMaskBlock - 1) / kMaskBlock;
     const float c = p.scale * kLog2e;
-    hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), grid, dim3(kT), 0, p.stream, dO, O, LSE, delta,
+    hipLaunchKernelGGL((bwd_pre_f32_kernel<T, D>), grid, dim3(kT), 0, p.stream, dO, O, LSE, delta,
                        lse2, p.N, p.d);
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), grid, dim3(kT), 0, p.stream, dO, Q, K, V, delta,
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<T, D>), grid, dim3(kT), 0, p.stream, dO, Q, K, V, delta,
                        lse2, dQ, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
-    hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, true>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
+    hipLaunchKernelGGL((bwd_dkv_f32_kernel<T, D, true>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
                        delta, lse2, dK, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
-    hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, false>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
+    hipLaunchKernelGGL((bwd_dkv_f32_kernel<T, D, false>), grid, dim3(kT), 0, p.stream, dO, Q, K, V,
                        delta, lse2, dV, p.N, p.d, p.scale, c, p.causal, p.mask, nmb);
     return hipGetLastError();
 }
@@ -282,10 +291,18 @@ hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, con
                           float *dK, float *dV, void *ws)
 {
     if (p.d <= 64)
-        return bwd_f32_d<64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+        return bwd_f32_d<float, 64>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
     if (p.d <= 128)
-        return bwd_f32_d<128>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
-    return bwd_f32_d<256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+        return bwd_f32_d<float, 128>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+    return bwd_f32_d<float, 256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
+}
+
+hipError_t launch_bwd_bf16_scalar(const Problem &p, const uint16_t *dO, const uint16_t *Q,
+                                  const uint16_t *K, const uint16_t *V, const uint16_t *O,
+                                  const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
+                                  void *ws)
+{
+    return bwd_f32_d<uint16_t, 256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
 }
 
 }  // namespace fa

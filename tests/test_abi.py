@@ -88,14 +88,22 @@ def test_backward_validation():
     assert ws > 0 and ws % 256 == 0
     assert _bwd(dQ=None) == 1
     assert _bwd(d=33) == 3
-    assert _bwd(d=136) == 3                       # the bf16 backward stops at 128
-    assert _bwd(d=256) == 3
+    assert _bwd(d=252) == 3                       # multiples of 8 up to 256
+    assert _bwd(d=264) == 3
     assert _bwd(dV=MIS) == 4
     assert _bwd(scale=0.0) == 5
     assert _bwd(ws=None) == 6
     assert _bwd(wsb=ws - 1) == 6
     assert _bwd(ws=P + 128, wsb=ws) == 6          # workspace must be 256-byte aligned
     assert _bwd(B=0, dO=None) == 0
+
+
+def test_backward_phases_head_dims():
+    """The phase entry points run only the matrix-core kernels (d <= 128)."""
+    lib = fa.lib()
+    assert lib.fa_bwd_prep(P, P, P, 1, 1, 128, 136, P, 1 << 30, None) == 3
+    assert lib.fa_bwd_dq(P, P, P, P, P, 1, 1, 128, 136, 0.125, 0, None, P, 1 << 30, None) == 3
+    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, 1, 1, 128, 256, 0.125, 0, None, P, 1 << 30, None) == 3
 
 
 def test_f32_backward_head_dims():

@@ -438,6 +438,24 @@ def test_wide_head_dims_forward_bf16(B, H, N, d, causal, sparse):
     assert torch.equal(O, O2) and torch.equal(LSE, LSE2)
 
 
+@pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS)
+def test_wide_head_dims_backward_bf16(B, H, N, d, causal, sparse):
+    """fa_fwd + fa_bwd in bf16 at 128 < d <= 256 (the backward there runs the
+    scalar kernels on bf16 tensors), every output against the oracle."""
+    seed = 6200 + N + d + 7 * causal + 3 * sparse
+    q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype="bf16")
+    nb = (N + 127) // 128
+    mask = None
+    if sparse:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        mask = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(mask, 1)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"bf16 fwd+bwd B={B} H={H} N={N} d={d} causal={causal} sparse={sparse}", flush=True)
+    got = _got(*gu.gpu_forward_backward(q, k, v, do, scale, causal, mask, "bf16"))
+    gu.check_outputs("bf16", got, _ref_all(q, k, v, do, scale, causal, mask))
+
+
 @pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS[:3])
 def test_wide_head_dims_f32(B, H, N, d, causal, sparse):
     seed = 6100 + N + d + 7 * causal + 3 * sparse
