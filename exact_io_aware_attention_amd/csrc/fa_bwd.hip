@@ -1058,7 +1058,9 @@ hipError_t launch_bwd_prep_bf16(const Problem &pr, const uint16_t *dO, const uin
 {
     const BwdPtrs b = bwd_ptrs(pr, dO, nullptr, nullptr, nullptr, O, LSE, nullptr, nullptr,
                                nullptr, workspace);
-    return pr.d <= 64 ? prep_d<64>(pr, b) : prep_d<128>(pr, b);
+    if (pr.d <= 64)
+        return prep_d<64>(pr, b);
+    return pr.d <= 128 ? prep_d<128>(pr, b) : prep_d<256>(pr, b);  // 256: the wide backward
 }
 
 hipError_t launch_bwd_dq_bf16(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
@@ -1085,7 +1087,7 @@ hipError_t launch_bwd_bf16(const Problem &pr, const uint16_t *dO, const uint16_t
                            void *workspace)
 {
     if (pr.d > 128)
-        return launch_bwd_bf16_scalar(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, workspace);
+        return launch_bwd_bf16_wide(pr, dO, Q, K, V, O, LSE, dQ, dK, dV, workspace);
     hipError_t e = launch_bwd_prep_bf16(pr, dO, O, LSE, workspace);
     if (e != hipSuccess)
         return e;

@@ -3,9 +3,8 @@
 // bf16 rounding anywhere), so that a disagreement with the reference can be
 // told apart from bf16 rounding. One thread owns one query row (forward,
 // dQ) or one key row (dK, dV); key/query tiles are staged in LDS and read by
-// broadcast. The backward kernels also run on bf16 tensors (fp32 arithmetic
-// throughout, bf16 only on load and store): they are the bf16 backward for
-// head dims past 128, which the matrix-core kernels do not cover. Head dims below the compiled width (64, 128 or 256) are
+// broadcast. (The element type of the backward kernels is a template
+// parameter; only fp32 storage is instantiated.) Head dims below the compiled width (64, 128 or 256) are
 // zero-padded on load and not stored. (At 256 a thread's row vectors exceed
 // the register file and live partly in scratch memory: slow, still exact
 // fp32.)
@@ -297,12 +296,5 @@ hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, con
     return bwd_f32_d<float, 256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
 }
 
-hipError_t launch_bwd_bf16_scalar(const Problem &p, const uint16_t *dO, const uint16_t *Q,
-                                  const uint16_t *K, const uint16_t *V, const uint16_t *O,
-                                  const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
-                                  void *ws)
-{
-    return bwd_f32_d<uint16_t, 256>(p, dO, Q, K, V, O, LSE, dQ, dK, dV, ws);
-}
 
 }  // namespace fa

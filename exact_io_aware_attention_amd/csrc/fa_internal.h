@@ -84,12 +84,12 @@ hipError_t launch_fwd_fp8(const Fp8Problem &p, const uint8_t *Q, const uint8_t *
 
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE);
-// bf16 backward for head dims in (128, 256]: the scalar kernels of the fp32
-// path on bf16 tensors (correct, far from the matrix-core rate).
-hipError_t launch_bwd_bf16_scalar(const Problem &p, const uint16_t *dO, const uint16_t *Q,
-                                  const uint16_t *K, const uint16_t *V, const uint16_t *O,
-                                  const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
-                                  void *ws);
+// bf16 backward for head dims in (128, 256] on the matrix cores (column
+// halves of the gradients, S and dP rebuilt over the full depth by each).
+hipError_t launch_bwd_bf16_wide(const Problem &p, const uint16_t *dO, const uint16_t *Q,
+                                const uint16_t *K, const uint16_t *V, const uint16_t *O,
+                                const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
+                                void *workspace);
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,
                           const float *V, const float *O, const float *LSE, float *dQ,
                           float *dK, float *dV, void *workspace);

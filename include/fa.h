@@ -42,10 +42,11 @@
  *     the cost is that of the padded width); fa_fwd, fa_fwd_f32 and
  *     fa_bwd_f32, fa_bwd and fa_decode also take 128 < d <= 256 (fa_fwd:
  *     256-deep scores, O computed in two column halves that each recompute
- *     the scores, so 1.5x the contraction work; fa_bwd: scalar fp32 kernels
- *     on the bf16 tensors, correct but far slower than the matrix-core
- *     path); the backward phase, dropout and FP8 entry points stay at
- *     d <= 128 and return FA_ERR_HEADDIM past it;
+ *     the scores, so 1.5x the contraction work; fa_bwd: dQ, dK, dV in
+ *     column halves that each rebuild S and dP, 2.2x the contraction work,
+ *     on a plainer schedule than the 128-wide kernels); the backward phase,
+ *     dropout and FP8 entry points stay at d <= 128 and return
+ *     FA_ERR_HEADDIM past it;
  *     N * d < 2^30; scale finite and > 0; causal is 0 or 1.
  *   - stream is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously on it; argument checks happen synchronously, before any

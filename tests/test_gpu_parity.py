@@ -197,8 +197,8 @@ def test_full_size_run_to_run_bitwise():
 
 def test_other_paths_run_to_run_bitwise():
     """Decode (d = 128 and 256), the FP8 forward, the dropout forward and
-    backward and the head-dim-256 forward, each three times on the same
-    sharp inputs (Q and K x 2): every output bit for bit the same."""
+    backward and the head-dim-256 forward and backward, each three times on
+    the same sharp inputs (Q and K x 2): every output bit for bit the same."""
     import exact_io_aware_attention_amd as fa
     g = torch.Generator(device="cuda")
     g.manual_seed(77)
@@ -255,14 +255,17 @@ def test_other_paths_run_to_run_bitwise():
     same("fp8", fp8)
 
     Qw, Kw, Vw = rnd(B, H, N, 256, mult=2.0), rnd(B, H, N, 256, mult=2.0), rnd(B, H, N, 256)
+    dOw = rnd(B, H, N, 256)
+    wsw = fa.new_workspace(B, H, N, 256)
 
     def wide():
-        O = torch.empty_like(Qw)
+        O, dQ, dK, dV = (torch.empty_like(Qw) for _ in range(4))
         L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         fa.fa_fwd(Qw, Kw, Vw, O, L, 256 ** -0.5, causal=True)
+        fa.fa_bwd(dOw, Qw, Kw, Vw, O, L, dQ, dK, dV, 256 ** -0.5, causal=True, workspace=wsw)
         torch.cuda.synchronize()
-        return O, L
-    same("forward d=256", wide)
+        return O, L, dQ, dK, dV
+    same("forward and backward d=256", wide)
 
 
 def _bits(t):
