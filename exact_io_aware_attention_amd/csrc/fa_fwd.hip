@@ -96,16 +96,19 @@ constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated wi
 // splits the columns of O over DK / DV workgroups per query block, each
 // recomputing the scores: the head dim then grows past what one workgroup's
 // registers hold for O. 256-deep rows run one wave per SIMD (4 waves, 512
-// registers each, the part past 256 in AGPRs) instead of two.
-template <int DK>
+// registers each, the part past 256 in AGPRs) instead of two; so do
+// block-sparse masks, so that a workgroup's 128 rows are one mask row and it
+// loads exactly the key tiles that row keeps (256 rows would load the union
+// of two rows' tiles and mask out, wave by wave, what each row drops).
+template <int DK, bool SPARSE>
 constexpr int fwd_waves()
 {
-    return DK > 128 ? 4 : 8;
+    return DK > 128 || SPARSE ? 4 : 8;
 }
 template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ void __launch_bounds__(64 * fwd_waves<DK>(), 1) fwd_bf16_kernel(FwdParams p)
+__global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_kernel(FwdParams p)
 {
-    constexpr int W = fwd_waves<DK>();  // waves
+    constexpr int W = fwd_waves<DK, SPARSE>();  // waves
     constexpr int RW = 32;          // query rows per wave
     constexpr int BR = RW * W;      // query rows per workgroup
     constexpr int BC = 64;          // keys per LDS tile
@@ -578,12 +581,12 @@ template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
 {
     FwdParams fp = fp0;
-    constexpr int BR = 32 * fwd_waves<DK>();  // query rows per workgroup
+    constexpr int BR = 32 * fwd_waves<DK, SPARSE>();  // query rows per workgroup
     fp.nqb = (pr.N + BR - 1) / BR;
     fp.items = pr.B * pr.H * fp.nqb * (DK / DV);
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
-    hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(64 * fwd_waves<DK>()), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(64 * fwd_waves<DK, SPARSE>()), 0,
                        pr.stream, fp);
     return hipGetLastError();
 }
