@@ -333,33 +333,24 @@ __device__ __forceinline__ float halves_sum(float x)
 
 // Wait states between an MFMA's write of an accumulator and the first read of
 // it by inline asm (the row maxima below read freshly computed scores): the
-// ISA requires 12 after v_mfma_f32_32x32x16_bf16 and 20 after
-// v_mfma_scale_f32_32x32x64_f8f6f4 before a vector ALU instruction reads the
+// ISA requires 12 after v_mfma_f32_32x32x16_bf16 (20 after the fp8
+// v_mfma_scale_f32_32x32x64_f8f6f4) before a vector ALU instruction reads the
 // result. The compiler inserts them before its own instructions but does not
 // look inside asm, so an asm reader it places right behind the MFMA would
-// read the registers' previous contents. Tying the accumulator through this
-// statement orders every later read after the wait.
-__device__ __forceinline__ void mfma_result_wait_bf16(f32x16 &x)
-{
-    asm volatile("s_nop 11" : "+v"(x));
-}
-// The same ordering without a fixed wait, for an asm chain that starts at one
-// register of a single MFMA's accumulator: a compiler-visible add of +0 (not
-// an identity for -0, so it is kept) before which the compiler inserts just
-// the wait states its own schedule still needs; the chain's first asm reads
-// the result, and every register of the accumulator is written by then.
+// read the registers' previous contents. An asm chain that starts at one
+// register of an accumulator therefore first passes that register through a
+// compiler-visible add of +0 (not an identity for -0, so it is kept): the
+// compiler inserts before it just the wait states its own schedule still
+// needs, the chain's first asm reads its result, and every register of the
+// accumulator is written by then.
 __device__ __forceinline__ void mfma_result_touch(f32x16 &x, int i)
 {
     x[i] += 0.f;
 }
-__device__ __forceinline__ void mfma_result_wait_fp8(f32x16 &x, f32x16 &y)
-{
-    asm volatile("s_nop 15\n\ts_nop 3" : "+v"(x), "+v"(y));
-}
 
 // Max of three scores without the NaN-quieting copies fmaxf brings in IEEE
 // mode (no operand here is ever NaN; -inf is an ordinary value). An operand
-// fresh from an MFMA must have passed mfma_result_wait_* first.
+// fresh from an MFMA must have passed mfma_result_touch first.
 __device__ __forceinline__ float vmax3(float a, float b, float c)
 {
     float y;

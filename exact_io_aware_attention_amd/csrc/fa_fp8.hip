@@ -226,7 +226,10 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                         s[blk][r] = -INFINITY;
                 }
         }
-        mfma_result_wait_fp8(s[0], s[1]);
+        // the asm max chain first reads s[0][0], then s[1][0] (two MFMA
+        // accumulators): both pass through a compiler-visible add first
+        mfma_result_touch(s[0], 0);
+        mfma_result_touch(s[1], 0);
         float mx = vmax3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
         for (int r = 3; r < 16; ++r)
