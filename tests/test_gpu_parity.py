@@ -197,8 +197,9 @@ def test_full_size_run_to_run_bitwise():
 
 def test_other_paths_run_to_run_bitwise():
     """Decode (d = 128 and 256), the FP8 forward, the dropout forward and
-    backward and the head-dim-256 forward and backward, each three times on
-    the same sharp inputs (Q and K x 2): every output bit for bit the same."""
+    backward, the head-dim-256 forward and backward and the 64-wide kernels
+    (dense causal, block-sparse), each three times on the same sharp inputs
+    (Q and K x 2): every output bit for bit the same."""
     import exact_io_aware_attention_amd as fa
     g = torch.Generator(device="cuda")
     g.manual_seed(77)
@@ -266,6 +267,26 @@ def test_other_paths_run_to_run_bitwise():
         torch.cuda.synchronize()
         return O, L, dQ, dK, dV
     same("forward and backward d=256", wide)
+
+    # the 64-wide kernels, dense causal and block-sparse (the latter's
+    # forward runs 4 waves on one mask row)
+    N64 = 4096
+    Q6, K6, V6, dO6 = (rnd(2, 4, N64, 64, mult=m) for m in (2.0, 2.0, 1.0, 1.0))
+    ws6 = fa.new_workspace(2, 4, N64, 64)
+    nb = N64 // 128
+    rng = np.random.Generator(np.random.PCG64(5))
+    m6 = (rng.random((nb, nb)) < 0.2).astype(np.uint8)
+    np.fill_diagonal(m6, 1)
+    M6 = torch.from_numpy(m6).to("cuda")
+    for causal, M in ((True, None), (False, M6)):
+        def run64():
+            O, dQ, dK, dV = (torch.empty_like(Q6) for _ in range(4))
+            L = torch.empty((2, 4, N64), dtype=torch.float32, device="cuda")
+            fa.fa_fwd(Q6, K6, V6, O, L, 0.125, causal=causal, blockmask=M)
+            fa.fa_bwd(dO6, Q6, K6, V6, O, L, dQ, dK, dV, 0.125, causal=causal, blockmask=M, workspace=ws6)
+            torch.cuda.synchronize()
+            return O, L, dQ, dK, dV
+        same(f"d=64 causal={causal} sparse={M is not None}", run64)
 
 
 def _bits(t):
