@@ -170,6 +170,10 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     }
     const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
     const float nDi = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
+    f32x16 ndv;  // dP^T accumulates from -D (this lane's row)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        ndv[r] = nDi;
 
     f32x16 dq[WDB];
 #pragma unroll
@@ -206,14 +210,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int kr = 32 * h;  // tile rows (keys) of this step
-            f32x16 s = f32x16{}, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dp[r] = nDi;
+            f32x16 s = f32x16{}, dp = ndv;
 #pragma unroll
             for (int kk = 0; kk < WKK; ++kk) {
                 s = mfma32x32x16(wide_rows(ks, kr, kk, l32, hi), qf[kk], s);
-                dp = mfma32x32x16(wide_rows(vs, kr, kk, l32, hi), gf[kk], dp);
+                dp = mfma32x32x16(wide_rows(vs, kr, kk, l32, hi), gf[kk], kk == 0 ? ndv : dp);
             }
             // register r: key t * 64 + kr + 8 (r / 4) + 4 hi + r % 4
             f32x16 ds;
@@ -323,11 +324,19 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int qr = 32 * h;  // tile rows (queries) of this step
-            f32x16 s = f32x16{}, dp;
-            // register r: query t * 64 + qr + 8 (r / 4) + 4 hi + r % 4
+            // register r: query t * 64 + qr + 8 (r / 4) + 4 hi + r % 4, so
+            // registers 4 j .. 4 j + 3 are 4 consecutive queries
+            f32x16 s = f32x16{}, dp, lq;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dp[r] = ns[qr + 8 * (r / 4) + 4 * hi + (r % 4)];
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 nv = *reinterpret_cast<const f32x4 *>(ns + qr + 8 * j + 4 * hi);
+                const f32x4 lv = *reinterpret_cast<const f32x4 *>(ls + qr + 8 * j + 4 * hi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dp[4 * j + e] = nv[e];
+                    lq[4 * j + e] = lv[e];
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < WKK; ++kk) {
                 s = mfma32x32x16(wide_rows(qs, qr, kk, l32, hi), kf[kk], s);
@@ -338,7 +347,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
             for (int r = 0; r < 16; ++r) {
                 const int qi = qr + 8 * (r / 4) + 4 * hi + (r % 4);
                 const int q = t * WBT + qi;
-                float pe = exp2_fast(fmaf(s[r], p.c, -ls[qi]));
+                float pe = exp2_fast(fmaf(s[r], p.c, -lq[r]));
                 if (q >= N || (CAUSAL && key > q))
                     pe = 0.f;
                 pm[r] = pe;
