@@ -119,6 +119,52 @@ def test_config4_sampled_rows_and_memory():
     gu.check_outputs("bf16", {"O": Og, "LSE": Lg}, {"O": Or, "LSE": Lr}, fields=("O", "LSE"))
 
 
+def test_no_device_allocation_in_any_entry_point():
+    """Every entry point works in caller-owned memory: with the workspaces
+    passed in, a call moves neither torch's allocator nor the device's free
+    memory (the library allocates nothing)."""
+    import exact_io_aware_attention_amd as fa
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    B, H, N = 1, 4, 3000
+
+    def rnd(*shape):
+        return torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+
+    calls = []
+    for d in (128, 256):
+        Q, K, V, dO = (rnd(B, H, N, d) for _ in range(4))
+        O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+        L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        ws = fa.new_workspace(B, H, N, d)
+        calls.append((f"fa_fwd d={d}", lambda Q=Q, K=K, V=V, O=O, L=L, d=d:
+                      fa.fa_fwd(Q, K, V, O, L, d ** -0.5, causal=True)))
+        calls.append((f"fa_bwd d={d}", lambda Q=Q, K=K, V=V, O=O, L=L, dO=dO, dQ=dQ, dK=dK, dV=dV, ws=ws, d=d:
+                      fa.fa_bwd(dO, Q, K, V, O, L, dQ, dK, dV, d ** -0.5, causal=True, workspace=ws)))
+        Qd, Od = rnd(B, H, 2, d), torch.empty((B, H, 2, d), dtype=torch.bfloat16, device="cuda")
+        Ld = torch.empty((B, H, 2), dtype=torch.float32, device="cuda")
+        wsd = torch.empty(fa.fa_decode_workspace_bytes(B, H, 2, N, d), dtype=torch.uint8, device="cuda")
+        calls.append((f"fa_decode d={d}", lambda Qd=Qd, K=K, V=V, Od=Od, Ld=Ld, wsd=wsd, d=d:
+                      fa.fa_decode(Qd, K, V, Od, Ld, d ** -0.5, causal=True, workspace=wsd)))
+    Q, K, V, dO = (rnd(B, H, N, 128) for _ in range(4))
+    O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+    L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ws = fa.new_workspace(B, H, N, 128)
+    calls.append(("fa_fwd_dropout", lambda: fa.fa_fwd_dropout(Q, K, V, O, L, 128 ** -0.5, 0.1, 5, causal=True)))
+    calls.append(("fa_bwd_dropout", lambda: fa.fa_bwd_dropout(dO, Q, K, V, O, L, dQ, dK, dV, 128 ** -0.5, 0.1, 5,
+                                                               causal=True, workspace=ws)))
+    for name, call in calls:
+        call()  # first call: kernel code objects load here
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info()
+        alloc0 = torch.cuda.memory_allocated()
+        call()
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        assert torch.cuda.memory_allocated() == alloc0, name
+        assert free0 == free1, (name, free0, free1)
+
+
 EDGE = [
     # (B, H, N, d, causal, sparse)
     (1, 1, 1, 64, False, False),
