@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--wide-steps", type=int, default=10,
                     help="timed calls of the supplementary head-dim-256 forward run (0: skip)")
     ap.add_argument("--wide-bwd", type=int, default=1,
-                    help="also time one head-dim-256 backward (0: skip)")
+                    help="timed calls of the supplementary head-dim-256 backward (0: skip)")
     return ap.parse_args()
 
 
@@ -368,19 +368,20 @@ def main():
                 "mfma_work_factor": 1.5, "steps": args.wide_steps}
         if args.wide_bwd:
             # the backward at d = 256 (column halves that each rebuild S and
-            # dP, a plain double-buffered schedule): one warm-up, one timed call
+            # dP): one warm-up call, then the median of --wide-bwd timed calls
             dOw = torch.randn(shp, generator=g, device=dev).to(torch.bfloat16)
             dQw, dKw, dVw = (torch.empty_like(Qw) for _ in range(3))
             wsw = fa.new_workspace(cfg.B, cfg.H, cfg.N, 256, dev)
             fa.fa_bwd(dOw, Qw, Kw, Vw, Ow, LSE, dQw, dKw, dVw, sw, causal=causal, workspace=wsw)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fa.fa_bwd(dOw, Qw, Kw, Vw, Ow, LSE, dQw, dKw, dVw, sw, causal=causal, workspace=wsw)
-            e1.record()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.wide_bwd)]
+            for e in ev:
+                e[0].record()
+                fa.fa_bwd(dOw, Qw, Kw, Vw, Ow, LSE, dQw, dKw, dVw, sw, causal=causal, workspace=wsw)
+                e[1].record()
             torch.cuda.synchronize()
-            b_s = e0.elapsed_time(e1) * 1e-3
+            b_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
             wide.update(bwd_ms=round(b_s * 1e3, 2), bwd_tflops=round(2.5 * wflops / b_s / 1e12, 3),
-                        bwd_mfma_work_factor=2.2)
+                        bwd_mfma_work_factor=2.2, bwd_steps=args.wide_bwd)
             del dOw, dQw, dKw, dVw, wsw
         del Qw, Kw, Vw, Ow
 
