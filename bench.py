@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=24)
     ap.add_argument("--supp-steps", type=int, default=10,
                     help="timed steps of the supplementary non-causal run (0: skip)")
     ap.add_argument("--decode-steps", type=int, default=10,
@@ -394,9 +394,12 @@ def main():
     if args.cpu_heads > 0:
         import oracle
         nh = min(args.cpu_heads, cfg.B * cfg.H)
-        sl = (slice(0, 1), slice(0, nh))
+        # the first nh (batch, head) pairs, as one batch of nh heads
+
+        def heads(x):
+            return x.reshape((1, cfg.B * cfg.H) + x.shape[2:])[:, :nh]
         t1 = time.perf_counter()
-        oracle.attention(q[sl], k[sl], v[sl], scale, causal=causal, blockmask=mask, do=do[sl])
+        oracle.attention(heads(q), heads(k), heads(v), scale, causal=causal, blockmask=mask, do=heads(do))
         cpu_s = time.perf_counter() - t1
         head_flops = (fwd_flops + bwd_flops) / (cfg.B * cfg.H)
         cpu = {"value": round(nh * head_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
