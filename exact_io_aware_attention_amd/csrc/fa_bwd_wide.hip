@@ -46,7 +46,8 @@ struct WideParams {
     int nblk;   // 128-row blocks per head
     int ntile;  // 64-row tiles per head
     int nmb;    // mask blocks per mask row
-    int items;  // B * H * nblk * 2
+    int items;    // B * H * nblk * 2: (block, column half), halves adjacent
+    int per_xcd;  // items per XCD (xcd_work_item)
     float c, scale;
 };
 
@@ -144,7 +145,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
     const uint32_t lds0 = lds_byte_addr(smem);
 
-    const int item0 = blockIdx.x;
+    const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
     const int item = item0 / 2, half = item0 % 2;
@@ -255,7 +256,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB + 4 * WBT * 4];
     const uint32_t lds0 = lds_byte_addr(smem);
 
-    const int item0 = blockIdx.x;
+    const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
     const int item = item0 / 2, half = item0 % 2;
@@ -383,11 +384,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
 template <bool CAUSAL, bool SPARSE>
 hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE>), dim3(wp.items), dim3(WW * kWave), 0, stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0, stream,
+                       wp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE>), dim3(wp.items), dim3(WW * kWave), 0, stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+                       stream, wp);
     return hipGetLastError();
 }
 
@@ -419,6 +422,7 @@ hipError_t launch_bwd_bf16_wide(const Problem &pr, const uint16_t *dO, const uin
     wp.ntile = (pr.N + WBT - 1) / WBT;
     wp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
     wp.items = pr.B * pr.H * wp.nblk * 2;
+    wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
     wp.c = pr.scale * kLog2e;
     wp.scale = pr.scale;
     const bool sparse = pr.mask != nullptr;
