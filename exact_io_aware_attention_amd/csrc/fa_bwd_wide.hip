@@ -21,7 +21,10 @@
 // preprocessing kernel. LDS tiles (512-byte rows, 16-byte chunks
 // XOR-swizzled) are double-buffered: the next tile streams in by direct
 // global->LDS loads while the current one is computed, one barrier per tile.
-// A plain schedule, far from the pipelined 128-wide kernels.
+// A plain schedule, far from the pipelined 128-wide kernels. Work items
+// (block, half), the two halves of a block adjacent, are dealt so that each
+// XCD takes one contiguous range of them: a head's blocks then share that
+// XCD's L2, which reads their K/V (or Q/dO) tiles once for all of them.
 #include "fa_common.h"
 #include "fa_internal.h"
 
