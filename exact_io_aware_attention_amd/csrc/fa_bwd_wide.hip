@@ -211,16 +211,19 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
             issue(tn, buf ^ 1);
         const uint16_t *ks = reinterpret_cast<const uint16_t *>(smem + (2 * buf) * TB);
         const uint16_t *vs = reinterpret_cast<const uint16_t *>(smem + (2 * buf + 1) * TB);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kr = 32 * h;  // tile rows (keys) of this step
-            f32x16 s = f32x16{}, dp = ndv;
+        // The tile's two steps of 32 keys (tile rows kr..): S^T and dP^T
+        // (MFMA), dS^T (vector ALU), dQ^T += K^T dS^T (MFMA). The second
+        // step's S^T and dP^T are issued before the first step's dS^T, so
+        // that the vector work runs beside independent MFMAs.
+        auto scores = [&](int kr, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
 #pragma unroll
             for (int kk = 0; kk < WKK; ++kk) {
-                s = mfma32x32x16(wide_rows(ks, kr, kk, l32, hi), qf[kk], s);
+                s = mfma32x32x16(wide_rows(ks, kr, kk, l32, hi), qf[kk], kk == 0 ? f32x16{} : s);
                 dp = mfma32x32x16(wide_rows(vs, kr, kk, l32, hi), gf[kk], kk == 0 ? ndv : dp);
             }
-            // register r: key t * 64 + kr + 8 (r / 4) + 4 hi + r % 4
+        };
+        // register r: key t * 64 + kr + 8 (r / 4) + 4 hi + r % 4
+        auto dscores = [&](int kr, const f32x16 &s, const f32x16 &dp) __attribute__((always_inline)) {
             f32x16 ds;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -230,6 +233,9 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
                     pe = 0.f;
                 ds[r] = pe * dp[r];
             }
+            return ds;
+        };
+        auto update = [&](int kr, const f32x16 &ds) __attribute__((always_inline)) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 sb = pack_bf16x8(ds, hh);
@@ -237,7 +243,12 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
                 for (int db = 0; db < WDB; ++db)
                     dq[db] = mfma32x32x16(tr.read(ks, kr + 16 * hh, 128 * half + 32 * db), sb, dq[db]);
             }
-        }
+        };
+        f32x16 s0, dp0, s1, dp1;
+        scores(0, s0, dp0);
+        scores(32, s1, dp1);
+        update(0, dscores(0, s0, dp0));
+        update(32, dscores(32, s1, dp1));
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
