@@ -23,6 +23,10 @@ Functions carry the C names:
 Tensors are contiguous CUDA (HIP) tensors of shape [B, H, N, d]: bfloat16 for
 fa_fwd / fa_bwd, float32 for the _f32 entry points; LSE is float32 [B, H, N];
 blockmask is uint8 [ceil(N/128), ceil(N/128)] on the same device, or None.
+Every tensor (LSE, blockmask and workspaces included) must be a contiguous
+device tensor on Q's device; a workspace must hold at least the bytes its
+*_workspace_bytes function returns. These checks raise ValueError before any
+launch.
 fa_decode takes Q, O of shape [B, H, Nq, d] and K, V of shape [B, H, Nk, d]
 (bfloat16), LSE float32 [B, H, Nq].
 """
@@ -94,8 +98,8 @@ _lib.fa_version.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 
 # Symbols declared in include/fa.h (checked by the ABI test).
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_f32",
-            "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout",
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv",
+            "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout",
             "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
             "fa_status_str", "fa_last_hip_error", "fa_version")
 
@@ -140,25 +144,43 @@ def _shape(q):
 
 
 def _require(ts, dtype, shape):
+    dev0 = ts[0].device
     for t in ts:
-        if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"expected contiguous {dtype} device tensors of shape {shape}")
+        if (t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda
+                or t.device != dev0):
+            raise ValueError(f"expected contiguous {dtype} tensors of shape {shape} on one device")
 
 
-def _require_lse(lse, shape):
+def _on(t, device):
+    """Whether t lives on `device` (the device of the main tensors)."""
+    return t.is_cuda and t.device == device
+
+
+def _require_lse(lse, shape, device):
     import torch
     B, H, N, _ = shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError(f"LSE must be contiguous float32 of shape {(B, H, N)}")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()
+            or not _on(lse, device)):
+        raise ValueError(f"LSE must be a contiguous float32 tensor of shape {(B, H, N)} on {device}")
 
 
-def _require_mask(mask, N):
+def _require_mask(mask, N, device):
     import torch
     if mask is None:
         return
     nb = (N + FA_MASK_BLOCK - 1) // FA_MASK_BLOCK
-    if mask.dtype != torch.uint8 or tuple(mask.shape) != (nb, nb) or not mask.is_contiguous():
-        raise ValueError(f"blockmask must be contiguous uint8 of shape {(nb, nb)}")
+    if (mask.dtype != torch.uint8 or tuple(mask.shape) != (nb, nb) or not mask.is_contiguous()
+            or not _on(mask, device)):
+        raise ValueError(f"blockmask must be a contiguous uint8 tensor of shape {(nb, nb)} on {device}")
+
+
+def _require_ws(ws, need, device):
+    """A caller's workspace: contiguous, on `device`, at least `need` bytes.
+    Returns its size in bytes."""
+    nbytes = ws.numel() * ws.element_size()
+    if not ws.is_contiguous() or not _on(ws, device) or nbytes < need:
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on {device}")
+    return nbytes
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -168,32 +190,33 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 def _fwd(fn, dtype, Q, K, V, O, LSE, scale, causal, blockmask, stream):
     shape = _shape(Q)
     _require((Q, K, V, O), dtype, shape)
-    _require_lse(LSE, shape)
-    _require_mask(blockmask, shape[2])
+    _require_lse(LSE, shape, Q.device)
+    _require_mask(blockmask, shape[2], Q.device)
     B, H, N, d = shape
     _check(fn(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, N, d, float(scale),
               int(bool(causal)), _ptr(blockmask), _stream_ptr(stream)))
 
 
-def _workspace(shape, workspace, device):
+def _workspace(need, workspace, device):
+    """The caller's workspace after its checks, or a new one of `need` bytes;
+    returns (tensor, bytes)."""
     import torch
-    need = fa_bwd_workspace_bytes(*shape)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    return workspace
+    return workspace, _require_ws(workspace, need, device)
 
 
 def _bwd(fn, dtype, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal, blockmask, workspace,
          stream):
     shape = _shape(Q)
     _require((dO, Q, K, V, O, dQ, dK, dV), dtype, shape)
-    _require_lse(LSE, shape)
-    _require_mask(blockmask, shape[2])
-    ws = _workspace(shape, workspace, Q.device)
+    _require_lse(LSE, shape, Q.device)
+    _require_mask(blockmask, shape[2], Q.device)
+    ws, nbytes = _workspace(fa_bwd_workspace_bytes(*shape), workspace, Q.device)
     B, H, N, d = shape
     _check(fn(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(dQ), _ptr(dK),
               _ptr(dV), B, H, N, d, float(scale), int(bool(causal)), _ptr(blockmask),
-              _ptr(ws), ws.numel() * ws.element_size(), _stream_ptr(stream)))
+              _ptr(ws), nbytes, _stream_ptr(stream)))
 
 
 def fa_fwd(Q, K, V, O, LSE, scale, causal=False, blockmask=None, stream=None):
@@ -228,21 +251,23 @@ def fa_bwd_prep(dO, O, LSE, workspace, stream=None):
     """Backward phase 1: D and LSE*log2(e) into the workspace."""
     shape = _shape(dO)
     _require((dO, O), torch.bfloat16, shape)
-    _require_lse(LSE, shape)
+    _require_lse(LSE, shape, dO.device)
+    nbytes = _require_ws(workspace, fa_bwd_workspace_bytes(*shape), dO.device)
     B, H, N, d = shape
     _check(_lib.fa_bwd_prep(_ptr(dO), _ptr(O), _ptr(LSE), B, H, N, d, _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+                            nbytes, _stream_ptr(stream)))
 
 
 def fa_bwd_dq(dO, Q, K, V, dQ, scale, workspace, causal=False, blockmask=None, stream=None):
     """Backward phase 2: dQ (needs fa_bwd_prep's workspace)."""
     shape = _shape(Q)
     _require((dO, Q, K, V, dQ), torch.bfloat16, shape)
-    _require_mask(blockmask, shape[2])
+    _require_mask(blockmask, shape[2], Q.device)
+    nbytes = _require_ws(workspace, fa_bwd_workspace_bytes(*shape), Q.device)
     B, H, N, d = shape
     _check(_lib.fa_bwd_dq(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(dQ), B, H, N, d,
                           float(scale), int(bool(causal)), _ptr(blockmask), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+                          nbytes, _stream_ptr(stream)))
 
 
 def fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, workspace, causal=False, blockmask=None,
@@ -250,12 +275,12 @@ def fa_bwd_dkdv(dO, Q, K, V, dK, dV, scale, workspace, causal=False, blockmask=N
     """Backward phase 3: dK and dV (needs fa_bwd_prep's workspace)."""
     shape = _shape(Q)
     _require((dO, Q, K, V, dK, dV), torch.bfloat16, shape)
-    _require_mask(blockmask, shape[2])
+    _require_mask(blockmask, shape[2], Q.device)
+    nbytes = _require_ws(workspace, fa_bwd_workspace_bytes(*shape), Q.device)
     B, H, N, d = shape
     _check(_lib.fa_bwd_dkdv(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(dK), _ptr(dV), B, H, N,
                             d, float(scale), int(bool(causal)), _ptr(blockmask),
-                            _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            _stream_ptr(stream)))
+                            _ptr(workspace), nbytes, _stream_ptr(stream)))
 
 
 def new_workspace(B, H, N, d, device="cuda"):
@@ -277,15 +302,15 @@ def fa_decode(Q, K, V, O, LSE, scale, causal=False, workspace=None, stream=None)
         raise ValueError("Q [B, H, Nq, d] and K, V [B, H, Nk, d] must agree on B, H, d")
     _require((Q, O), torch.bfloat16, qs)
     _require((K, V), torch.bfloat16, ks)
-    _require_lse(LSE, qs)
+    if K.device != Q.device or V.device != Q.device:
+        raise ValueError("Q, K, V, O must be on one device")
+    _require_lse(LSE, qs, Q.device)
     B, H, Nq, d = qs
     Nk = ks[2]
-    if workspace is None:
-        workspace = torch.empty(max(fa_decode_workspace_bytes(B, H, Nq, Nk, d), 1),
-                                dtype=torch.uint8, device=Q.device)
+    workspace, nbytes = _workspace(fa_decode_workspace_bytes(B, H, Nq, Nk, d), workspace, Q.device)
     _check(_lib.fa_decode(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, Nq, Nk, d,
-                          float(scale), int(bool(causal)), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+                          float(scale), int(bool(causal)), _ptr(workspace), nbytes,
+                          _stream_ptr(stream)))
 
 
 def fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=False, blockmask=None,
@@ -294,8 +319,8 @@ def fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=False, blockmask
     import torch
     shape = _shape(Q)
     _require((Q, K, V, O), torch.bfloat16, shape)
-    _require_lse(LSE, shape)
-    _require_mask(blockmask, shape[2])
+    _require_lse(LSE, shape, Q.device)
+    _require_mask(blockmask, shape[2], Q.device)
     B, H, N, d = shape
     _check(_lib.fa_fwd_dropout(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H, N, d,
                                float(scale), int(bool(causal)), _ptr(blockmask), float(p_drop),
@@ -308,14 +333,14 @@ def fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=
     import torch
     shape = _shape(Q)
     _require((dO, Q, K, V, O, dQ, dK, dV), torch.bfloat16, shape)
-    _require_lse(LSE, shape)
-    _require_mask(blockmask, shape[2])
-    ws = _workspace(shape, workspace, Q.device)
+    _require_lse(LSE, shape, Q.device)
+    _require_mask(blockmask, shape[2], Q.device)
+    ws, nbytes = _workspace(fa_bwd_workspace_bytes(*shape), workspace, Q.device)
     B, H, N, d = shape
     _check(_lib.fa_bwd_dropout(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(dQ),
                                _ptr(dK), _ptr(dV), B, H, N, d, float(scale), int(bool(causal)),
-                               _ptr(blockmask), float(p_drop), int(seed), _ptr(ws),
-                               ws.numel() * ws.element_size(), _stream_ptr(stream)))
+                               _ptr(blockmask), float(p_drop), int(seed), _ptr(ws), nbytes,
+                               _stream_ptr(stream)))
 
 
 def fa_fwd_fp8_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -330,12 +355,11 @@ def fa_fwd_fp8(Q8, K8, V8, O, LSE, scale, q_descale, k_descale, v_descale, causa
     shape = _shape(Q8)
     _require((Q8, K8, V8), torch.uint8, shape)
     _require((O,), torch.bfloat16, shape)
-    _require_lse(LSE, shape)
+    if any(t.device != Q8.device for t in (K8, V8, O)):
+        raise ValueError("Q8, K8, V8, O must be on one device")
+    _require_lse(LSE, shape, Q8.device)
     B, H, N, d = shape
-    if workspace is None:
-        workspace = torch.empty(max(fa_fwd_fp8_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
-                                device=Q8.device)
+    workspace, nbytes = _workspace(fa_fwd_fp8_workspace_bytes(B, H, N, d), workspace, Q8.device)
     _check(_lib.fa_fwd_fp8(_ptr(Q8), _ptr(K8), _ptr(V8), _ptr(O), _ptr(LSE), B, H, N, d,
                            float(scale), float(q_descale), float(k_descale), float(v_descale),
-                           int(bool(causal)), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+                           int(bool(causal)), _ptr(workspace), nbytes, _stream_ptr(stream)))

@@ -410,6 +410,44 @@ def test_empty_problem_is_a_no_op():
     torch.cuda.synchronize()
 
 
+def test_binding_rejects_host_side_buffers():
+    """LSE, the block mask and every workspace must be device tensors on the
+    main tensors' device: a host tensor raises ValueError in the binding
+    before any launch (a host pointer reaching a kernel would fault)."""
+    import exact_io_aware_attention_amd as fa
+    B, H, N, d = 1, 2, 256, 64
+    Q = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    O, dQ, dK, dV = (torch.empty_like(Q) for _ in range(4))
+    LSE = torch.zeros((B, H, N), dtype=torch.float32, device="cuda")
+    M = torch.ones((2, 2), dtype=torch.uint8, device="cuda")
+    ws = fa.new_workspace(B, H, N, d)
+    cpu_lse, cpu_mask, cpu_ws = LSE.cpu(), M.cpu(), ws.cpu()
+    small_ws = ws[:16]
+    calls = [
+        lambda: fa.fa_fwd(Q, Q, Q, O, cpu_lse, 0.125),
+        lambda: fa.fa_fwd(Q, Q, Q, O, LSE, 0.125, blockmask=cpu_mask),
+        lambda: fa.fa_bwd(Q, Q, Q, Q, O, cpu_lse, dQ, dK, dV, 0.125),
+        lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, blockmask=cpu_mask),
+        lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, workspace=cpu_ws),
+        lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, workspace=small_ws),
+        lambda: fa.fa_bwd_prep(Q, O, LSE, cpu_ws),
+        lambda: fa.fa_bwd_prep(Q, O, cpu_lse, ws),
+        lambda: fa.fa_bwd_dq(Q, Q, Q, Q, dQ, 0.125, cpu_ws),
+        lambda: fa.fa_bwd_dkdv(Q, Q, Q, Q, dK, dV, 0.125, ws, blockmask=cpu_mask),
+        lambda: fa.fa_bwd_dkdv(Q, Q, Q, Q, dK, dV, 0.125, small_ws),
+        lambda: fa.fa_fwd_dropout(Q, Q, Q, O, cpu_lse, 0.125, 0.1, 1),
+        lambda: fa.fa_bwd_dropout(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, 0.1, 1, workspace=cpu_ws),
+        lambda: fa.fa_decode(Q, Q, Q, O, cpu_lse, 0.125),
+        lambda: fa.fa_decode(Q, Q, Q, O, LSE, 0.125, workspace=cpu_ws),
+        lambda: fa.fa_fwd(Q, Q.cpu(), Q, O, LSE, 0.125),
+    ]
+    for i, c in enumerate(calls):
+        with pytest.raises(ValueError):
+            c()
+            print(f"call {i} did not raise", flush=True)
+    torch.cuda.synchronize()
+
+
 HEAD_DIMS = [
     # (B, H, N, d, causal, sparse): head dims other than 64 and 128 run in the
     # 64- or 128-wide kernels with the columns past d zero-padded
