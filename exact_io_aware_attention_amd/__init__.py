@@ -11,6 +11,9 @@ Functions carry the C names:
            blockmask=None, workspace=None, stream=None)
     fa_fwd_f32(...), fa_bwd_f32(...)  -- the fp32 debug path, same arguments
     fa_bwd_workspace_bytes(B, H, N, d)
+    fa_bwd_noalloc(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False,
+                   blockmask=None, stream=None)  -- scratch in the library's static
+                   device array (FA_NOALLOC_SCRATCH_BYTES per GPU), no workspace
     fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=False, blockmask=None,
                    stream=None)
     fa_bwd_dropout(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, p_drop, seed, causal=False,
@@ -49,8 +52,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 FA_OK = 0
 FA_MASK_BLOCK = 128
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa.h
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM",
-                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP"}
+                4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
+                8: "FA_ERR_SCRATCH"}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -66,6 +71,9 @@ _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                         _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
 _lib.fa_bwd_f32.restype = _i
 _lib.fa_bwd_f32.argtypes = _lib.fa_bwd.argtypes
+_lib.fa_bwd_noalloc.restype = _i
+_lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _i, _i, _i, _i, _f, _i, _vp, _vp]
 _lib.fa_bwd_prep.restype = _i
 _lib.fa_bwd_prep.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd_dq.restype = _i
@@ -98,7 +106,7 @@ _lib.fa_version.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
 
 # Symbols declared in include/fa.h (checked by the ABI test).
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv",
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_prep", "fa_bwd_dq", "fa_bwd_dkdv",
             "fa_fwd_f32", "fa_bwd_f32", "fa_bwd_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout",
             "fa_fwd_fp8", "fa_fwd_fp8_workspace_bytes", "fa_decode", "fa_decode_workspace_bytes",
             "fa_status_str", "fa_last_hip_error", "fa_version")
@@ -245,6 +253,21 @@ def fa_bwd_f32(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False, blockmask=N
     import torch
     _bwd(_lib.fa_bwd_f32, torch.float32, dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal,
          blockmask, workspace, stream)
+
+
+def fa_bwd_noalloc(dO, Q, K, V, O, LSE, dQ, dK, dV, scale, causal=False, blockmask=None,
+                   stream=None):
+    """Backward, bf16, with its scratch in the library's static device array
+    instead of a workspace (allocates nothing): writes dQ, dK, dV in place.
+    Calls on one GPU must not overlap in time (they share that array)."""
+    shape = _shape(Q)
+    _require((dO, Q, K, V, O, dQ, dK, dV), torch.bfloat16, shape)
+    _require_lse(LSE, shape, Q.device)
+    _require_mask(blockmask, shape[2], Q.device)
+    B, H, N, d = shape
+    _check(_lib.fa_bwd_noalloc(_ptr(dO), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(dQ),
+                               _ptr(dK), _ptr(dV), B, H, N, d, float(scale), int(bool(causal)),
+                               _ptr(blockmask), _stream_ptr(stream)))
 
 
 def fa_bwd_prep(dO, O, LSE, workspace, stream=None):

@@ -223,6 +223,33 @@ fa_status fa_bwd(const void *dO, const void *Q, const void *K, const void *V, co
         blockmask, workspace, workspace_bytes, stream, false, kMaxDWide);
 }
 
+fa_status fa_bwd_noalloc(const void *dO, const void *Q, const void *K, const void *V,
+                         const void *O, const float *LSE, void *dQ, void *dK, void *dV, int B,
+                         int H, int N, int d, float scale, int causal, const uint8_t *blockmask,
+                         void *stream)
+{
+    bool empty = false;
+    fa_status st = check_common(B, H, N, d, scale, causal, &empty, kMaxDWide);
+    if (st != FA_OK || empty)
+        return st;
+    st = check_ptrs({dO, Q, K, V, O, LSE, dQ, dK, dV});
+    if (st != FA_OK)
+        return st;
+    const size_t need = fa::bwd_workspace_layout(B, H, N, d).bytes;
+    if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_SCRATCH;
+    void *scratch = nullptr;
+    st = hip_status(fa::noalloc_scratch(need, &scratch));
+    if (st != FA_OK)
+        return st;
+    const fa::Problem p = make_problem(B, H, N, d, scale, causal, blockmask, stream);
+    return hip_status(fa::launch_bwd_bf16(
+        p, static_cast<const uint16_t *>(dO), static_cast<const uint16_t *>(Q),
+        static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V),
+        static_cast<const uint16_t *>(O), LSE, static_cast<uint16_t *>(dQ),
+        static_cast<uint16_t *>(dK), static_cast<uint16_t *>(dV), scratch));
+}
+
 fa_status fa_bwd_prep(const void *dO, const void *O, const float *LSE, int B, int H, int N, int d,
                       void *workspace, size_t workspace_bytes, void *stream)
 {
@@ -416,6 +443,9 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal 0 or 1, dropout probability in [0, 1)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP error";
+    case FA_ERR_SCRATCH:
+        return "problem needs more backward scratch than the no-allocation entry point's static "
+               "array holds (FA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

@@ -90,6 +90,11 @@ hipError_t launch_bwd_bf16_wide(const Problem &p, const uint16_t *dO, const uint
                                 const uint16_t *K, const uint16_t *V, const uint16_t *O,
                                 const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                                 void *workspace);
+// Device address of the static scratch array of the no-allocation backward
+// on the current device (looked up once per device); hipErrorInvalidValue if
+// `bytes` exceeds its size.
+hipError_t noalloc_scratch(size_t bytes, void **out);
+
 hipError_t launch_bwd_f32(const Problem &p, const float *dO, const float *Q, const float *K,
                           const float *V, const float *O, const float *LSE, float *dQ,
                           float *dK, float *dV, void *workspace);

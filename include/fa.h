@@ -53,11 +53,13 @@
  *     HIP call, and a failed check enqueues nothing.
  *   - Ownership: the caller owns every buffer. The library allocates and
  *     frees no device or host memory; backward scratch is passed in as
- *     `workspace`.
+ *     `workspace` (fa_bwd_noalloc instead uses a static device array of the
+ *     library, see there).
  *   - Errors are returned as fa_status; no exception crosses the ABI. After
  *     FA_ERR_HIP, fa_last_hip_error() describes the failure (thread-local).
  *   - Entry points keep no state between calls and may be called from
- *     several host threads on different streams.
+ *     several host threads on different streams (except fa_bwd_noalloc,
+ *     whose calls on one GPU share its static scratch array).
  */
 #ifndef FA_H
 #define FA_H
@@ -78,7 +80,9 @@ typedef enum {
     FA_ERR_SCALE = 5,     /* scale not finite or not > 0, causal not 0/1, or a
                              dropout probability outside [0, 1) */
     FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_bwd_workspace_bytes */
-    FA_ERR_HIP = 7        /* a HIP call failed; see fa_last_hip_error() */
+    FA_ERR_HIP = 7,       /* a HIP call failed; see fa_last_hip_error() */
+    FA_ERR_SCRATCH = 8    /* fa_bwd_noalloc: the problem needs more scratch than
+                             FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 #define FA_MASK_BLOCK 128
@@ -123,6 +127,27 @@ fa_status fa_bwd_dkdv(const void *dO, const void *Q, const void *K, const void *
                       void *dK, void *dV, int B, int H, int N, int d, float scale, int causal,
                       const uint8_t *blockmask, const void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* Size of the static device scratch array fa_bwd_noalloc uses (per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation). The backward's scratch (two floats per row) lives
+ * in a static device array of the library, FA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends; this call
+ * itself allocates nothing. Limit: fa_bwd_workspace_bytes(B, H, N, d) <=
+ * FA_NOALLOC_SCRATCH_BYTES (B*H*N up to about 2 million rows), else
+ * FA_ERR_SCRATCH before any HIP call. The array belongs to the GPU current on
+ * the calling host thread, which must be the GPU of the tensors and the
+ * stream. Every call on one GPU shares that GPU's array: calls must not
+ * overlap in time on one GPU (different streams or host threads race on
+ * it); calls ordered on one stream are safe, since each call rewrites every
+ * entry it reads. Other arguments, results and errors as fa_bwd. */
+fa_status fa_bwd_noalloc(const void *dO, const void *Q, const void *K, const void *V,
+                         const void *O, const float *LSE, void *dQ, void *dK, void *dV,
+                         int B, int H, int N, int d, float scale, int causal,
+                         const uint8_t *blockmask, void *stream);
 
 /* Forward with dropout on P (lukebest.github.io FlashAttention, "Kernel
  * fusion", lists dropout among the fused steps; the drawing rule is this

@@ -98,6 +98,37 @@ def test_backward_validation():
     assert _bwd(B=0, dO=None) == 0
 
 
+def test_noalloc_backward_validation():
+    """The no-allocation backward checks like fa_bwd (without a workspace)
+    and refuses, before any HIP call, a problem whose scratch exceeds its
+    static array."""
+    lib = fa.lib()
+
+    def call(**kw):
+        a = dict(dO=P, Q=P, K=P, V=P, O=P, LSE=P, dQ=P, dK=P, dV=P, B=1, H=1, N=128, d=64,
+                 scale=0.125, causal=0)
+        a.update(kw)
+        return lib.fa_bwd_noalloc(a["dO"], a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dQ"],
+                                  a["dK"], a["dV"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                                  a["causal"], None, None)
+
+    assert call(dK=None) == 1
+    assert call(d=33) == 3
+    assert call(d=264) == 3
+    assert call(LSE=MIS) == 4
+    assert call(scale=float("inf")) == 5
+    assert call(B=0, dO=None) == 0
+    # the largest problem whose two scratch vectors fit, and one row more
+    rows_max = fa.FA_NOALLOC_SCRATCH_BYTES // 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, rows_max, 8) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_bwd_workspace_bytes(1, 1, rows_max + 1, 8) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert call(N=rows_max + 1, d=8) == 8
+    assert call(B=4, H=8, N=rows_max // 16, d=8) == 8
+    assert "FA_NOALLOC_SCRATCH_BYTES" in lib.fa_status_str(8).decode()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
+
+
 def test_backward_phases_head_dims():
     """The phase entry points run only the matrix-core kernels (d <= 128)."""
     lib = fa.lib()
@@ -126,7 +157,7 @@ def test_workspace_bytes():
 
 def test_status_strings():
     lib = fa.lib()
-    for s in range(8):
+    for s in range(9):
         assert lib.fa_status_str(s)
     assert lib.fa_last_hip_error() is not None
     assert fa.version().startswith("fa-gfx950")

@@ -430,6 +430,7 @@ def test_binding_rejects_host_side_buffers():
         lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, blockmask=cpu_mask),
         lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, workspace=cpu_ws),
         lambda: fa.fa_bwd(Q, Q, Q, Q, O, LSE, dQ, dK, dV, 0.125, workspace=small_ws),
+        lambda: fa.fa_bwd_noalloc(Q, Q, Q, Q, O, cpu_lse, dQ, dK, dV, 0.125),
         lambda: fa.fa_bwd_prep(Q, O, LSE, cpu_ws),
         lambda: fa.fa_bwd_prep(Q, O, cpu_lse, ws),
         lambda: fa.fa_bwd_dq(Q, Q, Q, Q, dQ, 0.125, cpu_ws),
