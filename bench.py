@@ -16,9 +16,13 @@ Prints ONE JSON line. Options: --steps K --warmup W --config {1..5}
 --supp-steps S (the same shape without the causal mask) --dropout-steps S (the
 same workload with dropout p=0.1) --decode-steps S (the split-KV decode path on
 its own workload, HBM-bound) --fp8-steps S (the FP8 forward on the same
-shape) --wide-steps S (the forward at head dim 256 on the same B, H, N). The
-supplementary runs
-are reported beside the headline and never enter `value`.
+shape) --wide-steps S / --wide-bwd S (the forward and backward at head dim
+256 on the same B, H, N) --other-steps S (the GPT-2-shaped, 64K dense and
+block-sparse workloads) --sweep-steps S (the block-sparse shape at six mask
+densities, with a linear fit of time against kept blocks) --cpu-other 0|1
+(the CPU reference also on samples of the other workloads) --only LIST (run
+only these supplementary legs). The supplementary runs are reported beside
+the headline and never enter `value`.
 """
 import argparse
 import json
@@ -55,8 +59,18 @@ def parse():
                     help="timed calls of the supplementary FP8 forward run (0: skip)")
     ap.add_argument("--wide-steps", type=int, default=10,
                     help="timed calls of the supplementary head-dim-256 forward run (0: skip)")
-    ap.add_argument("--wide-bwd", type=int, default=1,
+    ap.add_argument("--wide-bwd", type=int, default=5,
                     help="timed calls of the supplementary head-dim-256 backward (0: skip)")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed steps of each of the other workloads (GPT-2 shape, 64K dense "
+                         "forward, block-sparse) (0: skip)")
+    ap.add_argument("--sweep-steps", type=int, default=3,
+                    help="timed steps per density of the block-sparse density sweep (0: skip)")
+    ap.add_argument("--cpu-other", type=int, default=1,
+                    help="also time the CPU reference on samples of the other workloads (0: skip)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of supplementary runs to do after the headline "
+                         "(supp,dropout,fp8,wide,decode,other,sweep); empty: all")
     return ap.parse_args()
 
 
@@ -154,6 +168,148 @@ def decode_run(steps, d=None):
     return out
 
 
+# Densities of the block-sparse sweep: the band |I - J| <= 1 plus this fraction
+# of the other 128 x 128 blocks (the block-sparse workload itself keeps 10%).
+SWEEP_KEEP = (0.01, 0.04, 0.10, 0.23, 0.49, 1.0)
+
+
+def workload_run(cfg, steps, mask=None, seed=None):
+    """fa_fwd, and when the workload has a backward fa_bwd's three kernels, on
+    cfg's shape with seeded N(0,1) bf16 inputs drawn on the device (Q and K
+    times cfg.qk_mult); per-kernel HIP-event averages over `steps` calls
+    after one warm-up. mask: a numpy block mask or None."""
+    import torch
+    import exact_io_aware_attention_amd as fa
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.cfg_id if seed is None else seed)
+    shp = (cfg.B, cfg.H, cfg.N, cfg.d)
+    Q, K, V, dO = (torch.randn(shp, generator=g, device=dev).mul_(m).to(torch.bfloat16)
+                   for m in (cfg.qk_mult, cfg.qk_mult, 1.0, 1.0))
+    M = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).to(dev)
+    O = torch.empty_like(Q)
+    LSE = torch.empty(shp[:3], dtype=torch.float32, device=dev)
+    bwd = cfg.has_bwd
+    if bwd:
+        dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
+        ws = fa.new_workspace(*shp, dev)
+    sc, causal = cfg.scale, cfg.causal
+
+    def run(ev=None):
+        ev and ev[0].record()
+        fa.fa_fwd(Q, K, V, O, LSE, sc, causal=causal, blockmask=M)
+        ev and ev[1].record()
+        if bwd:
+            fa.fa_bwd_prep(dO, O, LSE, ws)
+            ev and ev[2].record()
+            fa.fa_bwd_dq(dO, Q, K, V, dQ, sc, ws, causal=causal, blockmask=M)
+            ev and ev[3].record()
+            fa.fa_bwd_dkdv(dO, Q, K, V, dK, dV, sc, ws, causal=causal, blockmask=M)
+            ev and ev[4].record()
+
+    run()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    n_ev = 5 if bwd else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    names = ["fwd", "bwd_prep", "bwd_dq", "bwd_dkdv"][:n_ev - 1]
+    us = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps * 1e3 for j, n in enumerate(names)}
+    fwd_f, bwd_f = flop_counts(cfg, mask)
+    out = {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+           "causal": cfg.causal, "qk_mult": cfg.qk_mult,
+           "density": None if mask is None else round(float(mask.mean()), 5),
+           "fwd_us": round(us["fwd"], 2), "fwd_flop": fwd_f,
+           "fwd_tflops": round(fwd_f / us["fwd"] / 1e6, 2),
+           "fwd_frac_of_peak": round(fwd_f / us["fwd"] / 1e6 / PEAK_BF16_TFLOPS, 4),
+           "device_bytes_allocated_during_calls": int(extra), "steps": steps}
+    if bwd:
+        b_us = us["bwd_prep"] + us["bwd_dq"] + us["bwd_dkdv"]
+        out.update(bwd_us=round(b_us, 2), bwd_flop=bwd_f,
+                   bwd_kernels_us={n: round(us[n], 2) for n in names[1:]},
+                   bwd_tflops=round(bwd_f / b_us / 1e6, 2),
+                   bwd_frac_of_peak=round(bwd_f / b_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                   dkdv_tflops=round(0.8 * bwd_f / us["bwd_dkdv"] / 1e6, 2))
+    del Q, K, V, dO, O, LSE
+    if bwd:
+        del dQ, dK, dV, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def sparse_sweep(cfg, steps):
+    """The block-sparse workload's shape at several mask densities (the band
+    plus a growing fraction of the other blocks): forward and backward time
+    against kept blocks, with a least-squares line t = a + b * kept and its
+    largest relative residual."""
+    import synthetic as syn
+    nb = (cfg.N + 127) // 128
+    rows = []
+    for f in SWEEP_KEEP:
+        mask = syn.block_mask(nb, keep_frac=f)
+        r = workload_run(cfg, steps, mask=mask)
+        rows.append({"keep_frac_off_band": f, "kept_blocks": int(mask.sum()),
+                     "density": r["density"], "fwd_us": r["fwd_us"], "bwd_us": r["bwd_us"],
+                     "fwd_tflops": r["fwd_tflops"], "bwd_tflops": r["bwd_tflops"]})
+    kept = np.array([r["kept_blocks"] for r in rows], float)
+    fit = {}
+    for key in ("fwd_us", "bwd_us"):
+        t = np.array([r[key] for r in rows], float)
+        b, a = np.polyfit(kept, t, 1)
+        res = np.max(np.abs(t - (a + b * kept)) / t)
+        fit[key] = {"intercept_us": round(float(a), 2), "us_per_kept_block": round(float(b), 5),
+                    "max_rel_residual": round(float(res), 4)}
+    return {"workload": cfg.name + " shape, mask density sweep (supplementary)",
+            "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "points": rows,
+            "linear_fit": fit, "steps": steps}
+
+
+def cpu_other(args):
+    """The CPU reference (as is) on samples of the other workloads, on the
+    same host threads: workloads 1 and 2 in full (fwd+bwd), two heads of the
+    block-sparse workload (fwd+bwd), and the 256 sampled query rows of the
+    64K dense forward with a labelled extrapolation to all of its rows.
+    Rates use the same algorithmic FLOP counts as the GPU figures."""
+    import oracle
+    import synthetic as syn
+    out = {}
+    for cid in (1, 2):
+        cfg = syn.CONFIGS[cid]
+        q, k, v, do, mask = syn.config_inputs(cfg)
+        t1 = time.perf_counter()
+        oracle.attention(q, k, v, cfg.scale, causal=cfg.causal, blockmask=mask, do=do)
+        dt = time.perf_counter() - t1
+        f, b = flop_counts(cfg, mask)
+        out[cfg.name] = {"s": round(dt, 3), "tflops": round((f + b) / dt / 1e12, 6),
+                         "sample": "all heads, fwd+bwd"}
+    cfg = syn.CONFIGS[5]
+    q, k, v, do, mask = syn.config_inputs(cfg)
+    nh = 2
+    hs = lambda x: x.reshape((1, cfg.B * cfg.H) + x.shape[2:])[:, :nh]  # noqa: E731
+    t1 = time.perf_counter()
+    oracle.attention(hs(q), hs(k), hs(v), cfg.scale, causal=cfg.causal, blockmask=mask, do=hs(do))
+    dt = time.perf_counter() - t1
+    f, b = flop_counts(cfg, mask)
+    out[cfg.name] = {"s": round(dt, 3), "tflops": round(nh * (f + b) / (cfg.B * cfg.H) / dt / 1e12, 6),
+                     "sample": f"{nh} of {cfg.B * cfg.H} heads, fwd+bwd"}
+    cfg = syn.CONFIGS[4]
+    q, k, v, _, _ = syn.config_inputs(cfg)
+    rb, ri = syn.row_sample(cfg.B * cfg.H, cfg.N)
+    t1 = time.perf_counter()
+    oracle.attention_rows(q, k, v, cfg.scale, rb, ri, causal=cfg.causal)
+    dt = time.perf_counter() - t1
+    f, _ = flop_counts(cfg, None)
+    rows = cfg.B * cfg.H * cfg.N
+    out[cfg.name] = {"s": round(dt, 3), "tflops": round(f * len(rb) / rows / dt / 1e12, 6),
+                     "sample": f"{len(rb)} of {rows} query rows, fwd",
+                     "extrapolated_full_fwd_s": round(dt * rows / len(rb), 1)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +402,11 @@ def main():
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                # the whole forward, the whole backward (prep + dQ + dK/dV)
+                # and the whole step, each on its own algorithmic FLOPs
+                "fwd_frac": round(fwd_flops / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "bwd_frac": round(bwd_flops / bwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "step_frac": round(value / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(tag, symbols[dominant]),
                 "algorithmic_bytes": kernel_bytes[dominant]}
 
@@ -258,8 +419,10 @@ def main():
 
     # Supplementary: the same shape and inputs without the causal mask (twice
     # the work), forward and backward times only; never part of `value`.
+    only = set(x for x in args.only.split(",") if x)
+    want = lambda name: not only or name in only  # noqa: E731
     supp = None
-    if causal and mask is None and args.supp_steps > 0:
+    if causal and mask is None and args.supp_steps > 0 and want("supp"):
         def run_nc():
             fa.fa_fwd(Q, K, V, O, LSE, scale, causal=False)
             fa.fa_bwd_prep(dO, O, LSE, ws)
@@ -287,7 +450,7 @@ def main():
     # Supplementary: the same workload with dropout p = 0.1 on P (fa_fwd_dropout
     # + fa_bwd_dropout); never part of `value`.
     dropout = None
-    if args.dropout_steps > 0:
+    if args.dropout_steps > 0 and want("dropout"):
         p_drop, seed = 0.1, 1234
         def run_drop():
             fa.fa_fwd_dropout(Q, K, V, O, LSE, scale, p_drop, seed, causal=causal, blockmask=M)
@@ -316,7 +479,7 @@ def main():
     # Supplementary: the FP8 forward on the same shape (Q, K, V quantized to
     # E4M3 with per-tensor descales); never part of `value`.
     fp8 = None
-    if args.fp8_steps > 0 and cfg.d in (64, 128) and mask is None:
+    if args.fp8_steps > 0 and cfg.d in (64, 128) and mask is None and want("fp8"):
         def q8(t):
             amax = float(t.float().abs().max())
             ds = amax / 448.0
@@ -344,7 +507,7 @@ def main():
     # (fresh seeded N(0,1) inputs, Q and K scaled like the workload's);
     # never part of `value`.
     wide = None
-    if args.wide_steps > 0 and mask is None:
+    if args.wide_steps > 0 and mask is None and want("wide"):
         g = torch.Generator(device=dev)
         g.manual_seed(256)
         shp = (cfg.B, cfg.H, cfg.N, 256)
@@ -386,9 +549,23 @@ def main():
         del Qw, Kw, Vw, Ow
 
     decode = decode256 = None
-    if args.decode_steps > 0:
+    if args.decode_steps > 0 and want("decode"):
         decode = decode_run(args.decode_steps)
         decode256 = decode_run(args.decode_steps, d=256)
+
+    # Supplementary: the pages' other workloads (GPT-2-shaped attention, the
+    # 64K dense forward, block-sparse), each with its own algorithmic FLOPs
+    # and fraction of peak; never part of `value`.
+    other = None
+    if args.other_steps > 0 and want("other"):
+        other = []
+        for c in (2, 4, 5):
+            oc = syn.CONFIGS[c]
+            om = syn.block_mask((oc.N + 127) // 128) if oc.sparse else None
+            other.append(workload_run(oc, args.other_steps, mask=om))
+    sweep = None
+    if args.sweep_steps > 0 and want("sweep"):
+        sweep = sparse_sweep(syn.CONFIGS[5], args.sweep_steps)
 
     cpu = None
     if args.cpu_heads > 0:
@@ -406,6 +583,8 @@ def main():
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"{nh} of {cfg.B * cfg.H} heads of the same workload, fwd+bwd, "
                          f"fp64, {cpu_s:.1f} s"}
+        if args.cpu_other:
+            cpu["other_workloads"] = cpu_other(args)
 
     out = {
         "metric": METRIC,
@@ -438,6 +617,8 @@ def main():
         "wide_head": wide,
         "decode": decode,
         "decode_d256": decode256,
+        "other_workloads": other,
+        "sparse_density_sweep": sweep,
     }
     print(json.dumps(out), flush=True)
 
