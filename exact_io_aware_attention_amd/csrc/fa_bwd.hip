@@ -312,16 +312,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(DqParams p)
     int t_end = p.nkt;
     if (CAUSAL)
         t_end = min(p.nkt, (q0 + BR - 1) / BC + 1);
-    const int mrow = q0 / kMaskBlock;
-    auto tile_needed = [&](int t) __attribute__((always_inline)) -> bool {
-        return !SPARSE || p.mask[(size_t)mrow * p.nmb + (t * BC) / kMaskBlock] != 0;
-    };
+    // block-sparse: the kept key tiles of this workgroup's mask row
+    MaskCursor mc;
+    if (SPARSE)
+        mc.init(p.mask + (size_t)(q0 / kMaskBlock) * p.nmb, 1, p.nmb);
     auto next_tile = [&](int t) __attribute__((always_inline)) -> int {
-        ++t;
-        if (SPARSE)
-            while (t < t_end && !tile_needed(t))
-                ++t;
-        return t;
+        return SPARSE ? next_kept_tile(mc, t + 1, t_end, kMaskBlock / BC) : t + 1;
     };
 
     f32x16 dq[DB];
@@ -605,15 +601,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
     }
 
     const int t_begin = CAUSAL ? k0 / BQ : 0;
-    auto tile_needed = [&](int t) __attribute__((always_inline)) -> bool {
-        return !SPARSE || p.mask[(size_t)((t * BQ) / kMaskBlock) * p.nmb + kblk] != 0;
-    };
+    // block-sparse: the kept query tiles of this workgroup's mask column
+    MaskCursor mc;
+    if (SPARSE)
+        mc.init(p.mask + kblk, p.nmb, p.nmb);
     auto next_tile = [&](int t) __attribute__((always_inline)) -> int {
-        ++t;
-        if (SPARSE)
-            while (t < p.nqt && !tile_needed(t))
-                ++t;
-        return t;
+        return SPARSE ? next_kept_tile(mc, t + 1, p.nqt, kMaskBlock / BQ) : t + 1;
     };
     auto issue_tile = [&](int t, int b) __attribute__((always_inline)) {
         tl.load(Qh, lds0 + b * SLOT + Q_OFF, t * BQ, N, wave);
@@ -840,9 +833,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(DkvParams p)
             }
     };
 
-    int t = t_begin;
-    if (SPARSE && t < p.nqt && !tile_needed(t))
-        t = next_tile(t);
+    int t = next_tile(t_begin - 1);
     if (t < p.nqt) {
         issue_tile(t, 0);
 #pragma unroll

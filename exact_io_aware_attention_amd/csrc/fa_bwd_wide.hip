@@ -186,12 +186,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
 
     const int t_end = CAUSAL ? min(p.ntile, (q0 + WROWS - 1) / WBT + 1) : p.ntile;
     // key tiles the workgroup needs (one mask row, so uniform over it)
+    MaskCursor mc;
+    if (SPARSE)
+        mc.init(p.mask + (size_t)qb * p.nmb, 1, p.nmb);
     auto next_tile = [&](int t) -> int {
-        ++t;
-        if (SPARSE)
-            while (t < t_end && p.mask[(size_t)qb * p.nmb + (t * WBT) / kMaskBlock] == 0)
-                ++t;
-        return t;
+        return SPARSE ? next_kept_tile(mc, t + 1, t_end, kMaskBlock / WBT) : t + 1;
     };
     const WideDma dma(wave, lane, dh);
     auto issue = [&](int t, int buf) {
@@ -303,12 +302,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
 
     const int t_begin = CAUSAL ? k0 / WBT : 0;
     // query tiles the workgroup needs (one mask column, so uniform over it)
+    MaskCursor mc;
+    if (SPARSE)
+        mc.init(p.mask + kb, p.nmb, p.nmb);
     auto next_tile = [&](int t) -> int {
-        ++t;
-        if (SPARSE)
-            while (t < p.ntile && p.mask[(size_t)((t * WBT) / kMaskBlock) * p.nmb + kb] == 0)
-                ++t;
-        return t;
+        return SPARSE ? next_kept_tile(mc, t + 1, p.ntile, kMaskBlock / WBT) : t + 1;
     };
     const WideDma dma(wave, lane, dh);
     // rows past N read as zeros: their queries are masked below

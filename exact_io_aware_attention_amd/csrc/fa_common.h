@@ -379,6 +379,60 @@ __device__ __forceinline__ void sched_interleave()
     }
 }
 
+// Walks the kept blocks of one row (or column) of the block mask in order,
+// 64 blocks at a time: each lane of the wave reads one entry of a 64-block
+// window (entries `stride` bytes apart), one ballot turns the window into a
+// keep bitmask, and the next kept block is the lowest set bit at or after the
+// asked position. A window is read again only when the walk leaves it, so a
+// row of nb blocks costs ceil(nb / 64) parallel loads instead of one
+// dependent load per tile. The whole wave must call it with the same
+// arguments (the ballot needs every lane).
+struct MaskCursor {
+    const uint8_t *base;  // entry j at base[j * stride]
+    int stride, nb;
+    int w0;               // first block of the window in `bits`
+    uint64_t bits;        // keep bits of blocks w0 .. w0 + 63
+
+    __device__ __forceinline__ void init(const uint8_t *base_, int stride_, int nb_)
+    {
+        base = base_;
+        stride = stride_;
+        nb = nb_;
+        w0 = -(1 << 30);
+        bits = 0;
+    }
+    // Smallest kept block >= j, or nb when there is none.
+    __device__ __forceinline__ int next(int j)
+    {
+        while (j < nb) {
+            if (j < w0 || j >= w0 + 64) {
+                const int e = j + (int)(threadIdx.x % kWave);
+                const bool keep = e < nb && base[(size_t)e * stride] != 0;
+                bits = __ballot(keep);
+                w0 = j;
+            }
+            const uint64_t m = bits >> (j - w0);
+            if (m != 0)
+                return j + __builtin_ctzll(m);
+            j = w0 + 64;
+        }
+        return nb;
+    }
+};
+
+// First tile at or after t whose mask block is kept (tiles of kMaskBlock /
+// tpb rows, tpb tiles per mask block), or `end` when none is left before it.
+__device__ __forceinline__ int next_kept_tile(MaskCursor &mc, int t, int end, int tpb)
+{
+    if (t >= end)
+        return end;
+    const int b = t / tpb;
+    const int kb = mc.next(b);
+    if (kb != b)
+        t = kb * tpb;
+    return t < end ? t : end;
+}
+
 // Maps a launched workgroup to a work item so that each XCD (workgroups are
 // dealt to the XCDs round-robin) receives one contiguous range of the work
 // list: items of one head then run on one XCD and share its L2.

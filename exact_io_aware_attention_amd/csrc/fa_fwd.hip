@@ -62,9 +62,10 @@
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
 // never loaded, and the per-element mask runs only on 32-key steps that
 // straddle the diagonal or the end of the sequence; block-sparse
-// (lukebest.github.io "Block-Sparse FlashAttention") -- key tiles whose
-// 128 x 128 mask block is zero for every wave of the workgroup are skipped
-// without being loaded. Rows past the end of the sequence read as zeros
+// (lukebest.github.io "Block-Sparse FlashAttention") -- a block-sparse
+// workgroup's 128 rows are one row of the 128 x 128 block mask, and key tiles
+// whose block that row drops are skipped without being loaded (the kept ones
+// come from a ballot over 64 mask entries at a time, not a walk tile by tile). Rows past the end of the sequence read as zeros
 // (the tile loads go through buffer resources that end at row N, so no load
 // leaves the tensor) and are always masked. Iterations that need no element
 // mask run in a loop of their own, without any mask arithmetic.
@@ -169,26 +170,16 @@ __global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_ke
     if (CAUSAL)
         t_end = min(p.nkt, (q0 + BR - 1) / BC + 1);
 
-    // Block-sparse: a key tile is loaded when any wave's mask row keeps it;
-    // a wave whose own mask row drops it masks the whole tile.
-    const int mr_lo = q0 / kMaskBlock;
-    const int mr_hi = min(q0 + BR - 1, N - 1) / kMaskBlock;
-    const int wmr = min(wr0, N - 1) / kMaskBlock;
-    auto tile_needed = [&](int t) -> bool {
-        if (!SPARSE)
-            return true;
-        const int kbk = (t * BC) / kMaskBlock;
-        bool keep = false;
-        for (int mr = mr_lo; mr <= mr_hi; ++mr)
-            keep |= p.mask[(size_t)mr * p.nmb + kbk] != 0;
-        return keep;
-    };
+    // Block-sparse: the workgroup's rows are one mask row, so a key tile is
+    // loaded exactly when that row keeps its block, and then for every wave;
+    // the kept tiles come from a cursor over the row.
+    static_assert(!SPARSE || BR == kMaskBlock, "one mask row per block-sparse workgroup");
+    static_assert(kMaskBlock % BC == 0, "tiles per mask block");
+    MaskCursor mc;
+    if (SPARSE)
+        mc.init(p.mask + (size_t)(q0 / kMaskBlock) * p.nmb, 1, p.nmb);
     auto next_tile = [&](int t) -> int {
-        ++t;
-        if (SPARSE)
-            while (t < t_end && !tile_needed(t))
-                ++t;
-        return t;
+        return SPARSE ? next_kept_tile(mc, t + 1, t_end, kMaskBlock / BC) : t + 1;
     };
 
     // Lane-dependent byte offsets, computed once. Direct loads: lane `lane`
@@ -272,16 +263,11 @@ __global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_ke
     }
 
     // Element mask of 32 keys starting at kbase: keys past the end of the
-    // sequence, keys above the diagonal (causal), or all of them when this
-    // wave's block-mask row drops the tile.
+    // sequence and keys above the diagonal (causal). (A visited tile of a
+    // block-sparse workgroup is kept for all of its rows.)
     auto mask_half = [&](int kbase, f32x16 &s) {
-        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
         const bool edge = (kbase + 32 > N) || (CAUSAL && kbase + 31 > wr0);
-        if (drop) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[r] = -INFINITY;
-        } else if (edge) {
+        if (edge) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kbase + 8 * (r / 4) + 4 * hi + (r % 4);
@@ -370,8 +356,7 @@ __global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_ke
     // Whether the keys the iteration of tile t masks (the second half of t,
     // the first half of the next tile) need the element mask.
     auto half_masked = [&](int kbase) __attribute__((always_inline)) -> bool {
-        const bool drop = SPARSE && p.mask[(size_t)wmr * p.nmb + kbase / kMaskBlock] == 0;
-        return drop || (kbase + 32 > N) || (CAUSAL && kbase + 31 > wr0);
+        return (kbase + 32 > N) || (CAUSAL && kbase + 31 > wr0);
     };
     auto tile_masked = [&]() __attribute__((always_inline)) -> bool {
         return half_masked(t * BC + 32) || (t1 < t_end && half_masked(t1 * BC));
