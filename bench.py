@@ -396,7 +396,10 @@ def main():
     # kernel template arguments: head width (the forward's: score depth and
     # O column width), causal, block-sparse, dropout
     flags = f"{cfg.d}, {tf(cfg.causal)}, {tf(mask is not None)}, false"
-    symbols = {"fwd": f"fwd_bf16_kernel<{cfg.d}, {flags}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
+    # the forward's waves per workgroup: 4 for block-sparse masks and for
+    # problems with fewer 256-row blocks than two per CU, else 8
+    fwd_w = 4 if mask is not None or cfg.B * cfg.H * -(-cfg.N // 256) < 512 else 8
+    symbols = {"fwd": f"fwd_bf16_kernel<{cfg.d}, {flags}, {fwd_w}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
                "bwd_dq": f"bwd_dq_kernel<{flags}>", "bwd_dkdv": f"bwd_dkdv_kernel<{flags}>"}
     tag = f"{cfg.name.replace('-', '_')}_b{cfg.B}h{cfg.H}n{cfg.N}d{cfg.d}"
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),

@@ -96,20 +96,17 @@ constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated wi
 // width of the slice of V and O columns one workgroup computes. DV < DK
 // splits the columns of O over DK / DV workgroups per query block, each
 // recomputing the scores: the head dim then grows past what one workgroup's
-// registers hold for O. 256-deep rows run one wave per SIMD (4 waves, 512
-// registers each, the part past 256 in AGPRs) instead of two; so do
-// block-sparse masks, so that a workgroup's 128 rows are one mask row and it
-// loads exactly the key tiles that row keeps (256 rows would load the union
-// of two rows' tiles and mask out, wave by wave, what each row drops).
-template <int DK, bool SPARSE>
-constexpr int fwd_waves()
+// registers hold for O. W: waves per workgroup (32 query rows each). 8 (two
+// per SIMD) by default; 4 (one per SIMD) for 256-deep rows (512 registers
+// each, the part past 256 in AGPRs), for block-sparse masks (so that a
+// workgroup's 128 rows are one mask row and it loads exactly the key tiles
+// that row keeps; 256 rows would load the union of two rows' tiles and mask
+// out, wave by wave, what each row drops), and for problems too small to
+// give every CU two 256-row workgroups (twice as many workgroups, and at
+// d = 64 three fit a CU at once).
+template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP, int W>
+__global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
 {
-    return DK > 128 || SPARSE ? 4 : 8;
-}
-template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_kernel(FwdParams p)
-{
-    constexpr int W = fwd_waves<DK, SPARSE>();  // waves
     constexpr int RW = 32;          // query rows per wave
     constexpr int BR = RW * W;      // query rows per workgroup
     constexpr int BC = 64;          // keys per LDS tile
@@ -562,18 +559,36 @@ __global__ void __launch_bounds__((64 * fwd_waves<DK, SPARSE>()), 1) fwd_bf16_ke
     }
 }
 
-template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
-static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp0)
+template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP, int W>
+static hipError_t launch_fwd_w(const Problem &pr, const FwdParams &fp0)
 {
     FwdParams fp = fp0;
-    constexpr int BR = 32 * fwd_waves<DK, SPARSE>();  // query rows per workgroup
+    constexpr int BR = 32 * W;  // query rows per workgroup
     fp.nqb = (pr.N + BR - 1) / BR;
     fp.items = pr.B * pr.H * fp.nqb * (DK / DV);
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
-    hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP>), dim3(grid), dim3(64 * fwd_waves<DK, SPARSE>()), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP, W>), dim3(grid), dim3(64 * W), 0,
                        pr.stream, fp);
     return hipGetLastError();
+}
+
+constexpr int kCus = 256;  // MI355X compute units
+
+template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
+static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp)
+{
+    if constexpr (DK > 128 || SPARSE) {
+        return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 4>(pr, fp);
+    } else if constexpr (DROP) {
+        return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 8>(pr, fp);
+    } else {
+        // fewer 256-row blocks than two per CU: 128-row workgroups
+        const long blocks256 = (long)pr.B * pr.H * ((pr.N + 255) / 256);
+        if (blocks256 < 2 * kCus)
+            return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 4>(pr, fp);
+        return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 8>(pr, fp);
+    }
 }
 
 template <int DK, int DV, bool DROP>
