@@ -92,6 +92,18 @@ struct FwdParams {
 
 constexpr float kRescaleSlack = 8.f;  // log2 growth of the row max tolerated without rescale
 
+// acc + the sum of the 8 bf16 values in p, by dot products with (1, 1): the
+// row sum of the rounded weights that P V multiplies.
+__device__ __forceinline__ float bf16x8_sum_acc(bf16x8 p, float acc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+}
+
 // DK: width of the Q and K rows the kernel reads (the depth of Q K^T); DV:
 // width of the slice of V and O columns one workgroup computes. DV < DK
 // splits the columns of O over DK / DV workgroups per query block, each
@@ -278,7 +290,11 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         o[db] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    // Row sums against the reference max m: l of the fp32 weights (gives the
+    // LSE), lb of the bf16-rounded weights P V multiplies (divides O, so that
+    // a row dominated by one key gets that key's value row without the
+    // weight's rounding error). With dropout O is divided by l.
+    float m = -INFINITY, l = 0.f, lb = 0.f;
 
     const int t0 = next_tile(-1);
     if (t0 >= t_end) {
@@ -392,6 +408,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 thr = (m + kRescaleSlack) * inv_c;
                 nmref = (m == -INFINITY) ? 0.f : -m;
                 l *= alpha;
+                lb *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -464,6 +481,8 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
             l += ls0 + ls1;
             const bf16x8 p1 = pack_bf16x8(s_cur, 1);
+            if constexpr (!DROP)
+                lb = bf16x8_sum_acc(p1, bf16x8_sum_acc(p0, lb));
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
@@ -536,10 +555,12 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         run(std::true_type{});
     }
 
-    // Epilogue: O = O^T / l (transposed back per lane), LSE in natural log.
+    // Epilogue: O = O^T / lb (transposed back per lane), LSE from l in
+    // natural log.
     const float lt = halves_sum(l);
+    const float lbt = DROP ? lt : halves_sum(lb);
     if (row < N) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lbt > 0.f ? 1.f / lbt : 0.f;
         uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
