@@ -20,7 +20,12 @@ shape) --wide-steps S / --wide-bwd S (the forward and backward at head dim
 256 on the same B, H, N) --other-steps S (the GPT-2-shaped, 64K dense and
 block-sparse workloads) --sweep-steps S (the block-sparse shape at six mask
 densities, with a linear fit of time against kept blocks) --cpu-other 0|1
-(the CPU reference also on samples of the other workloads) --only LIST (run
+(the CPU reference also on samples of the other workloads) --padded-steps S
+(the headline B, H, N at head dims 64, 72, 96 and 128: dims between the
+kernel widths run zero-padded in the next one) --clock-seconds S (the
+headline step repeated for S seconds while the GPU's gfx clock and socket
+power are sampled through amdsmi: the clock the kernels actually run at
+under the board's power limit) --only LIST (run
 only these supplementary legs). The supplementary runs are reported beside
 the headline and never enter `value`.
 """
@@ -66,11 +71,17 @@ def parse():
                          "forward, block-sparse) (0: skip)")
     ap.add_argument("--sweep-steps", type=int, default=3,
                     help="timed steps per density of the block-sparse density sweep (0: skip)")
+    ap.add_argument("--padded-steps", type=int, default=3,
+                    help="timed steps at head dims 64, 72, 96, 128 on the headline B, H, N "
+                         "(0: skip)")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="seconds of repeated headline steps while the gfx clock and socket "
+                         "power are sampled (0: skip)")
     ap.add_argument("--cpu-other", type=int, default=1,
                     help="also time the CPU reference on samples of the other workloads (0: skip)")
     ap.add_argument("--only", default="",
                     help="comma-separated subset of supplementary runs to do after the headline "
-                         "(supp,dropout,fp8,wide,decode,other,sweep); empty: all")
+                         "(supp,dropout,fp8,wide,decode,other,sweep,padded,clock); empty: all")
     return ap.parse_args()
 
 
@@ -266,6 +277,67 @@ def sparse_sweep(cfg, steps):
     return {"workload": cfg.name + " shape, mask density sweep (supplementary)",
             "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "points": rows,
             "linear_fit": fit, "steps": steps}
+
+
+def clock_under_load(step, seconds):
+    """Repeats `step` (one headline step) for about `seconds` while a
+    thread samples the GPU's current gfx clock and socket power through
+    amdsmi every 50 ms; the first second (clock ramp) is dropped. Returns
+    medians and ranges, the steps' own rate over the sampled window, and
+    the bf16 MFMA peak scaled to the sampled clock (the published 2500
+    TFLOP/s is at the 2400 MHz peak engine clock); None when amdsmi is not
+    usable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # monitoring only: the bench goes on without it
+        return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                samples.append((time.perf_counter(), m.get("current_gfxclk"),
+                                m.get("current_socket_power")))
+            except Exception:
+                pass
+            stop.wait(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    marks = []
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        marks.append((time.perf_counter(), 20))
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    lo = t0 + 1.0
+    win = [s for s in samples if s[0] > lo]
+    clk = [s[1] for s in win if isinstance(s[1], (int, float))]
+    pw = [s[2] for s in win if isinstance(s[2], (int, float))]
+    done = [m for m in marks if m[0] > lo]
+    out = {"samples": len(clk), "seconds": round(time.perf_counter() - t0, 2)}
+    if clk:
+        med = statistics.median(clk)
+        out.update(gfxclk_mhz_median=med, gfxclk_mhz_min=min(clk), gfxclk_mhz_max=max(clk),
+                   bf16_peak_at_clock_tflops=round(PEAK_BF16_TFLOPS * med / 2400.0, 1))
+    if pw:
+        out.update(socket_power_w_median=statistics.median(pw), socket_power_w_max=max(pw))
+    if len(done) > 1:
+        span = done[-1][0] - done[0][0]
+        out["step_ms_in_window"] = round(span / sum(m[1] for m in done[1:]) * 1e3, 4)
+    return out
 
 
 def cpu_other(args):
@@ -570,6 +642,30 @@ def main():
     if args.sweep_steps > 0 and want("sweep"):
         sweep = sparse_sweep(syn.CONFIGS[5], args.sweep_steps)
 
+    # Supplementary: head dims between the kernel widths (64 and 128) run in
+    # the next wider kernel with zero-padded columns, so their algorithmic
+    # rate falls with d / width; measured on the headline B, H, N and mask.
+    padded = None
+    if args.padded_steps > 0 and mask is None and want("padded"):
+        from types import SimpleNamespace
+        padded = []
+        for dd in (64, 72, 96, 128):
+            pc = SimpleNamespace(name=f"{cfg.name} shape at d={dd}", cfg_id=cfg.cfg_id, B=cfg.B,
+                                 H=cfg.H, N=cfg.N, d=dd, qk_mult=cfg.qk_mult, causal=causal,
+                                 scale=dd ** -0.5, has_bwd=True)
+            r = workload_run(pc, args.padded_steps)
+            r["kernel_width"] = 64 if dd <= 64 else 128
+            padded.append(r)
+
+    clock = None
+    if args.clock_seconds > 0 and want("clock"):
+        clock = clock_under_load(step, args.clock_seconds)
+        if clock and "step_ms_in_window" in clock and "bf16_peak_at_clock_tflops" in clock:
+            # the step's algorithmic rate in that window against the peak at
+            # the sampled clock
+            rate = (fwd_flops + bwd_flops) / (clock["step_ms_in_window"] * 1e-3) / 1e12
+            clock["step_frac_of_peak_at_clock"] = round(rate / clock["bf16_peak_at_clock_tflops"], 4)
+
     cpu = None
     if args.cpu_heads > 0:
         import oracle
@@ -622,6 +718,8 @@ def main():
         "decode_d256": decode256,
         "other_workloads": other,
         "sparse_density_sweep": sweep,
+        "padded_head_dims": padded,
+        "clock_under_load": clock,
     }
     print(json.dumps(out), flush=True)
 
