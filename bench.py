@@ -81,7 +81,8 @@ def parse():
                     help="also time the CPU reference on samples of the other workloads (0: skip)")
     ap.add_argument("--only", default="",
                     help="comma-separated subset of supplementary runs to do after the headline "
-                         "(supp,dropout,fp8,wide,decode,other,sweep,padded,clock); empty: all")
+                         "(supp,dropout,fp8,wide,decode,other,sweep,padded,clock); empty: all; "
+                         "'headline': none")
     return ap.parse_args()
 
 
