@@ -293,7 +293,10 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // Row sums against the reference max m: l of the fp32 weights (gives the
     // LSE), lb of the bf16-rounded weights P V multiplies (divides O, so that
     // a row dominated by one key gets that key's value row without the
-    // weight's rounding error). With dropout O is divided by l.
+    // weight's rounding error). O is divided by l with dropout, and in the
+    // 64-deep instances, whose vector work bounds them: there the 8 extra
+    // dot products per 32 keys cost about 10%.
+    constexpr bool RSUM = DK >= 128 && !DROP;
     float m = -INFINITY, l = 0.f, lb = 0.f;
 
     const int t0 = next_tile(-1);
@@ -481,7 +484,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
             l += ls0 + ls1;
             const bf16x8 p1 = pack_bf16x8(s_cur, 1);
-            if constexpr (!DROP)
+            if constexpr (RSUM)
                 lb = bf16x8_sum_acc(p1, bf16x8_sum_acc(p0, lb));
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -558,7 +561,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // Epilogue: O = O^T / lb (transposed back per lane), LSE from l in
     // natural log.
     const float lt = halves_sum(l);
-    const float lbt = DROP ? lt : halves_sum(lb);
+    const float lbt = RSUM ? halves_sum(lb) : lt;
     if (row < N) {
         const float inv = lbt > 0.f ? 1.f / lbt : 0.f;
         uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
