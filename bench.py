@@ -620,7 +620,7 @@ def main():
             torch.cuda.synchronize()
             b_s = statistics.median([e[0].elapsed_time(e[1]) * 1e-3 for e in ev])
             wide.update(bwd_ms=round(b_s * 1e3, 2), bwd_tflops=round(2.5 * wflops / b_s / 1e12, 3),
-                        bwd_mfma_work_factor=2.2, bwd_steps=args.wide_bwd)
+                        bwd_mfma_work_factor=1.6, bwd_steps=args.wide_bwd)
             del dOw, dQw, dKw, dVw, wsw
         del Qw, Kw, Vw, Ow
 

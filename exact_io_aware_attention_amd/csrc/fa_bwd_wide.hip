@@ -4,27 +4,30 @@
 // §三.3): P = 2^(c s - lse2), dP = dO V^T, dS = P o (dP - D), dQ = scale dS K,
 // dK = scale dS^T Q, dV = P^T dO.
 //
-// At d = 256 the rows of Q, K, V, dO no longer fit a wave's registers beside
-// the accumulators of all 256 gradient columns, so each gradient is computed
-// in two column halves of 128 by two workgroups, both of which rebuild S and
-// dP over the full depth (the forward at 256 splits O the same way):
-//   - bwd_wide_dq_kernel: one workgroup per 128 query rows and dQ half; each
-//     wave holds 32 query rows of Q and dO as MFMA B operands; key/value
-//     tiles of 64 rows stream through LDS; S^T = K Q^T and dP^T = V dO^T
-//     (lane = query), dS^T by the vector ALU, dQ^T += K^T dS^T with K^T from
-//     LDS transpose reads;
-//   - bwd_wide_dkdv_kernel: one workgroup per 128 keys and dK/dV half; each
-//     wave holds 32 keys of K and V; query tiles of 64 rows (Q, dO, lse2, -D)
-//     stream through LDS; S = Q K^T and dP = dO V^T (lane = key),
-//     dV^T += dO^T P and dK^T += Q^T dS.
+// At d = 256 a wave holds 32 rows of two 256-wide operands (128 VGPRs) and
+// the accumulators of one 256-column gradient (128 AGPRs, asm MFMAs), but
+// not those of two:
+//   - bwd_wide_dq_kernel: one workgroup per 128 query rows; each wave holds
+//     32 query rows of Q and dO as MFMA B operands; key/value tiles of 64
+//     rows stream through LDS; S^T = K Q^T and dP^T = V dO^T (lane =
+//     query), dS^T by the vector ALU, dQ^T += K^T dS^T over all 256 columns
+//     with K^T from LDS transpose reads;
+//   - bwd_wide_dkdv_kernel: one workgroup per 128 keys; each wave holds 32
+//     keys of K (and V); query tiles of 64 rows (Q, dO, lse2, -D) stream
+//     through LDS; S = Q K^T (lane = key). dV and dK take a pass each (dV^T
+//     += dO^T P; then dP = dO V^T, dK^T += Q^T dS), so S is built twice:
+//     8 contractions of work against the method's 5. A split into column
+//     halves, each rebuilding S and dP (11), is kept as MODE 0 and the
+//     split dQ instance, selected at build time by FA_WIDE_SPLIT.
 // The D and lse2 rows come from the 256-wide instance of the backward's
 // preprocessing kernel. LDS tiles (512-byte rows, 16-byte chunks
 // XOR-swizzled) are double-buffered: the next tile streams in by direct
 // global->LDS loads while the current one is computed, one barrier per tile.
 // A plain schedule, far from the pipelined 128-wide kernels. Work items
-// (block, half), the two halves of a block adjacent, are dealt so that each
-// XCD takes one contiguous range of them: a head's blocks then share that
-// XCD's L2, which reads their K/V (or Q/dO) tiles once for all of them.
+// (blocks; in the split form (block, half) with the halves adjacent) are
+// dealt so that each XCD takes one contiguous range of them: a head's blocks
+// then share that XCD's L2, which reads their K/V (or Q/dO) tiles once for
+// all of them.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -140,9 +143,13 @@ __device__ __forceinline__ void wide_store(uint16_t *row_ptr, const f32x16 &acc,
     }
 }
 
-template <bool CAUSAL, bool SPARSE>
+template <bool CAUSAL, bool SPARSE, bool FULL>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p)
 {
+    // FULL: one workgroup per block computes all 256 dQ columns (its 8
+    // accumulators in AGPRs), so S^T and dP^T are built once; else one per
+    // (block, column half).
+    constexpr int NH = FULL ? 2 : 1;     // column halves per workgroup
     // two buffers of [K tile | V tile]
     constexpr uint32_t TB = WBT * WD * 2;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
@@ -151,7 +158,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
-    const int item = item0 / 2, half = item0 % 2;
+    const int item = FULL ? item0 : item0 / 2, half = FULL ? 0 : item0 % 2;
     const int bh = item / p.nblk;
     const int bi = item - bh * p.nblk;
     const int qb = CAUSAL ? p.nblk - 1 - bi : bi;  // causal: heaviest first
@@ -179,9 +186,9 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     for (int r = 0; r < 16; ++r)
         ndv[r] = nDi;
 
-    f32x16 dq[WDB];
+    f32x16 dq[NH * WDB];
 #pragma unroll
-    for (int db = 0; db < WDB; ++db)
+    for (int db = 0; db < NH * WDB; ++db)
         dq[db] = f32x16{};
 
     const int t_end = CAUSAL ? min(p.ntile, (q0 + WROWS - 1) / WBT + 1) : p.ntile;
@@ -239,8 +246,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 sb = pack_bf16x8(ds, hh);
 #pragma unroll
-                for (int db = 0; db < WDB; ++db)
-                    dq[db] = mfma32x32x16(tr.read(ks, kr + 16 * hh, 128 * half + 32 * db), sb, dq[db]);
+                for (int db = 0; db < NH * WDB; ++db) {
+                    const bf16x8 a = tr.read(ks, kr + 16 * hh, 128 * half + 32 * db);
+                    if constexpr (FULL)
+                        mfma_acc_agpr(dq[db], a, sb);
+                    else
+                        dq[db] = mfma32x32x16(a, sb, dq[db]);
+                }
             }
         };
         f32x16 s0, dp0, s1, dp1;
@@ -248,21 +260,37 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         scores(32, s1, dp1);
         update(0, dscores(0, s0, dp0));
         update(32, dscores(32, s1, dp1));
+        if constexpr (FULL)
+            mfma_drain();  // before the loop edge, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
     }
+    if constexpr (FULL) {
+        mfma_drain();
+#pragma unroll
+        for (int db = 0; db < NH * WDB; ++db)
+            mfma_settle(dq[db]);
+    }
     if (row < N) {
         uint16_t *out = p.dQ + head + (size_t)row * dh;
 #pragma unroll
-        for (int db = 0; db < WDB; ++db)
+        for (int db = 0; db < NH * WDB; ++db)
             wide_store(out, dq[db], 128 * half + 32 * db, hi, p.scale, dh);
     }
 }
 
-template <bool CAUSAL, bool SPARSE>
+// MODE 0: one workgroup per (key block, column half) computes that half of
+// dK and dV (S and dP rebuilt for each half). MODE 1: all 256 columns of dV
+// (S only); MODE 2: all 256 columns of dK (S and dP): the 256 accumulators
+// of both gradients do not fit beside the K and V rows, so the full-width
+// form takes two passes, 5 contractions of work against the split's 8.
+template <bool CAUSAL, bool SPARSE, int MODE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams p)
 {
+    constexpr bool FULL = MODE != 0;
+    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
+    constexpr int NH = FULL ? 2 : 1;
     // two buffers of [Q tile | dO tile], then lse2 and -D rows per buffer
     constexpr uint32_t TB = WBT * WD * 2;
     constexpr uint32_t VEC = 4 * TB;
@@ -272,7 +300,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
-    const int item = item0 / 2, half = item0 % 2;
+    const int item = FULL ? item0 : item0 / 2, half = FULL ? 0 : item0 % 2;
     const int bh = item / p.nblk;
     const int kb = item - bh * p.nblk;  // causal: low key blocks see the most queries
     const int k0 = kb * WROWS;
@@ -293,11 +321,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                     : bf16x8{};
     }
 
-    f32x16 dk[WDB], dv[WDB];
+    f32x16 dk[DO_DK ? NH * WDB : 1], dv[DO_DV ? NH * WDB : 1];
 #pragma unroll
-    for (int db = 0; db < WDB; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
+    for (int db = 0; db < NH * WDB; ++db) {
+        if (DO_DK)
+            dk[db] = f32x16{};
+        if (DO_DV)
+            dv[db] = f32x16{};
     }
 
     const int t_begin = CAUSAL ? k0 / WBT : 0;
@@ -353,7 +383,8 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
 #pragma unroll
             for (int kk = 0; kk < WKK; ++kk) {
                 s = mfma32x32x16(wide_rows(qs, qr, kk, l32, hi), kf[kk], s);
-                dp = mfma32x32x16(wide_rows(gs, qr, kk, l32, hi), vf[kk], dp);
+                if constexpr (DO_DK)
+                    dp = mfma32x32x16(wide_rows(gs, qr, kk, l32, hi), vf[kk], dp);
             }
             f32x16 pm, ds;
 #pragma unroll
@@ -364,44 +395,91 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 if (q >= N || (CAUSAL && key > q))
                     pe = 0.f;
                 pm[r] = pe;
-                ds[r] = pe * dp[r];
+                if constexpr (DO_DK)
+                    ds[r] = pe * dp[r];
             }
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 pb = pack_bf16x8(pm, hh);
-                const bf16x8 sb = pack_bf16x8(ds, hh);
+                const bf16x8 sb = DO_DK ? pack_bf16x8(ds, hh) : bf16x8{};
 #pragma unroll
-                for (int db = 0; db < WDB; ++db) {
+                for (int db = 0; db < NH * WDB; ++db) {
                     const int c0 = 128 * half + 32 * db;
-                    dv[db] = mfma32x32x16(tr.read(gs, qr + 16 * hh, c0), pb, dv[db]);
-                    dk[db] = mfma32x32x16(tr.read(qs, qr + 16 * hh, c0), sb, dk[db]);
+                    if constexpr (DO_DV) {
+                        const bf16x8 ga = tr.read(gs, qr + 16 * hh, c0);
+                        if constexpr (FULL)
+                            mfma_acc_agpr(dv[db], ga, pb);
+                        else
+                            dv[db] = mfma32x32x16(ga, pb, dv[db]);
+                    }
+                    if constexpr (DO_DK) {
+                        const bf16x8 qa = tr.read(qs, qr + 16 * hh, c0);
+                        if constexpr (FULL)
+                            mfma_acc_agpr(dk[db], qa, sb);
+                        else
+                            dk[db] = mfma32x32x16(qa, sb, dk[db]);
+                    }
                 }
             }
         }
+        if constexpr (FULL)
+            mfma_drain();  // before the loop edge, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
+    }
+    if constexpr (FULL) {
+        mfma_drain();
+#pragma unroll
+        for (int db = 0; db < NH * WDB; ++db) {
+            if constexpr (DO_DK)
+                mfma_settle(dk[db]);
+            if constexpr (DO_DV)
+                mfma_settle(dv[db]);
+        }
     }
     if (key < N) {
         uint16_t *ok = p.dK + head + (size_t)key * dh;
         uint16_t *ov = p.dV + head + (size_t)key * dh;
 #pragma unroll
-        for (int db = 0; db < WDB; ++db) {
-            wide_store(ok, dk[db], 128 * half + 32 * db, hi, p.scale, dh);
-            wide_store(ov, dv[db], 128 * half + 32 * db, hi, 1.f, dh);
+        for (int db = 0; db < NH * WDB; ++db) {
+            if constexpr (DO_DK)
+                wide_store(ok, dk[db], 128 * half + 32 * db, hi, p.scale, dh);
+            if constexpr (DO_DV)
+                wide_store(ov, dv[db], 128 * half + 32 * db, hi, 1.f, dh);
         }
     }
 }
 
 template <bool CAUSAL, bool SPARSE>
-hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
+hipError_t launch_wide(const WideParams &wp0, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0, stream,
-                       wp);
+#ifndef FA_WIDE_SPLIT
+    constexpr bool FULL = true;
+#else
+    constexpr bool FULL = false;
+#endif
+    WideParams wp = wp0;
+    if (FULL) {
+        wp.items = wp0.items / 2;
+        wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
+    }
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE, FULL>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+                       stream, wp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+    if (!FULL) {
+        hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 0>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+                           stream, wp);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 1>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+                       stream, wp);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 2>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
                        stream, wp);
     return hipGetLastError();
 }
