@@ -16,18 +16,17 @@
 //     keys of K (and V); query tiles of 64 rows (Q, dO, lse2, -D) stream
 //     through LDS; S = Q K^T (lane = key). dV and dK take a pass each (dV^T
 //     += dO^T P; then dP = dO V^T, dK^T += Q^T dS), so S is built twice:
-//     8 contractions of work against the method's 5. A split into column
-//     halves, each rebuilding S and dP (11), is kept as MODE 0 and the
-//     split dQ instance, selected at build time by FA_WIDE_SPLIT.
+//     8 contractions of work against the method's 5 (splitting each
+//     gradient into column halves whose workgroups both rebuild S and dP
+//     would take 11).
 // The D and lse2 rows come from the 256-wide instance of the backward's
 // preprocessing kernel. LDS tiles (512-byte rows, 16-byte chunks
 // XOR-swizzled) are double-buffered: the next tile streams in by direct
 // global->LDS loads while the current one is computed, one barrier per tile.
 // A plain schedule, far from the pipelined 128-wide kernels. Work items
-// (blocks; in the split form (block, half) with the halves adjacent) are
-// dealt so that each XCD takes one contiguous range of them: a head's blocks
-// then share that XCD's L2, which reads their K/V (or Q/dO) tiles once for
-// all of them.
+// (128-row blocks) are dealt so that each XCD takes one contiguous range of
+// them: a head's blocks then share that XCD's L2, which reads their K/V (or
+// Q/dO) tiles once for all of them.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -37,7 +36,7 @@ namespace {
 
 constexpr int WD = 256;          // LDS tile row width (elements)
 constexpr int WKK = WD / 16;     // 16-deep steps of a 256-deep contraction
-constexpr int WDB = 4;           // 32-column blocks of one 128-column half
+constexpr int WDB = 4;           // 32-column blocks of 128 columns
 constexpr int WBT = 64;          // rows per LDS tile
 constexpr int WW = 4;            // waves per workgroup, one per SIMD
 constexpr int WROWS = 32 * WW;   // query rows or keys per workgroup
@@ -52,7 +51,7 @@ struct WideParams {
     int nblk;   // 128-row blocks per head
     int ntile;  // 64-row tiles per head
     int nmb;    // mask blocks per mask row
-    int items;    // B * H * nblk * 2: (block, column half), halves adjacent
+    int items;    // B * H * nblk
     int per_xcd;  // items per XCD (xcd_work_item)
     float c, scale;
 };
@@ -143,13 +142,12 @@ __device__ __forceinline__ void wide_store(uint16_t *row_ptr, const f32x16 &acc,
     }
 }
 
-template <bool CAUSAL, bool SPARSE, bool FULL>
+template <bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p)
 {
-    // FULL: one workgroup per block computes all 256 dQ columns (its 8
-    // accumulators in AGPRs), so S^T and dP^T are built once; else one per
-    // (block, column half).
-    constexpr int NH = FULL ? 2 : 1;     // column halves per workgroup
+    // one workgroup per block computes all 256 dQ columns (its 8
+    // accumulators in AGPRs), so S^T and dP^T are built once
+    constexpr int NC = 2 * WDB;  // 32-column blocks of dQ
     // two buffers of [K tile | V tile]
     constexpr uint32_t TB = WBT * WD * 2;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
@@ -158,7 +156,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
-    const int item = FULL ? item0 : item0 / 2, half = FULL ? 0 : item0 % 2;
+    const int item = item0;
     const int bh = item / p.nblk;
     const int bi = item - bh * p.nblk;
     const int qb = CAUSAL ? p.nblk - 1 - bi : bi;  // causal: heaviest first
@@ -186,9 +184,9 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     for (int r = 0; r < 16; ++r)
         ndv[r] = nDi;
 
-    f32x16 dq[NH * WDB];
+    f32x16 dq[NC];
 #pragma unroll
-    for (int db = 0; db < NH * WDB; ++db)
+    for (int db = 0; db < NC; ++db)
         dq[db] = f32x16{};
 
     const int t_end = CAUSAL ? min(p.ntile, (q0 + WROWS - 1) / WBT + 1) : p.ntile;
@@ -246,13 +244,8 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 sb = pack_bf16x8(ds, hh);
 #pragma unroll
-                for (int db = 0; db < NH * WDB; ++db) {
-                    const bf16x8 a = tr.read(ks, kr + 16 * hh, 128 * half + 32 * db);
-                    if constexpr (FULL)
-                        mfma_acc_agpr(dq[db], a, sb);
-                    else
-                        dq[db] = mfma32x32x16(a, sb, dq[db]);
-                }
+                for (int db = 0; db < NC; ++db)
+                    mfma_acc_agpr(dq[db], tr.read(ks, kr + 16 * hh, 32 * db), sb);
             }
         };
         f32x16 s0, dp0, s1, dp1;
@@ -260,37 +253,33 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         scores(32, s1, dp1);
         update(0, dscores(0, s0, dp0));
         update(32, dscores(32, s1, dp1));
-        if constexpr (FULL)
-            mfma_drain();  // before the loop edge, where accumulators may be moved
+        mfma_drain();  // before the loop edge, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
     }
-    if constexpr (FULL) {
-        mfma_drain();
+    mfma_drain();
 #pragma unroll
-        for (int db = 0; db < NH * WDB; ++db)
-            mfma_settle(dq[db]);
-    }
+    for (int db = 0; db < NC; ++db)
+        mfma_settle(dq[db]);
     if (row < N) {
         uint16_t *out = p.dQ + head + (size_t)row * dh;
 #pragma unroll
-        for (int db = 0; db < NH * WDB; ++db)
-            wide_store(out, dq[db], 128 * half + 32 * db, hi, p.scale, dh);
+        for (int db = 0; db < NC; ++db)
+            wide_store(out, dq[db], 32 * db, hi, p.scale, dh);
     }
 }
 
-// MODE 0: one workgroup per (key block, column half) computes that half of
-// dK and dV (S and dP rebuilt for each half). MODE 1: all 256 columns of dV
-// (S only); MODE 2: all 256 columns of dK (S and dP): the 256 accumulators
-// of both gradients do not fit beside the K and V rows, so the full-width
-// form takes two passes, 5 contractions of work against the split's 8.
-template <bool CAUSAL, bool SPARSE, int MODE>
+// One workgroup per 128 keys. DV: all 256 columns of dV (S only); else all
+// 256 columns of dK (S and dP): the accumulators of both gradients do not
+// fit beside the K and V rows, so they take a pass each (5 contractions of
+// work, against 6 for both gradients in column halves that each rebuild S
+// and dP).
+template <bool CAUSAL, bool SPARSE, bool DV>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams p)
 {
-    constexpr bool FULL = MODE != 0;
-    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
-    constexpr int NH = FULL ? 2 : 1;
+    constexpr bool DO_DV = DV, DO_DK = !DV;
+    constexpr int NC = 2 * WDB;  // 32-column blocks of the gradient
     // two buffers of [Q tile | dO tile], then lse2 and -D rows per buffer
     constexpr uint32_t TB = WBT * WD * 2;
     constexpr uint32_t VEC = 4 * TB;
@@ -300,7 +289,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     const int item0 = xcd_work_item(p.per_xcd);
     if (item0 >= p.items)
         return;
-    const int item = FULL ? item0 : item0 / 2, half = FULL ? 0 : item0 % 2;
+    const int item = item0;
     const int bh = item / p.nblk;
     const int kb = item - bh * p.nblk;  // causal: low key blocks see the most queries
     const int k0 = kb * WROWS;
@@ -321,9 +310,9 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                     : bf16x8{};
     }
 
-    f32x16 dk[DO_DK ? NH * WDB : 1], dv[DO_DV ? NH * WDB : 1];
+    f32x16 dk[DO_DK ? NC : 1], dv[DO_DV ? NC : 1];
 #pragma unroll
-    for (int db = 0; db < NH * WDB; ++db) {
+    for (int db = 0; db < NC; ++db) {
         if (DO_DK)
             dk[db] = f32x16{};
         if (DO_DV)
@@ -403,84 +392,53 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 const bf16x8 pb = pack_bf16x8(pm, hh);
                 const bf16x8 sb = DO_DK ? pack_bf16x8(ds, hh) : bf16x8{};
 #pragma unroll
-                for (int db = 0; db < NH * WDB; ++db) {
-                    const int c0 = 128 * half + 32 * db;
-                    if constexpr (DO_DV) {
-                        const bf16x8 ga = tr.read(gs, qr + 16 * hh, c0);
-                        if constexpr (FULL)
-                            mfma_acc_agpr(dv[db], ga, pb);
-                        else
-                            dv[db] = mfma32x32x16(ga, pb, dv[db]);
-                    }
-                    if constexpr (DO_DK) {
-                        const bf16x8 qa = tr.read(qs, qr + 16 * hh, c0);
-                        if constexpr (FULL)
-                            mfma_acc_agpr(dk[db], qa, sb);
-                        else
-                            dk[db] = mfma32x32x16(qa, sb, dk[db]);
-                    }
+                for (int db = 0; db < NC; ++db) {
+                    if constexpr (DO_DV)
+                        mfma_acc_agpr(dv[db], tr.read(gs, qr + 16 * hh, 32 * db), pb);
+                    if constexpr (DO_DK)
+                        mfma_acc_agpr(dk[db], tr.read(qs, qr + 16 * hh, 32 * db), sb);
                 }
             }
         }
-        if constexpr (FULL)
-            mfma_drain();  // before the loop edge, where accumulators may be moved
+        mfma_drain();  // before the loop edge, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
     }
-    if constexpr (FULL) {
-        mfma_drain();
+    mfma_drain();
 #pragma unroll
-        for (int db = 0; db < NH * WDB; ++db) {
-            if constexpr (DO_DK)
-                mfma_settle(dk[db]);
-            if constexpr (DO_DV)
-                mfma_settle(dv[db]);
-        }
+    for (int db = 0; db < NC; ++db) {
+        if constexpr (DO_DK)
+            mfma_settle(dk[db]);
+        if constexpr (DO_DV)
+            mfma_settle(dv[db]);
     }
     if (key < N) {
         uint16_t *ok = p.dK + head + (size_t)key * dh;
         uint16_t *ov = p.dV + head + (size_t)key * dh;
 #pragma unroll
-        for (int db = 0; db < NH * WDB; ++db) {
+        for (int db = 0; db < NC; ++db) {
             if constexpr (DO_DK)
-                wide_store(ok, dk[db], 128 * half + 32 * db, hi, p.scale, dh);
+                wide_store(ok, dk[db], 32 * db, hi, p.scale, dh);
             if constexpr (DO_DV)
-                wide_store(ov, dv[db], 128 * half + 32 * db, hi, 1.f, dh);
+                wide_store(ov, dv[db], 32 * db, hi, 1.f, dh);
         }
     }
 }
 
 template <bool CAUSAL, bool SPARSE>
-hipError_t launch_wide(const WideParams &wp0, hipStream_t stream)
+hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
 {
-#ifndef FA_WIDE_SPLIT
-    constexpr bool FULL = true;
-#else
-    constexpr bool FULL = false;
-#endif
-    WideParams wp = wp0;
-    if (FULL) {
-        wp.items = wp0.items / 2;
-        wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
-    }
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE, FULL>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
-                       stream, wp);
+    const dim3 grid(wp.per_xcd * kXcds), block(WW * kWave);
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE>), grid, block, 0, stream, wp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (!FULL) {
-        hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 0>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
-                           stream, wp);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 1>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
-                       stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, true>), grid, block, 0, stream, wp);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, 2>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
-                       stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, false>), grid, block, 0, stream, wp);
     return hipGetLastError();
 }
 
@@ -511,7 +469,7 @@ hipError_t launch_bwd_bf16_wide(const Problem &pr, const uint16_t *dO, const uin
     wp.nblk = (pr.N + WROWS - 1) / WROWS;
     wp.ntile = (pr.N + WBT - 1) / WBT;
     wp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
-    wp.items = pr.B * pr.H * wp.nblk * 2;
+    wp.items = pr.B * pr.H * wp.nblk;
     wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
     wp.c = pr.scale * kLog2e;
     wp.scale = pr.scale;
