@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--supp-steps", type=int, default=10,
                     help="timed steps of the supplementary non-causal run (0: skip)")
     ap.add_argument("--decode-steps", type=int, default=10,
@@ -343,8 +343,8 @@ def clock_under_load(step, seconds):
 
 def cpu_other(args):
     """The CPU reference (as is) on samples of the other workloads, on the
-    same host threads: workloads 1 and 2 in full (fwd+bwd), two heads of the
-    block-sparse workload (fwd+bwd), and the 256 sampled query rows of the
+    same host threads: workloads 1, 2 and the block-sparse one in full
+    (fwd+bwd), and the 256 sampled query rows of the
     64K dense forward with a labelled extrapolation to all of its rows.
     Rates use the same algorithmic FLOP counts as the GPU figures."""
     import oracle
@@ -361,7 +361,7 @@ def cpu_other(args):
                          "sample": "all heads, fwd+bwd"}
     cfg = syn.CONFIGS[5]
     q, k, v, do, mask = syn.config_inputs(cfg)
-    nh = 2
+    nh = cfg.B * cfg.H
     hs = lambda x: x.reshape((1, cfg.B * cfg.H) + x.shape[2:])[:, :nh]  # noqa: E731
     t1 = time.perf_counter()
     oracle.attention(hs(q), hs(k), hs(v), cfg.scale, causal=cfg.causal, blockmask=mask, do=hs(do))
