@@ -604,7 +604,7 @@ def main():
         wide = {"workload": cfg.name + " forward at head dim 256 (supplementary)", "d": 256,
                 "fwd_ms": round(f_s * 1e3, 4), "fwd_tflops": round(wflops / f_s / 1e12, 2),
                 "frac_of_peak": round(wflops / f_s / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "mfma_work_factor": 1.5, "steps": args.wide_steps}
+                "mfma_work_factor": 1.0, "steps": args.wide_steps}
         if args.wide_bwd:
             # the backward at d = 256 (column halves that each rebuild S and
             # dP): one warm-up call, then the median of --wide-bwd timed calls

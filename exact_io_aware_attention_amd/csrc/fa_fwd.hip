@@ -131,12 +131,19 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     constexpr int LPWK = BC * DK * 2 / 1024 / W;  // 1 KB direct loads per wave per K tile
     constexpr int LPWV = BC * DV * 2 / 1024 / W;  // ... per V tile
     static_assert(LPWV >= 1, "tile too small for the direct-load layout");
+    // O wider than 128 columns: its accumulators live in AGPRs (asm MFMAs)
+    // and the V tiles are double-buffered, so that three K tiles and two V
+    // tiles fill the 160 KB of LDS; the buffer phases then repeat every 6
+    // tiles instead of 3.
+    constexpr bool WIDE_O = DV > 128;
+    constexpr int NBV = WIDE_O ? 2 : 3;
+    constexpr int U = WIDE_O ? 6 : 3;
 
-    // LDS: three K tiles, then three V tiles.
+    // LDS: three K tiles, then NBV V tiles.
     constexpr uint32_t TBK = BC * DK * 2;  // bytes per K tile
     constexpr uint32_t TBV = BC * DV * 2;  // bytes per V tile
     constexpr uint32_t V_OFF = 3 * TBK;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 3 * TBV];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + NBV * TBV];
     const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item0 = xcd_work_item(p.per_xcd);
@@ -320,7 +327,8 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     issue_v(t0, 0);
     if (t1 < t_end) {
         issue_k(t1, 1);
-        issue_v(t1, 1);
+        if (!WIDE_O)
+            issue_v(t1, 1);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -379,18 +387,24 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     };
     auto tile = [&](auto mtag, auto ptag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
-        constexpr int P = decltype(ptag)::value;           // j % 3
-        constexpr uint32_t KB_CUR = P * TBK;               // tile j's K buffer
+        constexpr int P = decltype(ptag)::value;           // j % U
+        constexpr uint32_t KB_CUR = (P % 3) * TBK;         // tile j's K buffer
         constexpr uint32_t KB_NXT = (P + 1) % 3 * TBK;     // tile j+1's
-        constexpr uint32_t VB_CUR = P * TBV;               // tile j's V buffer
+        constexpr uint32_t VB_CUR = (P % NBV) * TBV;       // tile j's V buffer
         constexpr int KB_NN = (P + 2) % 3;                 // tile j+2's
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
         // K and V of tile j+2 replace tile j-1's, last read before the
         // previous barrier; tile j+1's were issued one iteration ago (its K
-        // has landed, its V may still be in flight).
+        // has landed, its V may still be in flight). With two V buffers,
+        // tile j+1's V replaces tile j-1's now and lands by the barrier.
         const bool more = tnn < t_end;
-        if (more) {
+        if constexpr (WIDE_O) {
+            if (tn < t_end)
+                issue_v(tn, (P + 1) % 2);
+            if (more)
+                issue_k(tnn, KB_NN);
+        } else if (more) {
             issue_k(tnn, KB_NN);
             issue_v(tnn, KB_NN);
         }
@@ -412,6 +426,13 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 nmref = (m == -INFINITY) ? 0.f : -m;
                 l *= alpha;
                 lb *= alpha;
+                if constexpr (WIDE_O) {
+                    // the accumulators are read once their MFMAs drained
+                    mfma_drain();
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        mfma_settle(o[db]);
+                }
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -480,15 +501,23 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 ls1 += e1;
             }
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
+            for (int db = 0; db < DB; ++db) {
+                if constexpr (WIDE_O)
+                    mfma_acc_agpr(o[db], vf[0][db], p0);
+                else
+                    o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
+            }
             l += ls0 + ls1;
             const bf16x8 p1 = pack_bf16x8(s_cur, 1);
             if constexpr (RSUM)
                 lb = bf16x8_sum_acc(p1, bf16x8_sum_acc(p0, lb));
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
+            for (int db = 0; db < DB; ++db) {
+                if constexpr (WIDE_O)
+                    mfma_acc_agpr(o[db], vf[1][db], p1);
+                else
+                    o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
+            }
             // the next half-step's first K^T fragments: tile j+1's first 32
             // keys, then its second 32 (visible since the last barrier). The
             // latter stay in flight across the barrier below, which then must
@@ -520,7 +549,9 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         // last, may still be in flight); the barrier extends that to all
         // waves. The next iteration reads tile j+2's K from its second
         // half-step on and its V one iteration later.
-        if (more)
+        if constexpr (WIDE_O)
+            mfma_drain();  // before the loop edges, where accumulators may be moved
+        if (more && !WIDE_O)
             lds_dma_wait<LPWV>();
         else
             lds_dma_wait<0>();
@@ -531,27 +562,22 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // Iterations whose keys need no element mask run in a loop of their own
     // (causal: the masked ones are the last, on the diagonal; block-sparse:
     // a wave whose mask row drops a tile another wave keeps).
-    int phase = 0;  // j % 3
+    int phase = 0;  // j % U
     auto run = [&](auto mtag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
-        for (;;) {
-            if (phase == 0) {
-                if (t >= t_end || tile_masked() != MASKED)
-                    return;
-                tile(mtag, std::integral_constant<int, 0>{});
-                phase = 1;
-            }
-            if (phase == 1) {
-                if (t >= t_end || tile_masked() != MASKED)
-                    return;
-                tile(mtag, std::integral_constant<int, 1>{});
-                phase = 2;
-            }
-            if (t >= t_end || tile_masked() != MASKED)
-                return;
-            tile(mtag, std::integral_constant<int, 2>{});
-            phase = 0;
+#define FA_FWD_PHASE(k)                                                     \
+        if constexpr (k < U) {                                              \
+            if (phase == k) {                                               \
+                if (t >= t_end || tile_masked() != MASKED)                  \
+                    return;                                                 \
+                tile(mtag, std::integral_constant<int, k>{});               \
+                phase = (k + 1) % U;                                        \
+            }                                                               \
         }
+        for (;;) {
+            FA_FWD_PHASE(0) FA_FWD_PHASE(1) FA_FWD_PHASE(2) FA_FWD_PHASE(3) FA_FWD_PHASE(4) FA_FWD_PHASE(5)
+        }
+#undef FA_FWD_PHASE
     };
     while (t < t_end) {
         run(std::false_type{});
@@ -560,6 +586,12 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
 
     // Epilogue: O = O^T / lb (transposed back per lane), LSE from l in
     // natural log.
+    if constexpr (WIDE_O) {
+        mfma_drain();
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            mfma_settle(o[db]);
+    }
     const float lt = halves_sum(l);
     const float lbt = RSUM ? halves_sum(lb) : lt;
     if (row < N) {
@@ -660,7 +692,7 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
         return launch_fwd_d<128>(pr, fp);
     if (pr.dropout)
         return hipErrorInvalidValue;
-    return launch_fwd_dd<256, 128, false>(pr, fp);
+    return launch_fwd_dd<256, 256, false>(pr, fp);
 }
 
 }  // namespace fa
