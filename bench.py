@@ -280,6 +280,27 @@ def sparse_sweep(cfg, steps):
             "linear_fit": fit, "steps": steps}
 
 
+def _smi_handle_for_cuda0(amdsmi, handles):
+    """The amdsmi handle of the device torch calls cuda:0, matched by PCI
+    address (amdsmi may list devices that HIP does not expose); the first
+    handle when the address cannot be read."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    want = (getattr(p, "pci_domain_id", None), getattr(p, "pci_bus_id", None),
+            getattr(p, "pci_device_id", None))
+    if None not in want:
+        for h in handles:
+            try:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                dev = rest.split(".")[0]
+                if (int(dom, 16), int(bus, 16), int(dev, 16)) == want:
+                    return h
+            except Exception:
+                continue
+    return handles[0]
+
+
 def clock_under_load(step, seconds):
     """Repeats `step` (one headline step) for about `seconds` while a
     thread samples the GPU's current gfx clock and socket power through
@@ -293,7 +314,8 @@ def clock_under_load(step, seconds):
     try:
         import amdsmi
         amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        handles = amdsmi.amdsmi_get_processor_handles()
+        handle = _smi_handle_for_cuda0(amdsmi, handles)
     except Exception as e:  # monitoring only: the bench goes on without it
         return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"}
     samples, stop = [], threading.Event()
@@ -606,8 +628,8 @@ def main():
                 "frac_of_peak": round(wflops / f_s / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "mfma_work_factor": 1.0, "steps": args.wide_steps}
         if args.wide_bwd:
-            # the backward at d = 256 (column halves that each rebuild S and
-            # dP): one warm-up call, then the median of --wide-bwd timed calls
+            # the backward at d = 256 (dQ, dV and dK passes, S rebuilt in
+            # each): one warm-up call, then the median of --wide-bwd timed calls
             dOw = torch.randn(shp, generator=g, device=dev).to(torch.bfloat16)
             dQw, dKw, dVw = (torch.empty_like(Qw) for _ in range(3))
             wsw = fa.new_workspace(cfg.B, cfg.H, cfg.N, 256, dev)

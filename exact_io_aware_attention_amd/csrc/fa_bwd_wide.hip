@@ -4,14 +4,14 @@
 // §三.3): P = 2^(c s - lse2), dP = dO V^T, dS = P o (dP - D), dQ = scale dS K,
 // dK = scale dS^T Q, dV = P^T dO.
 //
-// At d = 256 a wave holds 32 rows of two 256-wide operands (128 VGPRs) and
-// the accumulators of one 256-column gradient (128 AGPRs, asm MFMAs), but
-// not those of two:
+// At d = 256 a wave holds 32 rows of two 256-wide MFMA B operands and the
+// accumulators of one 256-column gradient (128 + 128 AGPRs), but not those
+// of two:
 //   - bwd_wide_dq_kernel: one workgroup per 128 query rows; each wave holds
-//     32 query rows of Q and dO as MFMA B operands; key/value tiles of 64
-//     rows stream through LDS; S^T = K Q^T and dP^T = V dO^T (lane =
-//     query), dS^T by the vector ALU, dQ^T += K^T dS^T over all 256 columns
-//     with K^T from LDS transpose reads;
+//     32 query rows of Q and dO; key/value tiles of 64 rows stream through
+//     LDS; S^T = K Q^T and dP^T = V dO^T (lane = query), dS^T by the vector
+//     ALU, dQ^T += K^T dS^T over all 256 columns with K^T from LDS
+//     transpose reads;
 //   - bwd_wide_dkdv_kernel: one workgroup per 128 keys; each wave holds 32
 //     keys of K (and V); query tiles of 64 rows (Q, dO, lse2, -D) stream
 //     through LDS; S = Q K^T (lane = key). dV and dK take a pass each (dV^T
@@ -23,10 +23,15 @@
 // preprocessing kernel. LDS tiles (512-byte rows, 16-byte chunks
 // XOR-swizzled) are double-buffered: the next tile streams in by direct
 // global->LDS loads while the current one is computed, one barrier per tile.
-// A plain schedule, far from the pipelined 128-wide kernels. Work items
-// (128-row blocks) are dealt so that each XCD takes one contiguous range of
-// them: a head's blocks then share that XCD's L2, which reads their K/V (or
-// Q/dO) tiles once for all of them.
+// With one wave per SIMD nothing hides a wave's own latencies, so a tile's
+// work is laid out by hand in MFMA slots (WidePlan): every LDS operand is
+// read a few slots ahead of its MFMA and the softmax of one step runs beside
+// the MFMAs of the next phase; the B operands sit in AGPRs, which leaves the
+// VGPRs room for the reads in flight. Only tiles on the diagonal or at the
+// ragged end apply the element mask. Work items (128-row blocks) are dealt
+// so that each XCD takes one contiguous range of them: a head's blocks then
+// share that XCD's L2, which reads their K/V (or Q/dO) tiles once for all of
+// them.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -84,43 +89,87 @@ struct WideDma {
             off[i] = 8 * c < dh ? 2 * (r * dh + 8 * c) : kBufferOutOfRange;
         }
     }
+    __device__ __forceinline__ static i32x4 rsrc(const uint16_t *src, int row0, int N, int dh)
+    {
+        return buffer_rsrc(src + (size_t)row0 * dh, (uint32_t)(N - row0) * (2 * dh));
+    }
+    // the i-th of this wave's 8 blocks (for spreading them over slots)
+    __device__ __forceinline__ void issue_block(const i32x4 &rs, int i, uint32_t tile, int wave) const
+    {
+        lds_dma_buf_b128(rs, off[i], tile + (8 * wave + i) * 1024);
+    }
     __device__ __forceinline__ void issue(const uint16_t *src, int row0, int N, int dh, uint32_t tile,
                                           int wave) const
     {
-        const i32x4 rs = buffer_rsrc(src + (size_t)row0 * dh, (uint32_t)(N - row0) * (2 * dh));
+        const i32x4 rs = rsrc(src, row0, N, dh);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            lds_dma_buf_b128(rs, off[i], tile + (8 * wave + i) * 1024);
+            issue_block(rs, i, tile, wave);
     }
 };
 
-// MFMA A operand: rows rb .. rb + 31 of a tile (rb a multiple of 16), depth
-// 16 kk .. 16 kk + 15 (logical chunk 2 kk + hi).
-__device__ __forceinline__ bf16x8 wide_rows(const uint16_t *tile, int rb, int kk, int l32, int hi)
-{
-    return *reinterpret_cast<const bf16x8 *>(tile + (rb + l32) * WD + 8 * ((2 * kk + hi) ^ wide_swz(l32)));
-}
-
-// Lane part of a transpose read: 16 tile rows starting at r0, 32 columns
-// starting at c0 (the A operand whose depth runs over rows, in the row order
-// that matches a C tile's registers 8 s .. 8 s + 7 used as B operand).
-struct WideTr {
-    // lane offsets: rows 4 (g / 2) + sl / 4 and 8 further, logical chunk lc
-    // (plus the block's), element in within it
-    int row, lc, in;
-    __device__ __forceinline__ explicit WideTr(int lane)
+// Lane parts of the LDS operand addresses on a 64 x 256 tile. The swizzle
+// is an XOR on address bits 4..8 of a row's bytes, which a tile base (a
+// multiple of 512) and the row offsets leave clear, so a read takes the
+// tile base plus the lane part, XORs in a per-read constant and adds the
+// row offset through the instruction's immediate:
+//   b128 operand, rows rb + l32, depth 16 kk.. (logical chunk 2 kk + hi,
+//     = (2 kk) ^ hi): ((base + b128) ^ (32 kk)) + 512 rb;
+//   transpose operand of 16 rows r0.. (a multiple of 16) x 32 columns
+//     32 db..: lane 4 t + u of 16-lane group g points at rows
+//     rl = 4 (g / 2) + t and rl + 8, logical chunk 4 db + lc with
+//     lc = 2 (g % 2) + u / 2 (= (4 db) ^ lc), element 4 (u % 2) in it:
+//     ((base + tr0) ^ (64 db)) + 512 r0 and the same with tr1.
+// (wide_swz depends on the row modulo 16, so row blocks at multiples of 16
+// share the lane parts.)
+struct WideLane {
+    uint32_t b128, tr0, tr1;
+    __device__ __forceinline__ explicit WideLane(int lane)
     {
+        const int l32 = lane % 32, hi = lane / 32;
+        b128 = l32 * (2 * WD) + 16 * (hi ^ wide_swz(l32));
         const int g = lane / 16, sl = lane % 16;
-        row = 4 * (g / 2) + sl / 4;
-        lc = 2 * (g % 2) + (sl % 4) / 2;
-        in = 4 * (sl % 2);
+        const int rl = 4 * (g / 2) + sl / 4;
+        const int lc = 2 * (g % 2) + (sl % 4) / 2;
+        const int in = 4 * (sl % 2);
+        tr0 = rl * (2 * WD) + 16 * (lc ^ wide_swz(rl)) + 2 * in;
+        tr1 = (rl + 8) * (2 * WD) + 16 * (lc ^ wide_swz(rl + 8)) + 2 * in;
     }
-    // r0 a multiple of 16, c0 a multiple of 32
-    __device__ __forceinline__ bf16x8 read(const uint16_t *tile, int r0, int c0) const
+    // base: tile address (a multiple of 512); off: byte offset of the row
+    // block (and of the tile within a slot), a compile-time constant
+    __device__ __forceinline__ bf16x8 rows(uint32_t base, uint32_t off, int kk) const
     {
-        const int c = c0 / 8 + lc;
-        return lds_read_tr_pair(tile + (r0 + row) * WD + 8 * (c ^ wide_swz(row)) + in,
-                                tile + (r0 + row + 8) * WD + 8 * (c ^ wide_swz(row + 8)) + in);
+        return lds_b128_at(((base + b128) ^ (32u * kk)) + off);
+    }
+    __device__ __forceinline__ bf16x8 trans(uint32_t base, uint32_t off, int db) const
+    {
+        return lds_tr_pair_at(((base + tr0) ^ (64u * db)) + off, ((base + tr1) ^ (64u * db)) + off);
+    }
+};
+
+// Slot plan of a tile's two steps (32 rows each) shared by the kernels
+// below: A(0), A(1) with B(0) spread over its MFMAs, C(0) with B(1), C(1),
+// one MFMA per slot. A step's softmax elements pass three stages (F: the
+// exponent argument, E: the exponential and the mask, M: the product and
+// the packing into MFMA operands) in consecutive slots, element e of B(0)
+// starting at slot NA + R0 e, of B(1) at slot 2 NA + e, so that no slot
+// waits on a value it produced itself; the last stages run into the first
+// slots of the next phase, whose MFMAs take the second operand half (the
+// elements 8..15) only from their ninth slot on.
+template <int NA, int NCS>
+struct WidePlan {
+    static constexpr int NSLOT = 2 * NA + 2 * NCS;
+    static constexpr int R0 = NA / 16;  // slots per element of B(0)
+    static_assert(R0 * 16 == NA && NCS == 16, "slot plan");
+    static constexpr int PF = 5;        // operand reads issued this many slots ahead
+    // element of step st whose stage k (0 F, 1 E, 2 M) falls into slot m,
+    // or -1
+    __device__ static constexpr int elem(int m, int st, int k)
+    {
+        const int first = st == 0 ? NA : 2 * NA;
+        const int r = st == 0 ? R0 : 1;
+        const int d = m - first - k;
+        return (d >= 0 && d % r == 0 && d / r < 16) ? d / r : -1;
     }
 };
 
@@ -142,15 +191,26 @@ __device__ __forceinline__ void wide_store(uint16_t *row_ptr, const f32x16 &acc,
     }
 }
 
+// One workgroup per 128 query rows; each wave holds 32 query rows of Q and
+// dO, the B operands of S^T and dP^T, in AGPRs beside its eight dQ^T
+// accumulators, so that the VGPRs hold the scores, the softmax and the
+// operands read ahead. Per 32 keys (a step):
+//   A: S^T = K Q^T and dP^T = V dO^T (lane = query; 16 MFMA pairs, K and V
+//      rows read from LDS);
+//   B: P^T = 2^(c s - lse2), dS^T = P^T o (dP^T - D) (vector ALU);
+//   C: dQ^T += K^T dS^T over all 256 columns (16 MFMAs, K^T by transpose
+//      reads).
+// Every step ends inside its tile (WidePlan), so two LDS slots suffice: the
+// next tile streams into the other one, a load per slot of the first step.
 template <bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p)
 {
-    // one workgroup per block computes all 256 dQ columns (its 8
-    // accumulators in AGPRs), so S^T and dP^T are built once
-    constexpr int NC = 2 * WDB;  // 32-column blocks of dQ
-    // two buffers of [K tile | V tile]
-    constexpr uint32_t TB = WBT * WD * 2;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB];
+    constexpr int NC = 2 * WDB;            // 32-column blocks of dQ
+    constexpr uint32_t TB = WBT * WD * 2;  // bytes per tile
+    constexpr uint32_t SLOT = 2 * TB;      // [K tile | V tile]
+    using Plan = WidePlan<2 * WKK, 2 * NC>;
+    constexpr int NA = 2 * WKK, NSLOT = Plan::NSLOT, PF = Plan::PF;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLOT];
     const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item0 = xcd_work_item(p.per_xcd);
@@ -162,11 +222,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     const int qb = CAUSAL ? p.nblk - 1 - bi : bi;  // causal: heaviest first
     const int q0 = qb * WROWS;
     const int N = p.N, dh = p.dh;
+    const float c = p.c;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave, l32 = lane % 32, hi = lane / 32;
-    const int row = q0 + 32 * wave + l32;  // this lane's query
+    const int wr0 = q0 + 32 * wave;  // this wave's first query
+    const int row = wr0 + l32;       // this lane's query
     const size_t head = (size_t)bh * N * dh;
-    const WideTr tr(lane);
+    const WideLane wl(lane);
 
     bf16x8 qf[WKK], gf[WKK];
 #pragma unroll
@@ -176,6 +238,8 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
                     : bf16x8{};
         gf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.dO + head + (size_t)row * dh + 16 * kk + 8 * hi)
                     : bf16x8{};
+        keep_in_agpr(qf[kk]);
+        keep_in_agpr(gf[kk]);
     }
     const float lse2 = row < N ? p.lse2[(size_t)bh * N + row] : INFINITY;
     const float nDi = row < N ? p.ndelta[(size_t)bh * N + row] : 0.f;
@@ -198,67 +262,126 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         return SPARSE ? next_kept_tile(mc, t + 1, t_end, kMaskBlock / WBT) : t + 1;
     };
     const WideDma dma(wave, lane, dh);
-    auto issue = [&](int t, int buf) {
-        dma.issue(p.K + head, t * WBT, N, dh, lds0 + (2 * buf) * TB, wave);
-        dma.issue(p.V + head, t * WBT, N, dh, lds0 + (2 * buf + 1) * TB, wave);
+
+    // One tile (keys t * 64..) in the slot at `base`; the loads of tile tl
+    // go into the slot at `nbase`. MASKED applies the element mask: key
+    // past the end or above the query (causal).
+    auto tile = [&](auto mtag, int t, uint32_t base, int tl, uint32_t nbase) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        const int kbase = t * WBT;
+        const i32x4 rk = WideDma::rsrc(p.K + head, tl * WBT, N, dh);
+        const i32x4 rv = WideDma::rsrc(p.V + head, tl * WBT, N, dh);
+        // operand of slot m: A slots alternate K rows (S^T) and V rows
+        // (dP^T); C slot pr = (hh, db) takes K^T of keys 16 hh.. of its step
+        bf16x8 op[NSLOT];
+        auto read_op = [&](int m) __attribute__((always_inline)) {
+            if (m < 2 * NA) {
+                const int st = m / NA, kk = (m % NA) / 2;
+                op[m] = wl.rows(base, (m % 2) * TB + 32 * st * (2 * WD), kk);
+            } else {
+                const int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
+                op[m] = wl.trans(base, (32 * st + 16 * (pr / NC)) * (2 * WD), pr % NC);
+            }
+        };
+        f32x16 s[2], dp[2];
+        float tx[2][16], pe[2][16], dsm[2][16];
+        bf16x8 sb[2][2];
+        auto stage = [&](int st, int k, int e) __attribute__((always_inline)) {
+            if (k == 0) {
+                tx[st][e] = fmaf(s[st][e], c, -lse2);
+                slot_done(tx[st][e]);
+            } else if (k == 1) {
+                float v = exp2_fast(tx[st][e]);
+                if (MASKED) {
+                    const int key = kbase + 32 * st + 8 * (e / 4) + 4 * hi + (e % 4);
+                    if (key >= N || (CAUSAL && key > row))
+                        v = 0.f;
+                }
+                pe[st][e] = v;
+                slot_done(v);
+            } else {
+                dsm[st][e] = pe[st][e] * dp[st][e];
+                if (e % 8 == 7) {
+                    bf16x8 sk;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        sk[i] = (__bf16)dsm[st][e - 7 + i];
+                    sb[st][e / 8] = sk;
+                    slot_done(sk);
+                } else {
+                    slot_done(dsm[st][e]);
+                }
+            }
+        };
+        static_for<PF>([&](auto mc) __attribute__((always_inline)) { read_op(decltype(mc)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NSLOT>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr (m < 2 * NA) {
+                constexpr int st = m / NA, kk = (m % NA) / 2;
+                if constexpr (m % 2 == 0)
+                    s[st] = mfma32x32x16(op[m], qf[kk], kk == 0 ? f32x16{} : s[st]);
+                else
+                    dp[st] = mfma32x32x16(op[m], gf[kk], kk == 0 ? ndv : dp[st]);
+            } else {
+                constexpr int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
+                mfma_acc_agpr_ordered(dq[pr % NC], op[m], sb[st][pr / NC]);
+            }
+            if constexpr (m + PF < NSLOT)
+                read_op(m + PF);
+            if constexpr (m < 8)
+                dma.issue_block(rk, m, nbase, wave);
+            else if constexpr (m < 16)
+                dma.issue_block(rv, m - 8, nbase + TB, wave);
+            static_for<6>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int st = decltype(ic)::value / 3, k = 2 - decltype(ic)::value % 3;
+                constexpr int e = Plan::elem(m, st, k);
+                if constexpr (e >= 0)
+                    stage(st, k, e);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
+
     int t = next_tile(-1);
-    if (t < t_end)
-        issue(t, 0);
+    if (t < t_end) {
+        dma.issue(p.K + head, t * WBT, N, dh, lds0, wave);
+        dma.issue(p.V + head, t * WBT, N, dh, lds0 + TB, wave);
+    }
+#pragma unroll
+    for (int kk = 0; kk < WKK; ++kk) {
+        wait_loaded(qf[kk]);
+        wait_loaded(gf[kk]);
+    }
+    wait_loaded(lse2);
+    wait_loaded(nDi);
     lds_dma_wait<0>();
     __syncthreads();
-    // Tile t computes from buffer `buf` while tile t+1 loads into the other,
-    // whose last reads ended before the previous barrier.
-    for (int buf = 0; t < t_end; buf ^= 1) {
+    // Whether this wave's elements of tile t need the element mask.
+    auto tile_masked = [&](int t) __attribute__((always_inline)) -> bool {
+        const int kbase = t * WBT;
+        return (kbase + WBT > N) || (CAUSAL && kbase + WBT - 1 > wr0);
+    };
+    int j = 0;
+    // One tile and the barrier after which the next one has landed (without
+    // a next tile the current one is loaded again, into the free slot).
+    auto step_tile = [&](auto mtag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
-        if (tn < t_end)
-            issue(tn, buf ^ 1);
-        const uint16_t *ks = reinterpret_cast<const uint16_t *>(smem + (2 * buf) * TB);
-        const uint16_t *vs = reinterpret_cast<const uint16_t *>(smem + (2 * buf + 1) * TB);
-        // The tile's two steps of 32 keys (tile rows kr..): S^T and dP^T
-        // (MFMA), dS^T (vector ALU), dQ^T += K^T dS^T (MFMA). The second
-        // step's S^T and dP^T are issued before the first step's dS^T, so
-        // that the vector work runs beside independent MFMAs.
-        auto scores = [&](int kr, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
-#pragma unroll
-            for (int kk = 0; kk < WKK; ++kk) {
-                s = mfma32x32x16(wide_rows(ks, kr, kk, l32, hi), qf[kk], kk == 0 ? f32x16{} : s);
-                dp = mfma32x32x16(wide_rows(vs, kr, kk, l32, hi), gf[kk], kk == 0 ? ndv : dp);
-            }
-        };
-        // register r: key t * 64 + kr + 8 (r / 4) + 4 hi + r % 4
-        auto dscores = [&](int kr, const f32x16 &s, const f32x16 &dp) __attribute__((always_inline)) {
-            f32x16 ds;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = t * WBT + kr + 8 * (r / 4) + 4 * hi + (r % 4);
-                float pe = exp2_fast(fmaf(s[r], p.c, -lse2));
-                if (key >= N || (CAUSAL && key > row))
-                    pe = 0.f;
-                ds[r] = pe * dp[r];
-            }
-            return ds;
-        };
-        auto update = [&](int kr, const f32x16 &ds) __attribute__((always_inline)) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 sb = pack_bf16x8(ds, hh);
-#pragma unroll
-                for (int db = 0; db < NC; ++db)
-                    mfma_acc_agpr(dq[db], tr.read(ks, kr + 16 * hh, 32 * db), sb);
-            }
-        };
-        f32x16 s0, dp0, s1, dp1;
-        scores(0, s0, dp0);
-        scores(32, s1, dp1);
-        update(0, dscores(0, s0, dp0));
-        update(32, dscores(32, s1, dp1));
-        mfma_drain();  // before the loop edge, where accumulators may be moved
+        tile(mtag, t, lds0 + (j % 2) * SLOT, tn < t_end ? tn : t, lds0 + ((j + 1) % 2) * SLOT);
+        mfma_drain();  // before the loop edges, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
+        ++j;
+    };
+    // Runs of masked and unmasked tiles each get a loop of their own
+    // (causal: the masked tiles are the last ones, on the diagonal).
+    while (t < t_end) {
+        while (t < t_end && !tile_masked(t))
+            step_tile(std::false_type{});
+        while (t < t_end && tile_masked(t))
+            step_tile(std::true_type{});
     }
-    mfma_drain();
 #pragma unroll
     for (int db = 0; db < NC; ++db)
         mfma_settle(dq[db]);
@@ -270,20 +393,29 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     }
 }
 
-// One workgroup per 128 keys. DV: all 256 columns of dV (S only); else all
-// 256 columns of dK (S and dP): the accumulators of both gradients do not
-// fit beside the K and V rows, so they take a pass each (5 contractions of
-// work, against 6 for both gradients in column halves that each rebuild S
-// and dP).
+// One workgroup per 128 keys; each wave holds 32 keys of K (and of V for
+// dK), the B operands of S (and dP), in AGPRs beside the accumulators of
+// one 256-column gradient. The accumulators of both gradients do not fit
+// beside the K and V rows, so they take a pass each (5 contractions of
+// work; 6 for both gradients in column halves that each rebuild S and dP).
+// Per 32 queries (a step), lane = key:
+//   A: S = Q K^T (and dP - D = dO V^T - D for dK, the accumulator starting
+//      from -D); Q and dO rows read from LDS;
+//   B: P = 2^(c s - lse2) (and dS = P o (dP - D)) (vector ALU);
+//   C: dV^T += dO^T P, or dK^T += Q^T dS (16 MFMAs, transpose reads).
+// The slots follow WidePlan, as in the dQ kernel.
 template <bool CAUSAL, bool SPARSE, bool DV>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams p)
 {
     constexpr bool DO_DV = DV, DO_DK = !DV;
-    constexpr int NC = 2 * WDB;  // 32-column blocks of the gradient
-    // two buffers of [Q tile | dO tile], then lse2 and -D rows per buffer
-    constexpr uint32_t TB = WBT * WD * 2;
-    constexpr uint32_t VEC = 4 * TB;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TB + 4 * WBT * 4];
+    constexpr int NC = 2 * WDB;            // 32-column blocks of the gradient
+    constexpr uint32_t TB = WBT * WD * 2;  // bytes per tile
+    constexpr uint32_t SLOT = 2 * TB;      // [Q tile | dO tile]
+    constexpr uint32_t VEC = 2 * SLOT;     // then lse2 and -D rows per slot
+    constexpr int NA = DO_DK ? 2 * WKK : WKK;
+    using Plan = WidePlan<NA, 2 * NC>;
+    constexpr int NSLOT = Plan::NSLOT, PF = Plan::PF;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[VEC + 4 * WBT * 4];
     const uint32_t lds0 = lds_byte_addr(smem);
 
     const int item0 = xcd_work_item(p.per_xcd);
@@ -294,30 +426,32 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     const int kb = item - bh * p.nblk;  // causal: low key blocks see the most queries
     const int k0 = kb * WROWS;
     const int N = p.N, dh = p.dh;
+    const float c = p.c;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave, l32 = lane % 32, hi = lane / 32;
-    const int key = k0 + 32 * wave + l32;  // this lane's key
+    const int wk0 = k0 + 32 * wave;  // this wave's first key
+    const int key = wk0 + l32;       // this lane's key
     const size_t head = (size_t)bh * N * dh;
-    const WideTr tr(lane);
+    const WideLane wl(lane);
 
-    bf16x8 kf[WKK], vf[WKK];
+    bf16x8 kf[WKK], vf[DO_DK ? WKK : 1];
 #pragma unroll
     for (int kk = 0; kk < WKK; ++kk) {
         const bool in = key < N && 16 * kk + 8 * hi < dh;
         kf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.K + head + (size_t)key * dh + 16 * kk + 8 * hi)
                     : bf16x8{};
-        vf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.V + head + (size_t)key * dh + 16 * kk + 8 * hi)
-                    : bf16x8{};
+        keep_in_agpr(kf[kk]);
+        if constexpr (DO_DK) {
+            vf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.V + head + (size_t)key * dh + 16 * kk + 8 * hi)
+                        : bf16x8{};
+            keep_in_agpr(vf[kk]);
+        }
     }
 
-    f32x16 dk[DO_DK ? NC : 1], dv[DO_DV ? NC : 1];
+    f32x16 acc[NC];  // dK^T or dV^T
 #pragma unroll
-    for (int db = 0; db < NC; ++db) {
-        if (DO_DK)
-            dk[db] = f32x16{};
-        if (DO_DV)
-            dv[db] = f32x16{};
-    }
+    for (int db = 0; db < NC; ++db)
+        acc[db] = f32x16{};
 
     const int t_begin = CAUSAL ? k0 / WBT : 0;
     // query tiles the workgroup needs (one mask column, so uniform over it)
@@ -328,101 +462,172 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         return SPARSE ? next_kept_tile(mc, t + 1, p.ntile, kMaskBlock / WBT) : t + 1;
     };
     const WideDma dma(wave, lane, dh);
-    // rows past N read as zeros: their queries are masked below
-    auto issue = [&](int t, int buf) {
-        dma.issue(p.Q + head, t * WBT, N, dh, lds0 + (2 * buf) * TB, wave);
-        dma.issue(p.dO + head, t * WBT, N, dh, lds0 + (2 * buf + 1) * TB, wave);
+    // the statistics rows of tile t into slot b (rows past N read as zeros:
+    // their queries are masked)
+    auto issue_vec = [&](int t, int b) __attribute__((always_inline)) {
         if (wave < 2) {
             const float *v = (wave == 0 ? p.lse2 : p.ndelta) + (size_t)bh * N + t * WBT;
             const i32x4 rs = buffer_rsrc(v, (uint32_t)(N - t * WBT) * 4);
-            lds_dma_buf_b32(rs, 4 * lane, lds0 + VEC + (2 * buf + wave) * WBT * 4);
+            lds_dma_buf_b32(rs, 4 * lane, lds0 + VEC + (2 * b + wave) * WBT * 4);
         }
     };
+
+    // One tile (queries t * 64..) in slot b; the loads of tile tl go into
+    // slot 1 - b. MASKED applies the element mask: query past the end or
+    // key above the query (causal).
+    auto tile = [&](auto mtag, int t, int b, int tl) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        const uint32_t base = lds0 + b * SLOT, nbase = lds0 + (1 - b) * SLOT;
+        const int qbase = t * WBT;
+        const i32x4 rq = WideDma::rsrc(p.Q + head, tl * WBT, N, dh);
+        const i32x4 rg = WideDma::rsrc(p.dO + head, tl * WBT, N, dh);
+        // lse2 and -D of the 16 queries a lane's S / dP registers cover in
+        // step st: register r <-> query 32 st + 8 (r / 4) + 4 hi + r % 4
+        float lq[2][16];
+        f32x16 nd[2];
+        auto read_vec = [&](int st) __attribute__((always_inline)) {
+            const uint32_t a = lds0 + VEC + 2 * b * WBT * 4 + 4 * (32 * st + 4 * hi);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 lv = lds_f32x4_at(a + 32 * jj);
+                lq[st][4 * jj + 0] = lv.x; lq[st][4 * jj + 1] = lv.y;
+                lq[st][4 * jj + 2] = lv.z; lq[st][4 * jj + 3] = lv.w;
+                if constexpr (DO_DK) {
+                    const f32x4 dv4 = lds_f32x4_at(a + WBT * 4 + 32 * jj);
+                    nd[st][4 * jj + 0] = dv4.x; nd[st][4 * jj + 1] = dv4.y;
+                    nd[st][4 * jj + 2] = dv4.z; nd[st][4 * jj + 3] = dv4.w;
+                }
+            }
+        };
+        // operand of slot m: A slots take Q rows (S), alternating with dO
+        // rows (dP) for dK; C slot pr = (hh, db) takes dO^T (dV) or Q^T (dK)
+        // of queries 16 hh.. of its step
+        bf16x8 op[NSLOT];
+        auto read_op = [&](int m) __attribute__((always_inline)) {
+            if (m < 2 * NA) {
+                const int st = m / NA, i = m % NA;
+                const int kk = DO_DK ? i / 2 : i;
+                const uint32_t mat = (DO_DK && i % 2 == 1) ? TB : 0;
+                op[m] = wl.rows(base, mat + 32 * st * (2 * WD), kk);
+            } else {
+                const int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
+                op[m] = wl.trans(base, (DO_DV ? TB : 0) + (32 * st + 16 * (pr / NC)) * (2 * WD), pr % NC);
+            }
+        };
+        f32x16 s[2], dp[2];
+        float tx[2][16], pe[2][16], gm[2][16];
+        bf16x8 ob[2][2];  // the B operands of C: P (dV) or dS (dK)
+        auto stage = [&](int st, int k, int e) __attribute__((always_inline)) {
+            if (k == 0) {
+                tx[st][e] = fmaf(s[st][e], c, -lq[st][e]);
+                slot_done(tx[st][e]);
+            } else if (k == 1) {
+                float v = exp2_fast(tx[st][e]);
+                if (MASKED) {
+                    const int q = qbase + 32 * st + 8 * (e / 4) + 4 * hi + (e % 4);
+                    if (q >= N || (CAUSAL && key > q))
+                        v = 0.f;
+                }
+                pe[st][e] = v;
+                slot_done(v);
+            } else {
+                gm[st][e] = DO_DK ? pe[st][e] * dp[st][e] : pe[st][e];
+                if (e % 8 == 7) {
+                    bf16x8 pk;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        pk[i] = (__bf16)gm[st][e - 7 + i];
+                    ob[st][e / 8] = pk;
+                    slot_done(pk);
+                } else {
+                    slot_done(gm[st][e]);
+                }
+            }
+        };
+        read_vec(0);
+        static_for<PF>([&](auto mc) __attribute__((always_inline)) { read_op(decltype(mc)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NSLOT>([&](auto mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr (m < 2 * NA) {
+                constexpr int st = m / NA, i = m % NA;
+                constexpr int kk = DO_DK ? i / 2 : i;
+                if constexpr (DO_DK && i % 2 == 1)
+                    dp[st] = mfma32x32x16(op[m], vf[DO_DK ? kk : 0], kk == 0 ? nd[st] : dp[st]);
+                else
+                    s[st] = mfma32x32x16(op[m], kf[kk], kk == 0 ? f32x16{} : s[st]);
+            } else {
+                constexpr int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
+                mfma_acc_agpr_ordered(acc[pr % NC], op[m], ob[st][pr / NC]);
+            }
+            if constexpr (m + PF < NSLOT)
+                read_op(m + PF);
+            if constexpr (m == 4)
+                read_vec(1);
+            if constexpr (m < 8)
+                dma.issue_block(rq, m, nbase, wave);
+            else if constexpr (m < 16)
+                dma.issue_block(rg, m - 8, nbase + TB, wave);
+            else if constexpr (m == 16)
+                issue_vec(tl, 1 - b);
+            static_for<6>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int st = decltype(ic)::value / 3, k = 2 - decltype(ic)::value % 3;
+                constexpr int e = Plan::elem(m, st, k);
+                if constexpr (e >= 0)
+                    stage(st, k, e);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
     int t = next_tile(t_begin - 1);
-    if (t < p.ntile)
-        issue(t, 0);
+    if (t < p.ntile) {
+        dma.issue(p.Q + head, t * WBT, N, dh, lds0, wave);
+        dma.issue(p.dO + head, t * WBT, N, dh, lds0 + TB, wave);
+        issue_vec(t, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < WKK; ++kk) {
+        wait_loaded(kf[kk]);
+        if constexpr (DO_DK)
+            wait_loaded(vf[kk]);
+    }
     lds_dma_wait<0>();
     __syncthreads();
-    // Tile t computes from buffer `buf` while tile t+1 loads into the other,
-    // whose last reads ended before the previous barrier.
-    for (int buf = 0; t < p.ntile; buf ^= 1) {
+    // Whether this wave's elements of tile t need the element mask.
+    auto tile_masked = [&](int t) __attribute__((always_inline)) -> bool {
+        const int qbase = t * WBT;
+        return (qbase + WBT > N) || (CAUSAL && qbase < wk0 + 31);
+    };
+    int j = 0;
+    // One tile and the barrier after which the next one has landed (without
+    // a next tile the current one is loaded again, into the free slot).
+    auto step_tile = [&](auto mtag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
-        if (tn < p.ntile)
-            issue(tn, buf ^ 1);
-        const uint16_t *qs = reinterpret_cast<const uint16_t *>(smem + (2 * buf) * TB);
-        const uint16_t *gs = reinterpret_cast<const uint16_t *>(smem + (2 * buf + 1) * TB);
-        const float *ls = reinterpret_cast<const float *>(smem + VEC + (2 * buf) * WBT * 4);
-        const float *ns = reinterpret_cast<const float *>(smem + VEC + (2 * buf + 1) * WBT * 4);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int qr = 32 * h;  // tile rows (queries) of this step
-            // register r: query t * 64 + qr + 8 (r / 4) + 4 hi + r % 4, so
-            // registers 4 j .. 4 j + 3 are 4 consecutive queries
-            f32x16 s = f32x16{}, dp, lq;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 nv = *reinterpret_cast<const f32x4 *>(ns + qr + 8 * j + 4 * hi);
-                const f32x4 lv = *reinterpret_cast<const f32x4 *>(ls + qr + 8 * j + 4 * hi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dp[4 * j + e] = nv[e];
-                    lq[4 * j + e] = lv[e];
-                }
-            }
-#pragma unroll
-            for (int kk = 0; kk < WKK; ++kk) {
-                s = mfma32x32x16(wide_rows(qs, qr, kk, l32, hi), kf[kk], s);
-                if constexpr (DO_DK)
-                    dp = mfma32x32x16(wide_rows(gs, qr, kk, l32, hi), vf[kk], dp);
-            }
-            f32x16 pm, ds;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qi = qr + 8 * (r / 4) + 4 * hi + (r % 4);
-                const int q = t * WBT + qi;
-                float pe = exp2_fast(fmaf(s[r], p.c, -lq[r]));
-                if (q >= N || (CAUSAL && key > q))
-                    pe = 0.f;
-                pm[r] = pe;
-                if constexpr (DO_DK)
-                    ds[r] = pe * dp[r];
-            }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 pb = pack_bf16x8(pm, hh);
-                const bf16x8 sb = DO_DK ? pack_bf16x8(ds, hh) : bf16x8{};
-#pragma unroll
-                for (int db = 0; db < NC; ++db) {
-                    if constexpr (DO_DV)
-                        mfma_acc_agpr(dv[db], tr.read(gs, qr + 16 * hh, 32 * db), pb);
-                    if constexpr (DO_DK)
-                        mfma_acc_agpr(dk[db], tr.read(qs, qr + 16 * hh, 32 * db), sb);
-                }
-            }
-        }
-        mfma_drain();  // before the loop edge, where accumulators may be moved
+        tile(mtag, t, j % 2, tn < p.ntile ? tn : t);
+        mfma_drain();  // before the loop edges, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
+        ++j;
+    };
+    // Runs of masked and unmasked tiles each get a loop of their own
+    // (causal: the masked tiles are the first ones, on the diagonal, and
+    // the ragged last one).
+    while (t < p.ntile) {
+        while (t < p.ntile && tile_masked(t))
+            step_tile(std::true_type{});
+        while (t < p.ntile && !tile_masked(t))
+            step_tile(std::false_type{});
     }
-    mfma_drain();
 #pragma unroll
-    for (int db = 0; db < NC; ++db) {
-        if constexpr (DO_DK)
-            mfma_settle(dk[db]);
-        if constexpr (DO_DV)
-            mfma_settle(dv[db]);
-    }
+    for (int db = 0; db < NC; ++db)
+        mfma_settle(acc[db]);
     if (key < N) {
-        uint16_t *ok = p.dK + head + (size_t)key * dh;
-        uint16_t *ov = p.dV + head + (size_t)key * dh;
+        uint16_t *out = (DO_DK ? p.dK : p.dV) + head + (size_t)key * dh;
 #pragma unroll
-        for (int db = 0; db < NC; ++db) {
-            if constexpr (DO_DK)
-                wide_store(ok, dk[db], 32 * db, hi, p.scale, dh);
-            if constexpr (DO_DV)
-                wide_store(ov, dv[db], 32 * db, hi, 1.f, dh);
-        }
+        for (int db = 0; db < NC; ++db)
+            wide_store(out, acc[db], 32 * db, hi, DO_DK ? p.scale : 1.f, dh);
     }
 }
 

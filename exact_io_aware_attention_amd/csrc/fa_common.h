@@ -24,6 +24,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -84,6 +87,28 @@ __device__ __forceinline__ void wait_loaded(const bf16x8 &x)
 __device__ __forceinline__ void wait_loaded(float x)
 {
     asm volatile("" ::"v"(x));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 in order: an
+// unrolled loop whose index is a compile-time constant in the body, for
+// bodies too large for the loop unroller.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// Moves a long-lived MFMA operand into AGPRs: the MFMA reads its A and B
+// operands from AGPRs as well as VGPRs, so an operand used only by MFMAs
+// stays there and leaves the VGPRs to the values the vector ALU works on.
+__device__ __forceinline__ void keep_in_agpr(bf16x8 &x)
+{
+    asm volatile("" : "+a"(x));
 }
 
 // Wait states between the last AGPR-accumulating MFMA and any vector
@@ -177,8 +202,6 @@ __device__ __forceinline__ uint32_t opaque_addr(uint32_t x)
     asm("" : "+v"(x));
     return x;
 }
-// Waits until at most N of this wave's vector memory operations (the
-// direct loads included) are outstanding.
 // Workgroup barrier that waits for none of this wave's own LDS reads: a
 // caller reading, across it, data that no wave writes until a later barrier
 // keeps those reads in flight. Memory accesses are not moved across it.
@@ -251,6 +274,8 @@ __device__ __forceinline__ uint32_t drop_keep4(const DropParams &dp, uint32_t j0
 // padded head dimension.
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;
 
+// Waits until at most N of this wave's vector memory operations (the
+// direct loads included) are outstanding.
 template <int N>
 __device__ __forceinline__ void lds_dma_wait()
 {

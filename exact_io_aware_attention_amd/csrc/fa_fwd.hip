@@ -52,11 +52,8 @@
 //
 // Head dims below the kernel width (64, 128 or 256) are zero-padded: the
 // tile loads read zeros for the columns past dh and only dh columns are
-// stored. Past 128, O^T no longer fits one wave's registers beside the rest:
-// the 256-wide instance reads 256-deep Q and K rows but V and O in column
-// slices of 128, one per workgroup, so the two workgroups of a query block
-// both compute its scores (1.5x the contraction work of one pass), with 128
-// query rows per workgroup (one wave per SIMD).
+// stored. The 256-wide instance runs one wave per SIMD (128 query rows per
+// workgroup) with its 256 columns of O^T in AGPRs, V double-buffered.
 //
 // Masking: causal (key j visible to query i iff j <= i, nanhubrain.csdn.net
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
@@ -684,8 +681,8 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.drop.seed_hi = (uint32_t)(pr.drop_seed >> 32);
     fp.drop.inv_keep = pr.drop_inv_keep;
     // head dims up to 64 run in the 64-wide kernel, up to 128 in the
-    // 128-wide one, zero-padded; up to 256 with 256-deep scores and the O
-    // columns split over two workgroups of 128 (no dropout there)
+    // 128-wide one, up to 256 in the 256-wide one (no dropout there),
+    // zero-padded
     if (pr.d <= 64)
         return launch_fwd_d<64>(pr, fp);
     if (pr.d <= 128)

@@ -41,10 +41,9 @@
  *     64 < d <= 128 in the 128-wide ones, the columns past d taken as zero:
  *     the cost is that of the padded width); fa_fwd, fa_fwd_f32 and
  *     fa_bwd_f32, fa_bwd and fa_decode also take 128 < d <= 256 (fa_fwd:
- *     256-deep scores, O computed in two column halves that each recompute
- *     the scores, so 1.5x the contraction work; fa_bwd: dQ, dK, dV in
- *     column halves that each rebuild S and dP, 2.2x the contraction work,
- *     on a plainer schedule than the 128-wide kernels); the backward phase,
+ *     all 256 columns of O in one workgroup; fa_bwd: dQ in one pass and
+ *     dV and dK in a pass each, so S is rebuilt once more than at d <= 128,
+ *     1.6x the method's contraction work); the backward phase,
  *     dropout and FP8 entry points stay at d <= 128 and return
  *     FA_ERR_HEADDIM past it;
  *     N * d < 2^30; scale finite and > 0; causal is 0 or 1.

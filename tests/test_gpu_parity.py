@@ -517,9 +517,8 @@ def test_other_head_dims(precision, B, H, N, d, causal, sparse):
 
 
 WIDE_HEAD_DIMS = [
-    # (B, H, N, d, causal, sparse): 128 < d <= 256 -- the bf16 forward runs
-    # 256-deep scores with O in two column halves of 128 (the second half
-    # zero-padded past d), the fp32 path both directions
+    # (B, H, N, d, causal, sparse): 128 < d <= 256 -- the bf16 kernels run
+    # 256 wide (zero-padded past d), the fp32 path both directions
     (1, 2, 300, 256, True, False),
     (1, 1, 1000, 256, False, False),
     (1, 1, 260, 192, False, True),
@@ -562,8 +561,8 @@ def test_wide_head_dims_forward_bf16(B, H, N, d, causal, sparse):
 @pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS)
 def test_wide_head_dims_backward_bf16(B, H, N, d, causal, sparse):
     """fa_fwd + fa_bwd in bf16 at 128 < d <= 256 (the backward there runs
-    bwd_wide_dq_kernel and bwd_wide_dkdv_kernel on the matrix cores, in
-    column halves of 128), every output against the oracle."""
+    bwd_wide_dq_kernel and bwd_wide_dkdv_kernel on the matrix cores, all
+    256 columns of a gradient per pass), every output against the oracle."""
     seed = 6200 + N + d + 7 * causal + 3 * sparse
     q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype="bf16")
     nb = (N + 127) // 128
