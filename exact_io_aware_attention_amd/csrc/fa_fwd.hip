@@ -203,10 +203,12 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // distinct bank groups).
     auto k_swz = [](int r) -> int { return CPRK >= 16 ? (r % 16) : ((r / 2) % 8); };
     // V rows are only read by transpose reads: the aligned 4-chunk blocks of
-    // any 4 aligned rows land on distinct banks (f(r) / 4 distinct), for
-    // d = 64 with the row parity taking one bit's place.
+    // any 4 aligned rows land on distinct banks (f(r) / 4 distinct; the bank
+    // of a byte is its address modulo 256, so 512-byte rows take the
+    // 256-byte rows' pattern), for d = 64 with the row parity taking one
+    // bit's place.
     auto v_swz = [](int r) -> int {
-        return CPRV == 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
+        return CPRV >= 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
     };
     // Global rows are dh wide; chunks past dh read as zeros. V tiles hold
     // columns col0 .. col0 + DV - 1.
