@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_wide.hip", "fa_decode.hip", "fa_fp8.hip",
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_bwd.hip", "fa_bwd_wide.hip", "fa_decode.hip", "fa_fp8.hip",
            "fa_f32.hip", "fa_noalloc.hip"]
 
 COMMON_FLAGS = [

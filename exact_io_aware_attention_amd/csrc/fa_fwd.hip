@@ -50,10 +50,9 @@
 // A row that has seen no visible key keeps m = -inf and takes exponents
 // against 0, so no (-inf) - (-inf) arises; it ends with O = 0, LSE = -inf.
 //
-// Head dims below the kernel width (64, 128 or 256) are zero-padded: the
-// tile loads read zeros for the columns past dh and only dh columns are
-// stored. The 256-wide instance runs one wave per SIMD (128 query rows per
-// workgroup) with its 256 columns of O^T in AGPRs, V double-buffered.
+// Head dims below the kernel width (64 or 128) are zero-padded: the tile
+// loads read zeros for the columns past dh and only dh columns are stored.
+// Head dims past 128 run in the 256-wide kernel of fa_fwd_wide.hip.
 //
 // Masking: causal (key j visible to query i iff j <= i, nanhubrain.csdn.net
 // §三.1 tile set) -- key tiles wholly above the diagonal of the workgroup are
@@ -81,7 +80,7 @@ struct FwdParams {
     int nqb;      // query blocks per head
     int nkt;      // 64-key tiles per head
     int nmb;      // mask blocks per mask row
-    int items;    // B * H * nqb * (DK / DV)
+    int items;    // B * H * nqb
     int per_xcd;  // work items per XCD
     float c;      // scale * log2(e)
     DropParams drop;  // used by the DROP instances
@@ -102,12 +101,9 @@ __device__ __forceinline__ float bf16x8_sum_acc(bf16x8 p, float acc)
 }
 
 // DK: width of the Q and K rows the kernel reads (the depth of Q K^T); DV:
-// width of the slice of V and O columns one workgroup computes. DV < DK
-// splits the columns of O over DK / DV workgroups per query block, each
-// recomputing the scores: the head dim then grows past what one workgroup's
-// registers hold for O. W: waves per workgroup (32 query rows each). 8 (two
-// per SIMD) by default; 4 (one per SIMD) for 256-deep rows (512 registers
-// each, the part past 256 in AGPRs), for block-sparse masks (so that a
+// width of the V and O rows (equal to DK; head dims past 128 run in
+// fa_fwd_wide.hip). W: waves per workgroup (32 query rows each). 8 (two
+// per SIMD) by default; 4 (one per SIMD) for block-sparse masks (so that a
 // workgroup's 128 rows are one mask row and it loads exactly the key tiles
 // that row keeps; 256 rows would load the union of two rows' tiles and mask
 // out, wave by wave, what each row drops), and for problems too small to
@@ -121,35 +117,24 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     constexpr int BC = 64;          // keys per LDS tile
     constexpr int KK = DK / 16;     // depth steps of Q K^T
     constexpr int DB = DV / 32;     // 32-row blocks of O^T
-    constexpr int NSPLIT = DK / DV; // workgroups per query block
-    static_assert(NSPLIT * DV == DK && DV >= 64, "column split");
+    static_assert(DV == DK && DV >= 64 && DV <= 128, "64- or 128-wide rows");
     constexpr int CPRK = DK / 8;    // 16-byte chunks per K row
     constexpr int CPRV = DV / 8;    // 16-byte chunks per V tile row
     constexpr int LPWK = BC * DK * 2 / 1024 / W;  // 1 KB direct loads per wave per K tile
     constexpr int LPWV = BC * DV * 2 / 1024 / W;  // ... per V tile
     static_assert(LPWV >= 1, "tile too small for the direct-load layout");
-    // O wider than 128 columns: its accumulators live in AGPRs (asm MFMAs)
-    // and the V tiles are double-buffered, so that three K tiles and two V
-    // tiles fill the 160 KB of LDS; the buffer phases then repeat every 6
-    // tiles instead of 3.
-    constexpr bool WIDE_O = DV > 128;
-    constexpr int NBV = WIDE_O ? 2 : 3;
-    constexpr int U = WIDE_O ? 6 : 3;
+    constexpr int U = 3;  // buffer phases (tile j in buffers j % 3)
 
-    // LDS: three K tiles, then NBV V tiles.
+    // LDS: three K tiles, then three V tiles.
     constexpr uint32_t TBK = BC * DK * 2;  // bytes per K tile
     constexpr uint32_t TBV = BC * DV * 2;  // bytes per V tile
     constexpr uint32_t V_OFF = 3 * TBK;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + NBV * TBV];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[V_OFF + 3 * TBV];
     const uint32_t lds0 = lds_byte_addr(smem);
 
-    const int item0 = xcd_work_item(p.per_xcd);
-    if (item0 >= p.items)
+    const int item = xcd_work_item(p.per_xcd);
+    if (item >= p.items)
         return;
-    // the column slices of one query block are consecutive items (same XCD,
-    // sharing the K tiles in its L2)
-    const int item = item0 / NSPLIT;
-    const int col0 = (item0 - item * NSPLIT) * DV;  // first V / O column
     const int bh = item / p.nqb;
     const int qi = item - bh * p.nqb;
     const int qblk = CAUSAL ? (p.nqb - 1 - qi) : qi;  // causal: longest rows first
@@ -199,19 +184,16 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // of 1 KB block b writes chunk `lane` of the block, i.e. row
     // r = b * (64 / CPR) + lane / CPR, physical chunk lane % CPR, which holds
     // logical chunk (lane % CPR) ^ swz(r), CPR the chunks per row. K rows of
-    // 256 or 512 bytes: r % 16 (16 consecutive rows, one logical chunk, 16
+    // 256 bytes: r % 16 (16 consecutive rows, one logical chunk, 16
     // distinct bank groups).
     auto k_swz = [](int r) -> int { return CPRK >= 16 ? (r % 16) : ((r / 2) % 8); };
     // V rows are only read by transpose reads: the aligned 4-chunk blocks of
-    // any 4 aligned rows land on distinct banks (f(r) / 4 distinct; the bank
-    // of a byte is its address modulo 256, so 512-byte rows take the
-    // 256-byte rows' pattern), for d = 64 with the row parity taking one
-    // bit's place.
+    // any 4 aligned rows land on distinct banks (f(r) / 4 distinct), for
+    // d = 64 with the row parity taking one bit's place.
     auto v_swz = [](int r) -> int {
         return CPRV >= 16 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
     };
-    // Global rows are dh wide; chunks past dh read as zeros. V tiles hold
-    // columns col0 .. col0 + DV - 1.
+    // Global rows are dh wide; chunks past dh read as zeros.
     uint32_t kdma[LPWK], vdma[LPWV];
 #pragma unroll
     for (int i = 0; i < LPWK; ++i) {
@@ -223,24 +205,20 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     for (int i = 0; i < LPWV; ++i) {
         const int r = (wave * LPWV + i) * (64 / CPRV) + lane / CPRV;
         const int vc = (lane % CPRV) ^ v_swz(r);
-        vdma[i] = col0 + 8 * vc < dh ? 2 * (r * dh + 8 * vc) : kBufferOutOfRange;
+        vdma[i] = 8 * vc < dh ? 2 * (r * dh + 8 * vc) : kBufferOutOfRange;
     }
     // Rows past the end of the sequence read as zeros (the buffer resource
-    // ends at row N; for a column slice starting at col0 it starts col0
-    // elements in and ends as many before, at the end of the tensor's row
-    // N - 1) and are masked.
-    auto issue = [&](const uint16_t *src, auto const &off, uint32_t tile, int t, int c0)
+    // ends at row N) and are masked.
+    auto issue = [&](const uint16_t *src, auto const &off, uint32_t tile, int t)
                      __attribute__((always_inline)) {
         constexpr int L = sizeof(off) / sizeof(off[0]);
-        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * dh + c0, (uint32_t)(N - t * BC) * (2 * dh) - 2 * c0);
+        const i32x4 rs = buffer_rsrc(src + (size_t)t * BC * dh, (uint32_t)(N - t * BC) * (2 * dh));
 #pragma unroll
         for (int i = 0; i < L; ++i)
             lds_dma_buf_b128(rs, off[i], tile + (wave * L + i) * 1024);
     };
-    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TBK, t, 0); };
-    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) {
-        issue(Vh, vdma, lds0 + V_OFF + buf * TBV, t, col0);
-    };
+    auto issue_k = [&](int t, int buf) __attribute__((always_inline)) { issue(Kh, kdma, lds0 + buf * TBK, t); };
+    auto issue_v = [&](int t, int buf) __attribute__((always_inline)) { issue(Vh, vdma, lds0 + V_OFF + buf * TBV, t); };
 
     // Operand read addresses are this lane's byte address in buffer 0; the
     // buffer, which each unrolled iteration fixes, and the row block go into
@@ -309,14 +287,14 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     if (t0 >= t_end) {
         // no visible key tile at all (fully masked rows): O = 0, LSE = -inf
         if (row < N) {
-            uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
+            uint16_t *Oh = p.O + head + (size_t)row * dh;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (col0 + 32 * db + 8 * j + 4 * hi < dh)
+                    if (32 * db + 8 * j + 4 * hi < dh)
                         *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * j + 4 * hi) = uint2{0, 0};
-            if (hi == 0 && col0 == 0)
+            if (hi == 0)
                 p.LSE[(size_t)bh * N + row] = -INFINITY;
         }
         return;
@@ -326,8 +304,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     issue_v(t0, 0);
     if (t1 < t_end) {
         issue_k(t1, 1);
-        if (!WIDE_O)
-            issue_v(t1, 1);
+        issue_v(t1, 1);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -366,7 +343,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
     // The first K^T fragments of each half-step are read one half-step
     // early, so that its first MFMAs wait for no LDS read: here those of the
     // first half-step (tile t0's second 32 keys, buffer 0). Half the depth
-    // steps, at most 4 (256-deep rows: the registers of 8 would spill).
+    // steps.
     constexpr int NPRE = KK / 2 < 4 ? KK / 2 : 4;
     bf16x8 kpre[NPRE];
 #pragma unroll
@@ -389,21 +366,15 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         constexpr int P = decltype(ptag)::value;           // j % U
         constexpr uint32_t KB_CUR = (P % 3) * TBK;         // tile j's K buffer
         constexpr uint32_t KB_NXT = (P + 1) % 3 * TBK;     // tile j+1's
-        constexpr uint32_t VB_CUR = (P % NBV) * TBV;       // tile j's V buffer
+        constexpr uint32_t VB_CUR = (P % 3) * TBV;         // tile j's V buffer
         constexpr int KB_NN = (P + 2) % 3;                 // tile j+2's
         const int tn = t1;                                   // tile j+1
         const int tnn = tn < t_end ? next_tile(tn) : t_end;  // tile j+2
         // K and V of tile j+2 replace tile j-1's, last read before the
         // previous barrier; tile j+1's were issued one iteration ago (its K
-        // has landed, its V may still be in flight). With two V buffers,
-        // tile j+1's V replaces tile j-1's now and lands by the barrier.
+        // has landed, its V may still be in flight).
         const bool more = tnn < t_end;
-        if constexpr (WIDE_O) {
-            if (tn < t_end)
-                issue_v(tn, (P + 1) % 2);
-            if (more)
-                issue_k(tnn, KB_NN);
-        } else if (more) {
+        if (more) {
             issue_k(tnn, KB_NN);
             issue_v(tnn, KB_NN);
         }
@@ -425,13 +396,6 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 nmref = (m == -INFINITY) ? 0.f : -m;
                 l *= alpha;
                 lb *= alpha;
-                if constexpr (WIDE_O) {
-                    // the accumulators are read once their MFMAs drained
-                    mfma_drain();
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        mfma_settle(o[db]);
-                }
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -500,23 +464,15 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                 ls1 += e1;
             }
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                if constexpr (WIDE_O)
-                    mfma_acc_agpr(o[db], vf[0][db], p0);
-                else
-                    o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+                o[db] = mfma32x32x16(vf[0][db], p0, o[db]);
             l += ls0 + ls1;
             const bf16x8 p1 = pack_bf16x8(s_cur, 1);
             if constexpr (RSUM)
                 lb = bf16x8_sum_acc(p1, bf16x8_sum_acc(p0, lb));
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                if constexpr (WIDE_O)
-                    mfma_acc_agpr(o[db], vf[1][db], p1);
-                else
-                    o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+                o[db] = mfma32x32x16(vf[1][db], p1, o[db]);
             // the next half-step's first K^T fragments: tile j+1's first 32
             // keys, then its second 32 (visible since the last barrier). The
             // latter stay in flight across the barrier below, which then must
@@ -548,9 +504,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         // last, may still be in flight); the barrier extends that to all
         // waves. The next iteration reads tile j+2's K from its second
         // half-step on and its V one iteration later.
-        if constexpr (WIDE_O)
-            mfma_drain();  // before the loop edges, where accumulators may be moved
-        if (more && !WIDE_O)
+        if (more)
             lds_dma_wait<LPWV>();
         else
             lds_dma_wait<0>();
@@ -574,7 +528,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
             }                                                               \
         }
         for (;;) {
-            FA_FWD_PHASE(0) FA_FWD_PHASE(1) FA_FWD_PHASE(2) FA_FWD_PHASE(3) FA_FWD_PHASE(4) FA_FWD_PHASE(5)
+            FA_FWD_PHASE(0) FA_FWD_PHASE(1) FA_FWD_PHASE(2)
         }
 #undef FA_FWD_PHASE
     };
@@ -585,22 +539,16 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
 
     // Epilogue: O = O^T / lb (transposed back per lane), LSE from l in
     // natural log.
-    if constexpr (WIDE_O) {
-        mfma_drain();
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            mfma_settle(o[db]);
-    }
     const float lt = halves_sum(l);
     const float lbt = RSUM ? halves_sum(lb) : lt;
     if (row < N) {
         const float inv = lbt > 0.f ? 1.f / lbt : 0.f;
-        uint16_t *Oh = p.O + head + (size_t)row * dh + col0;
+        uint16_t *Oh = p.O + head + (size_t)row * dh;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                if (col0 + 32 * db + 8 * jj + 4 * hi >= dh)
+                if (32 * db + 8 * jj + 4 * hi >= dh)
                     continue;
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16_bits(o[db][4 * jj + 0] * inv) |
@@ -609,7 +557,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
                        ((uint32_t)f32_to_bf16_bits(o[db][4 * jj + 3] * inv) << 16);
                 *reinterpret_cast<uint2 *>(Oh + 32 * db + 8 * jj + 4 * hi) = pk;
             }
-        if (hi == 0 && col0 == 0)
+        if (hi == 0)
             p.LSE[(size_t)bh * N + row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
     }
 }
@@ -620,7 +568,7 @@ static hipError_t launch_fwd_w(const Problem &pr, const FwdParams &fp0)
     FwdParams fp = fp0;
     constexpr int BR = 32 * W;  // query rows per workgroup
     fp.nqb = (pr.N + BR - 1) / BR;
-    fp.items = pr.B * pr.H * fp.nqb * (DK / DV);
+    fp.items = pr.B * pr.H * fp.nqb;
     fp.per_xcd = (fp.items + kXcds - 1) / kXcds;
     const int grid = fp.per_xcd * kXcds;
     hipLaunchKernelGGL((fwd_bf16_kernel<DK, DV, CAUSAL, SPARSE, DROP, W>), dim3(grid), dim3(64 * W), 0,
@@ -633,7 +581,7 @@ constexpr int kCus = 256;  // MI355X compute units
 template <int DK, int DV, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const Problem &pr, const FwdParams &fp)
 {
-    if constexpr (DK > 128 || SPARSE) {
+    if constexpr (SPARSE) {
         return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 4>(pr, fp);
     } else if constexpr (DROP) {
         return launch_fwd_w<DK, DV, CAUSAL, SPARSE, DROP, 8>(pr, fp);
@@ -683,7 +631,7 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
     fp.drop.seed_hi = (uint32_t)(pr.drop_seed >> 32);
     fp.drop.inv_keep = pr.drop_inv_keep;
     // head dims up to 64 run in the 64-wide kernel, up to 128 in the
-    // 128-wide one, up to 256 in the 256-wide one (no dropout there),
+    // 128-wide one, up to 256 in the 256-wide kernel (no dropout there),
     // zero-padded
     if (pr.d <= 64)
         return launch_fwd_d<64>(pr, fp);
@@ -691,7 +639,7 @@ hipError_t launch_fwd_bf16(const Problem &pr, const uint16_t *Q, const uint16_t 
         return launch_fwd_d<128>(pr, fp);
     if (pr.dropout)
         return hipErrorInvalidValue;
-    return launch_fwd_dd<256, 256, false>(pr, fp);
+    return launch_fwd_bf16_wide(pr, Q, K, V, O, LSE);
 }
 
 }  // namespace fa

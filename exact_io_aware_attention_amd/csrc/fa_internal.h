@@ -84,8 +84,11 @@ hipError_t launch_fwd_fp8(const Fp8Problem &p, const uint8_t *Q, const uint8_t *
 
 hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, const float *V,
                           float *O, float *LSE);
-// bf16 backward for head dims in (128, 256] on the matrix cores (column
-// halves of the gradients, S and dP rebuilt over the full depth by each).
+// bf16 forward and backward for head dims in (128, 256] on the matrix
+// cores (256-wide kernels; the backward rebuilds S in each of its dQ, dV
+// and dK passes).
+hipError_t launch_fwd_bf16_wide(const Problem &p, const uint16_t *Q, const uint16_t *K,
+                                const uint16_t *V, uint16_t *O, float *LSE);
 hipError_t launch_bwd_bf16_wide(const Problem &p, const uint16_t *dO, const uint16_t *Q,
                                 const uint16_t *K, const uint16_t *V, const uint16_t *O,
                                 const float *LSE, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
