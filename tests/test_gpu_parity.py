@@ -524,6 +524,8 @@ WIDE_HEAD_DIMS = [
     (1, 1, 260, 192, False, True),
     (2, 1, 200, 136, True, False),
     (1, 1, 64, 248, True, True),
+    (1, 2, 1100, 256, True, False),   # 18 key tiles: masked and unmasked loops, ragged end
+    (1, 1, 1000, 200, True, True),
 ]
 
 
@@ -575,6 +577,20 @@ def test_wide_head_dims_backward_bf16(B, H, N, d, causal, sparse):
     print(f"bf16 fwd+bwd B={B} H={H} N={N} d={d} causal={causal} sparse={sparse}", flush=True)
     got = _got(*gu.gpu_forward_backward(q, k, v, do, scale, causal, mask, "bf16"))
     gu.check_outputs("bf16", got, _ref_all(q, k, v, do, scale, causal, mask))
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 2, 1100, 256, True), (1, 1, 700, 256, False)])
+def test_wide_head_dims_sharp_bf16(B, H, N, d, causal):
+    """fa_fwd + fa_bwd in bf16 at d = 256 with Q and K x 3: the row maxima
+    grow by several times the rescale slack along each row, so the 256-wide
+    forward takes its rescale path (O's accumulators read back from AGPRs)
+    after the first block too; every output against the oracle."""
+    seed = 6300 + N + 7 * causal
+    q, k, v, do = syn.random_inputs(B, H, N, d, seed, dtype="bf16", qk_mult=3.0)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    print(f"bf16 sharp fwd+bwd B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    got = _got(*gu.gpu_forward_backward(q, k, v, do, scale, causal, None, "bf16"))
+    gu.check_outputs("bf16", got, _ref_all(q, k, v, do, scale, causal, None))
 
 
 @pytest.mark.parametrize("B,H,N,d,causal,sparse", WIDE_HEAD_DIMS[:3])
