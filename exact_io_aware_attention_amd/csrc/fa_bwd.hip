@@ -12,11 +12,11 @@
 // Kernels, all on the caller's stream:
 //   1. bwd_pre:  -D and LSE * log2(e) per row (bandwidth-bound, one pass
 //      over dO and O);
-//   2. bwd_dq:   one workgroup per 128 (d = 128) or 256 (d = 64) query
-//      rows, key/value tiles streamed through LDS; recomputes S^T and dP^T,
+//   2. bwd_dq:   one workgroup per 128 query rows, key/value tiles
+//      streamed through LDS; recomputes S^T and dP^T,
 //      forms dS^T and accumulates dQ^T = K^T dS^T (lane = query, as in the
 //      forward);
-//   3. bwd_dkdv: one workgroup per 128 or 256 keys (K and V rows in
+//   3. bwd_dkdv: one workgroup per 128 keys (K and V rows in
 //      registers), query tiles streamed through LDS; recomputes S and dP,
 //      accumulates dV^T = dO^T P and dK^T = Q^T dS (lane = key).
 // Splitting dQ from dK/dV recomputes S and dP once more (7 contractions
@@ -68,8 +68,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const uint16_t *dO, const 
 // ------------------------------------------------------- shared pieces ---
 //
 // Both main kernels run 4 waves per workgroup, one per SIMD (up to 512
-// registers each), with 32 rows per wave for d = 128 and 64 for d = 64 (so
-// each operand fragment read from LDS feeds two MFMAs). The long-lived
+// registers each), with 32 rows per wave. The long-lived
 // accumulators (dQ^T, or dK^T and dV^T) stay in AGPRs; operands, S, dP and
 // the softmax temporaries use the VGPRs.
 //
