@@ -995,6 +995,10 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
 {
+    if constexpr (D == 128) {
+        if (!pr.dropout)
+            return launch_bwd_dkdv_bf16_slot(pr, b.dO, b.Q, b.K, b.V, b.dK, b.dV, b.ndelta, b.lse2);
+    }
     DkvParams kp{};
     kp.dO = b.dO; kp.Q = b.Q; kp.K = b.K; kp.V = b.V;
     kp.ndelta = b.ndelta; kp.lse2 = b.lse2; kp.dK = b.dK; kp.dV = b.dV; kp.mask = pr.mask;

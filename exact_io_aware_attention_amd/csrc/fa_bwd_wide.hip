@@ -80,6 +80,17 @@ struct WidePlan {
     }
 };
 
+// One workgroup per 128 query rows; each wave holds 32 query rows of Q and
+// dO, the B operands of S^T and dP^T, in AGPRs beside its eight dQ^T
+// accumulators, so that the VGPRs hold the scores, the softmax and the
+// operands read ahead. Per 32 keys (a step):
+//   A: S^T = K Q^T and dP^T = V dO^T (lane = query; 16 MFMA pairs, K and V
+//      rows read from LDS);
+//   B: P^T = 2^(c s - lse2), dS^T = P^T o (dP^T - D) (vector ALU);
+//   C: dQ^T += K^T dS^T over all 256 columns (16 MFMAs, K^T by transpose
+//      reads).
+// Every step ends inside its tile (WidePlan), so two LDS slots suffice: the
+// next tile streams into the other one, a load per slot of the first step.
 template <bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p)
 {
@@ -271,28 +282,39 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     }
 }
 
-// One workgroup per 128 keys; each wave holds 32 keys of K (and of V for
-// dK), the B operands of S (and dP), in AGPRs beside the accumulators of
-// one 256-column gradient. The accumulators of both gradients do not fit
-// beside the K and V rows, so they take a pass each (5 contractions of
-// work; 6 for both gradients in column halves that each rebuild S and dP).
-// Per 32 queries (a step), lane = key:
+// Which gradients a dK/dV pass accumulates.
+enum WidePass { kPassDV = 0, kPassDK = 1, kPassBoth = 2 };
+
+// One workgroup per 128 keys; each wave holds 32 keys of K (and of V when
+// dP is built), the B operands of S (and dP), in AGPRs beside the
+// accumulators of its gradients. At D = 256 the accumulators of both
+// gradients do not fit beside the K and V rows, so dV and dK take a pass
+// each (5 contractions of work; 6 for both gradients in column halves that
+// each rebuild S and dP); at D = 128 one pass accumulates both (the
+// method's 4 contractions of this side). Per 32 queries (a step), lane =
+// key:
 //   A: S = Q K^T (and dP - D = dO V^T - D for dK, the accumulator starting
 //      from -D); Q and dO rows read from LDS;
 //   B: P = 2^(c s - lse2) (and dS = P o (dP - D)) (vector ALU);
-//   C: dV^T += dO^T P, or dK^T += Q^T dS (16 MFMAs, transpose reads).
+//   C: dV^T += dO^T P and / or dK^T += Q^T dS (transpose reads; with both,
+//      the two alternate slot by slot).
 // The slots follow WidePlan, as in the dQ kernel.
-template <bool CAUSAL, bool SPARSE, bool DV>
+template <int D, int PASS, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams p)
 {
-    constexpr bool DO_DV = DV, DO_DK = !DV;
-    constexpr int NC = 2 * WDB;            // 32-column blocks of the gradient
-    constexpr uint32_t TB = WBT * WD * 2;  // bytes per tile
+    constexpr bool DO_DV = PASS != kPassDK, DO_DK = PASS != kPassDV;
+    constexpr int KK = D / 16;             // 16-deep steps of S and dP
+    constexpr int NC = D / 32;             // 32-column blocks of a gradient
+    constexpr uint32_t ROW = 2 * D;        // bytes per tile row
+    constexpr uint32_t TB = WBT * ROW;     // bytes per tile
     constexpr uint32_t SLOT = 2 * TB;      // [Q tile | dO tile]
     constexpr uint32_t VEC = 2 * SLOT;     // then lse2 and -D rows per slot
-    constexpr int NA = DO_DK ? 2 * WKK : WKK;
-    using Plan = WidePlan<NA, 2 * NC>;
-    constexpr int NSLOT = Plan::NSLOT, PF = Plan::PF;
+    constexpr int NA = DO_DK ? 2 * KK : KK;                  // A MFMAs per step
+    constexpr int NCS = (DO_DV && DO_DK ? 2 : 1) * 2 * NC;   // C MFMAs per step
+    using Plan = WidePlan<NA, NCS>;
+    using Lane = WideLaneT<D>;
+    using Dma = WideDmaT<D>;
+    constexpr int NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[VEC + 4 * WBT * 4];
     const uint32_t lds0 = lds_byte_addr(smem);
 
@@ -310,11 +332,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     const int wk0 = k0 + 32 * wave;  // this wave's first key
     const int key = wk0 + l32;       // this lane's key
     const size_t head = (size_t)bh * N * dh;
-    const WideLane wl(lane);
+    const Lane wl(lane);
 
-    bf16x8 kf[WKK], vf[DO_DK ? WKK : 1];
+    bf16x8 kf[KK], vf[DO_DK ? KK : 1];
 #pragma unroll
-    for (int kk = 0; kk < WKK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
         const bool in = key < N && 16 * kk + 8 * hi < dh;
         kf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.K + head + (size_t)key * dh + 16 * kk + 8 * hi)
                     : bf16x8{};
@@ -326,10 +348,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         }
     }
 
-    f32x16 acc[NC];  // dK^T or dV^T
+    f32x16 acc_v[DO_DV ? NC : 1], acc_k[DO_DK ? NC : 1];  // dV^T, dK^T
 #pragma unroll
-    for (int db = 0; db < NC; ++db)
-        acc[db] = f32x16{};
+    for (int db = 0; db < NC; ++db) {
+        if constexpr (DO_DV)
+            acc_v[db] = f32x16{};
+        if constexpr (DO_DK)
+            acc_k[db] = f32x16{};
+    }
 
     const int t_begin = CAUSAL ? k0 / WBT : 0;
     // query tiles the workgroup needs (one mask column, so uniform over it)
@@ -339,15 +365,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     auto next_tile = [&](int t) -> int {
         return SPARSE ? next_kept_tile(mc, t + 1, p.ntile, kMaskBlock / WBT) : t + 1;
     };
-    const WideDma dma(wave, lane, dh);
-    // the statistics rows of tile t into slot b (rows past N read as zeros:
-    // their queries are masked)
+    const Dma dma(wave, lane, dh);
+    // the statistics rows of tile t into slot b: lse2 by the even waves, -D
+    // by the odd ones (the same bytes twice, no branch in the slot plan;
+    // rows past N read as zeros: their queries are masked)
     auto issue_vec = [&](int t, int b) __attribute__((always_inline)) {
-        if (wave < 2) {
-            const float *v = (wave == 0 ? p.lse2 : p.ndelta) + (size_t)bh * N + t * WBT;
-            const i32x4 rs = buffer_rsrc(v, (uint32_t)(N - t * WBT) * 4);
-            lds_dma_buf_b32(rs, 4 * lane, lds0 + VEC + (2 * b + wave) * WBT * 4);
-        }
+        const float *v = ((wave & 1) ? p.ndelta : p.lse2) + (size_t)bh * N + t * WBT;
+        const i32x4 rs = buffer_rsrc(v, (uint32_t)(N - t * WBT) * 4);
+        lds_dma_buf_b32(rs, 4 * lane, lds0 + VEC + (2 * b + (wave & 1)) * WBT * 4);
     };
 
     // One tile (queries t * 64..) in slot b; the loads of tile tl go into
@@ -357,8 +382,8 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         constexpr bool MASKED = decltype(mtag)::value;
         const uint32_t base = lds0 + b * SLOT, nbase = lds0 + (1 - b) * SLOT;
         const int qbase = t * WBT;
-        const i32x4 rq = WideDma::rsrc(p.Q + head, tl * WBT, N, dh);
-        const i32x4 rg = WideDma::rsrc(p.dO + head, tl * WBT, N, dh);
+        const i32x4 rq = Dma::rsrc(p.Q + head, tl * WBT, N, dh);
+        const i32x4 rg = Dma::rsrc(p.dO + head, tl * WBT, N, dh);
         // lse2 and -D of the 16 queries a lane's S / dP registers cover in
         // step st: register r <-> query 32 st + 8 (r / 4) + 4 hi + r % 4
         float lq[2][16];
@@ -377,24 +402,38 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 }
             }
         };
+        // C slot ci of a step: pair pr = ci / 2 (both gradients) or ci, the
+        // gradient of the slot, and the operand half hh = pr / NC
+        auto c_slot = [](int ci, int &pr, bool &is_v) __attribute__((always_inline)) {
+            if (DO_DV && DO_DK) {
+                pr = ci / 2;
+                is_v = ci % 2 == 0;
+            } else {
+                pr = ci;
+                is_v = DO_DV;
+            }
+        };
         // operand of slot m: A slots take Q rows (S), alternating with dO
-        // rows (dP) for dK; C slot pr = (hh, db) takes dO^T (dV) or Q^T (dK)
-        // of queries 16 hh.. of its step
+        // rows (dP) when dP is built; C slots take dO^T (dV) or Q^T (dK)
+        // of queries 16 hh.. of their step
         bf16x8 op[NSLOT];
         auto read_op = [&](int m) __attribute__((always_inline)) {
             if (m < 2 * NA) {
                 const int st = m / NA, i = m % NA;
                 const int kk = DO_DK ? i / 2 : i;
                 const uint32_t mat = (DO_DK && i % 2 == 1) ? TB : 0;
-                op[m] = wl.rows(base, mat + 32 * st * (2 * WD), kk);
+                op[m] = wl.rows(base, mat + 32 * st * ROW, kk);
             } else {
-                const int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
-                op[m] = wl.trans(base, (DO_DV ? TB : 0) + (32 * st + 16 * (pr / NC)) * (2 * WD), pr % NC);
+                const int st = (m - 2 * NA) / NCS;
+                int pr;
+                bool is_v;
+                c_slot((m - 2 * NA) % NCS, pr, is_v);
+                op[m] = wl.trans(base, (is_v ? TB : 0) + (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
             }
         };
         f32x16 s[2], dp[2];
-        float tx[2][16], pe[2][16], gm[2][16];
-        bf16x8 ob[2][2];  // the B operands of C: P (dV) or dS (dK)
+        float tx[2][16], pe[2][16], gs[2][16];
+        bf16x8 ob_v[2][2], ob_k[2][2];  // the B operands of C: P (dV), dS (dK)
         auto stage = [&](int st, int k, int e) __attribute__((always_inline)) {
             if (k == 0) {
                 tx[st][e] = fmaf(s[st][e], c, -lq[st][e]);
@@ -409,16 +448,27 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 pe[st][e] = v;
                 slot_done(v);
             } else {
-                gm[st][e] = DO_DK ? pe[st][e] * dp[st][e] : pe[st][e];
+                if constexpr (DO_DK)
+                    gs[st][e] = pe[st][e] * dp[st][e];
                 if (e % 8 == 7) {
-                    bf16x8 pk;
+                    if constexpr (DO_DV) {
+                        bf16x8 pk;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        pk[i] = (__bf16)gm[st][e - 7 + i];
-                    ob[st][e / 8] = pk;
-                    slot_done(pk);
-                } else {
-                    slot_done(gm[st][e]);
+                        for (int i = 0; i < 8; ++i)
+                            pk[i] = (__bf16)pe[st][e - 7 + i];
+                        ob_v[st][e / 8] = pk;
+                        slot_done(pk);
+                    }
+                    if constexpr (DO_DK) {
+                        bf16x8 sk;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            sk[i] = (__bf16)gs[st][e - 7 + i];
+                        ob_k[st][e / 8] = sk;
+                        slot_done(sk);
+                    }
+                } else if constexpr (DO_DK) {
+                    slot_done(gs[st][e]);
                 }
             }
         };
@@ -435,18 +485,23 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 else
                     s[st] = mfma32x32x16(op[m], kf[kk], kk == 0 ? f32x16{} : s[st]);
             } else {
-                constexpr int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
-                mfma_acc_agpr_ordered(acc[pr % NC], op[m], ob[st][pr / NC]);
+                constexpr int st = (m - 2 * NA) / NCS, ci = (m - 2 * NA) % NCS;
+                constexpr int pr = (DO_DV && DO_DK) ? ci / 2 : ci;
+                constexpr bool is_v = (DO_DV && DO_DK) ? ci % 2 == 0 : DO_DV;
+                if constexpr (is_v)
+                    mfma_acc_agpr_ordered(acc_v[pr % NC], op[m], ob_v[st][pr / NC]);
+                else
+                    mfma_acc_agpr_ordered(acc_k[pr % NC], op[m], ob_k[st][pr / NC]);
             }
             if constexpr (m + PF < NSLOT)
                 read_op(m + PF);
             if constexpr (m == 4)
                 read_vec(1);
-            if constexpr (m < 8)
+            if constexpr (m < LPW)
                 dma.issue_block(rq, m, nbase, wave);
-            else if constexpr (m < 16)
-                dma.issue_block(rg, m - 8, nbase + TB, wave);
-            else if constexpr (m == 16)
+            else if constexpr (m < 2 * LPW)
+                dma.issue_block(rg, m - LPW, nbase + TB, wave);
+            else if constexpr (m == 2 * LPW)
                 issue_vec(tl, 1 - b);
             static_for<6>([&](auto ic) __attribute__((always_inline)) {
                 constexpr int st = decltype(ic)::value / 3, k = 2 - decltype(ic)::value % 3;
@@ -465,7 +520,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         issue_vec(t, 0);
     }
 #pragma unroll
-    for (int kk = 0; kk < WKK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
         wait_loaded(kf[kk]);
         if constexpr (DO_DK)
             wait_loaded(vf[kk]);
@@ -499,13 +554,20 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
             step_tile(std::false_type{});
     }
 #pragma unroll
-    for (int db = 0; db < NC; ++db)
-        mfma_settle(acc[db]);
+    for (int db = 0; db < NC; ++db) {
+        if constexpr (DO_DV)
+            mfma_settle(acc_v[db]);
+        if constexpr (DO_DK)
+            mfma_settle(acc_k[db]);
+    }
     if (key < N) {
-        uint16_t *out = (DO_DK ? p.dK : p.dV) + head + (size_t)key * dh;
 #pragma unroll
-        for (int db = 0; db < NC; ++db)
-            wide_store(out, acc[db], 32 * db, hi, DO_DK ? p.scale : 1.f, dh);
+        for (int db = 0; db < NC; ++db) {
+            if constexpr (DO_DV)
+                wide_store(p.dV + head + (size_t)key * dh, acc_v[db], 32 * db, hi, 1.f, dh);
+            if constexpr (DO_DK)
+                wide_store(p.dK + head + (size_t)key * dh, acc_k[db], 32 * db, hi, p.scale, dh);
+        }
     }
 }
 
@@ -517,15 +579,52 @@ hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, true>), grid, block, 0, stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<WD, kPassDV, CAUSAL, SPARSE>), grid, block, 0, stream, wp);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<CAUSAL, SPARSE, false>), grid, block, 0, stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<WD, kPassDK, CAUSAL, SPARSE>), grid, block, 0, stream, wp);
+    return hipGetLastError();
+}
+
+template <bool CAUSAL, bool SPARSE>
+hipError_t launch_dkdv128(const WideParams &wp, hipStream_t stream)
+{
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<128, kPassBoth, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds),
+                       dim3(WW * kWave), 0, stream, wp);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_bwd_dkdv_bf16_slot(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
+                                     const uint16_t *K, const uint16_t *V, uint16_t *dK, uint16_t *dV,
+                                     const float *ndelta, const float *lse2)
+{
+    WideParams wp{};
+    wp.Q = Q;
+    wp.K = K;
+    wp.V = V;
+    wp.dO = dO;
+    wp.dK = dK;
+    wp.dV = dV;
+    wp.ndelta = ndelta;
+    wp.lse2 = lse2;
+    wp.mask = pr.mask;
+    wp.N = pr.N;
+    wp.dh = pr.d;
+    wp.nblk = (pr.N + WROWS - 1) / WROWS;
+    wp.ntile = (pr.N + WBT - 1) / WBT;
+    wp.nmb = (pr.N + kMaskBlock - 1) / kMaskBlock;
+    wp.items = pr.B * pr.H * wp.nblk;
+    wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
+    wp.c = pr.scale * kLog2e;
+    wp.scale = pr.scale;
+    const bool sparse = pr.mask != nullptr;
+    if (pr.causal)
+        return sparse ? launch_dkdv128<true, true>(wp, pr.stream) : launch_dkdv128<true, false>(wp, pr.stream);
+    return sparse ? launch_dkdv128<false, true>(wp, pr.stream) : launch_dkdv128<false, false>(wp, pr.stream);
+}
 
 hipError_t launch_bwd_bf16_wide(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
                                 const uint16_t *K, const uint16_t *V, const uint16_t *O,
