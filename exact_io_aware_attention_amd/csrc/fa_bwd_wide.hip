@@ -58,26 +58,41 @@ struct WideParams {
 // below: A(0), A(1) with B(0) spread over its MFMAs, C(0) with B(1), C(1),
 // one MFMA per slot. A step's softmax elements pass three stages (F: the
 // exponent argument, E: the exponential and the mask, M: the product and
-// the packing into MFMA operands) in consecutive slots, element e of B(0)
-// starting at slot NA + R0 e, of B(1) at slot 2 NA + e, so that no slot
-// waits on a value it produced itself; the last stages run into the first
-// slots of the next phase, whose MFMAs take the second operand half (the
-// elements 8..15) only from their ninth slot on.
+// the packing into MFMA operands) in consecutive slots; element e of B(0)
+// starts at slot NA + e NA / 16, of B(1) at slot 2 NA + e NCS / 16 (two
+// elements a slot when C has 8 MFMAs), so that no slot waits on a value it
+// produced itself. The last stages run into the next phase, whose MFMAs
+// take the operand half of elements 8..15 only from their second half on
+// (checked below).
 template <int NA, int NCS>
 struct WidePlan {
     static constexpr int NSLOT = 2 * NA + 2 * NCS;
-    static constexpr int R0 = NA / 16;  // slots per element of B(0)
-    static_assert(R0 * 16 == NA && NCS == 16, "slot plan");
-    static constexpr int PF = 5;        // operand reads issued this many slots ahead
-    // element of step st whose stage k (0 F, 1 E, 2 M) falls into slot m,
-    // or -1
-    __device__ static constexpr int elem(int m, int st, int k)
+    static constexpr int PF = 5;  // operand reads issued this many slots ahead
+    // slot of stage k (0 F, 1 E, 2 M) of element e of step st
+    __device__ static constexpr int slot(int st, int k, int e)
     {
-        const int first = st == 0 ? NA : 2 * NA;
-        const int r = st == 0 ? R0 : 1;
-        const int d = m - first - k;
-        return (d >= 0 && d % r == 0 && d / r < 16) ? d / r : -1;
+        return (st == 0 ? NA + e * NA / 16 : 2 * NA + e * NCS / 16) + k;
     }
+    // the elements of step st whose stage k falls into slot m: the j-th
+    // (j < 2) of them, or 16 when there are fewer
+    __device__ static constexpr int elem(int m, int st, int k, int j)
+    {
+        const int S = st == 0 ? NA : NCS;
+        const int d = m - k - (st == 0 ? NA : 2 * NA);
+        if (d < 0)
+            return 16;
+        const int lo = (16 * d + S - 1) / S, hi = (16 * (d + 1) + S - 1) / S;
+        return (lo + j < hi && lo + j < 16) ? lo + j : 16;
+    }
+    // each step's two operand halves (elements 0..7, 8..15) are packed
+    // before the first C MFMA that takes them
+    static constexpr bool ordered()
+    {
+        return NA % 16 == 0 && NCS % 8 == 0 && slot(0, 0, 0) >= NA && slot(0, 2, 7) < 2 * NA &&
+               slot(0, 2, 15) < 2 * NA + NCS / 2 && slot(1, 0, 0) >= 2 * NA &&
+               slot(1, 2, 7) < 2 * NA + NCS && slot(1, 2, 15) < 2 * NA + NCS + NCS / 2;
+    }
+    static_assert(ordered(), "slot plan");
 };
 
 // One workgroup per 128 query rows; each wave holds 32 query rows of Q and
@@ -91,14 +106,18 @@ struct WidePlan {
 //      reads).
 // Every step ends inside its tile (WidePlan), so two LDS slots suffice: the
 // next tile streams into the other one, a load per slot of the first step.
-template <bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p)
 {
-    constexpr int NC = 2 * WDB;            // 32-column blocks of dQ
-    constexpr uint32_t TB = WBT * WD * 2;  // bytes per tile
+    constexpr int KK = D / 16;             // 16-deep steps of S^T and dP^T
+    constexpr int NC = D / 32;             // 32-column blocks of dQ
+    constexpr uint32_t ROW = 2 * D;        // bytes per tile row
+    constexpr uint32_t TB = WBT * ROW;     // bytes per tile
     constexpr uint32_t SLOT = 2 * TB;      // [K tile | V tile]
-    using Plan = WidePlan<2 * WKK, 2 * NC>;
-    constexpr int NA = 2 * WKK, NSLOT = Plan::NSLOT, PF = Plan::PF;
+    using Plan = WidePlan<2 * KK, 2 * NC>;
+    using Lane = WideLaneT<D>;
+    using Dma = WideDmaT<D>;
+    constexpr int NA = 2 * KK, NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLOT];
     const uint32_t lds0 = lds_byte_addr(smem);
 
@@ -117,11 +136,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     const int wr0 = q0 + 32 * wave;  // this wave's first query
     const int row = wr0 + l32;       // this lane's query
     const size_t head = (size_t)bh * N * dh;
-    const WideLane wl(lane);
+    const Lane wl(lane);
 
-    bf16x8 qf[WKK], gf[WKK];
+    bf16x8 qf[KK], gf[KK];
 #pragma unroll
-    for (int kk = 0; kk < WKK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
         const bool in = row < N && 16 * kk + 8 * hi < dh;
         qf[kk] = in ? *reinterpret_cast<const bf16x8 *>(p.Q + head + (size_t)row * dh + 16 * kk + 8 * hi)
                     : bf16x8{};
@@ -150,7 +169,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     auto next_tile = [&](int t) -> int {
         return SPARSE ? next_kept_tile(mc, t + 1, t_end, kMaskBlock / WBT) : t + 1;
     };
-    const WideDma dma(wave, lane, dh);
+    const Dma dma(wave, lane, dh);
 
     // One tile (keys t * 64..) in the slot at `base`; the loads of tile tl
     // go into the slot at `nbase`. MASKED applies the element mask: key
@@ -158,18 +177,18 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     auto tile = [&](auto mtag, int t, uint32_t base, int tl, uint32_t nbase) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
         const int kbase = t * WBT;
-        const i32x4 rk = WideDma::rsrc(p.K + head, tl * WBT, N, dh);
-        const i32x4 rv = WideDma::rsrc(p.V + head, tl * WBT, N, dh);
+        const i32x4 rk = Dma::rsrc(p.K + head, tl * WBT, N, dh);
+        const i32x4 rv = Dma::rsrc(p.V + head, tl * WBT, N, dh);
         // operand of slot m: A slots alternate K rows (S^T) and V rows
         // (dP^T); C slot pr = (hh, db) takes K^T of keys 16 hh.. of its step
         bf16x8 op[NSLOT];
         auto read_op = [&](int m) __attribute__((always_inline)) {
             if (m < 2 * NA) {
                 const int st = m / NA, kk = (m % NA) / 2;
-                op[m] = wl.rows(base, (m % 2) * TB + 32 * st * (2 * WD), kk);
+                op[m] = wl.rows(base, (m % 2) * TB + 32 * st * ROW, kk);
             } else {
                 const int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
-                op[m] = wl.trans(base, (32 * st + 16 * (pr / NC)) * (2 * WD), pr % NC);
+                op[m] = wl.trans(base, (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
             }
         };
         f32x16 s[2], dp[2];
@@ -218,14 +237,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
             }
             if constexpr (m + PF < NSLOT)
                 read_op(m + PF);
-            if constexpr (m < 8)
+            if constexpr (m < LPW)
                 dma.issue_block(rk, m, nbase, wave);
-            else if constexpr (m < 16)
-                dma.issue_block(rv, m - 8, nbase + TB, wave);
-            static_for<6>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int st = decltype(ic)::value / 3, k = 2 - decltype(ic)::value % 3;
-                constexpr int e = Plan::elem(m, st, k);
-                if constexpr (e >= 0)
+            else if constexpr (m < 2 * LPW)
+                dma.issue_block(rv, m - LPW, nbase + TB, wave);
+            static_for<12>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int st = decltype(ic)::value / 6, k = 2 - decltype(ic)::value / 2 % 3;
+                constexpr int e = Plan::elem(m, st, k, decltype(ic)::value % 2);
+                if constexpr (e < 16)
                     stage(st, k, e);
             });
             __builtin_amdgcn_sched_barrier(0);
@@ -238,7 +257,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         dma.issue(p.V + head, t * WBT, N, dh, lds0 + TB, wave);
     }
 #pragma unroll
-    for (int kk = 0; kk < WKK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
         wait_loaded(qf[kk]);
         wait_loaded(gf[kk]);
     }
@@ -503,10 +522,10 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 dma.issue_block(rg, m - LPW, nbase + TB, wave);
             else if constexpr (m == 2 * LPW)
                 issue_vec(tl, 1 - b);
-            static_for<6>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int st = decltype(ic)::value / 3, k = 2 - decltype(ic)::value % 3;
-                constexpr int e = Plan::elem(m, st, k);
-                if constexpr (e >= 0)
+            static_for<12>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int st = decltype(ic)::value / 6, k = 2 - decltype(ic)::value / 2 % 3;
+                constexpr int e = Plan::elem(m, st, k, decltype(ic)::value % 2);
+                if constexpr (e < 16)
                     stage(st, k, e);
             });
             __builtin_amdgcn_sched_barrier(0);
@@ -575,7 +594,7 @@ template <bool CAUSAL, bool SPARSE>
 hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
 {
     const dim3 grid(wp.per_xcd * kXcds), block(WW * kWave);
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<CAUSAL, SPARSE>), grid, block, 0, stream, wp);
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<WD, CAUSAL, SPARSE>), grid, block, 0, stream, wp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -595,19 +614,23 @@ hipError_t launch_dkdv128(const WideParams &wp, hipStream_t stream)
     return hipGetLastError();
 }
 
-}  // namespace
+template <bool CAUSAL, bool SPARSE>
+hipError_t launch_dq128(const WideParams &wp, hipStream_t stream)
+{
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<128, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+                       stream, wp);
+    return hipGetLastError();
+}
 
-hipError_t launch_bwd_dkdv_bf16_slot(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
-                                     const uint16_t *K, const uint16_t *V, uint16_t *dK, uint16_t *dV,
-                                     const float *ndelta, const float *lse2)
+// The parameters of the slot-scheduled kernels at 64 < d <= 128.
+WideParams slot_params(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
+                       const uint16_t *V, const float *ndelta, const float *lse2)
 {
     WideParams wp{};
     wp.Q = Q;
     wp.K = K;
     wp.V = V;
     wp.dO = dO;
-    wp.dK = dK;
-    wp.dV = dV;
     wp.ndelta = ndelta;
     wp.lse2 = lse2;
     wp.mask = pr.mask;
@@ -620,10 +643,34 @@ hipError_t launch_bwd_dkdv_bf16_slot(const Problem &pr, const uint16_t *dO, cons
     wp.per_xcd = (wp.items + kXcds - 1) / kXcds;
     wp.c = pr.scale * kLog2e;
     wp.scale = pr.scale;
+    return wp;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv_bf16_slot(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
+                                     const uint16_t *K, const uint16_t *V, uint16_t *dK, uint16_t *dV,
+                                     const float *ndelta, const float *lse2)
+{
+    WideParams wp = slot_params(pr, dO, Q, K, V, ndelta, lse2);
+    wp.dK = dK;
+    wp.dV = dV;
     const bool sparse = pr.mask != nullptr;
     if (pr.causal)
         return sparse ? launch_dkdv128<true, true>(wp, pr.stream) : launch_dkdv128<true, false>(wp, pr.stream);
     return sparse ? launch_dkdv128<false, true>(wp, pr.stream) : launch_dkdv128<false, false>(wp, pr.stream);
+}
+
+hipError_t launch_bwd_dq_bf16_slot(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
+                                   const uint16_t *K, const uint16_t *V, uint16_t *dQ, const float *ndelta,
+                                   const float *lse2)
+{
+    WideParams wp = slot_params(pr, dO, Q, K, V, ndelta, lse2);
+    wp.dQ = dQ;
+    const bool sparse = pr.mask != nullptr;
+    if (pr.causal)
+        return sparse ? launch_dq128<true, true>(wp, pr.stream) : launch_dq128<true, false>(wp, pr.stream);
+    return sparse ? launch_dq128<false, true>(wp, pr.stream) : launch_dq128<false, false>(wp, pr.stream);
 }
 
 hipError_t launch_bwd_bf16_wide(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
