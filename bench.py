@@ -496,11 +496,12 @@ def main():
     fwd_w = 4 if mask is not None or cfg.B * cfg.H * -(-cfg.N // 256) < 512 else 8
     symbols = {"fwd": f"fwd_bf16_kernel<{cfg.d}, {flags}, {fwd_w}>", "bwd_prep": f"bwd_pre_kernel<{cfg.d}>",
                "bwd_dq": f"bwd_dq_kernel<{flags}>", "bwd_dkdv": f"bwd_dkdv_kernel<{flags}>"}
+    # without dropout the slot-scheduled dQ kernel, and at 64 < d <= 128 the
+    # slot-scheduled dK/dV kernel (template arguments: row width, [both
+    # gradients,] causal, block-sparse)
+    bflags = f"{tf(cfg.causal)}, {tf(mask is not None)}"
+    symbols["bwd_dq"] = f"bwd_wide_dq_kernel<{cfg.d}, {bflags}>"
     if cfg.d > 64:
-        # 64 < d <= 128 without dropout: the slot-scheduled backward kernels
-        # (template arguments: row width, [both gradients,] causal, block-sparse)
-        bflags = f"{tf(cfg.causal)}, {tf(mask is not None)}"
-        symbols["bwd_dq"] = f"bwd_wide_dq_kernel<128, {bflags}>"
         symbols["bwd_dkdv"] = f"bwd_wide_dkdv_kernel<128, 2, {bflags}>"
     tag = f"{cfg.name.replace('-', '_')}_b{cfg.B}h{cfg.H}n{cfg.N}d{cfg.d}"
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2),

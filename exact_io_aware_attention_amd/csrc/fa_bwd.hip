@@ -970,10 +970,9 @@ DropParams drop_params(const Problem &pr)
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
 {
-    if constexpr (D == 128) {
-        if (!pr.dropout)
-            return launch_bwd_dq_bf16_slot(pr, b.dO, b.Q, b.K, b.V, b.dQ, b.ndelta, b.lse2);
-    }
+    // without dropout: the slot-scheduled kernel
+    if (!pr.dropout)
+        return launch_bwd_dq_bf16_slot(pr, b.dO, b.Q, b.K, b.V, b.dQ, b.ndelta, b.lse2);
     DqParams qp{};
     qp.dO = b.dO; qp.Q = b.Q; qp.K = b.K; qp.V = b.V;
     qp.ndelta = b.ndelta; qp.lse2 = b.lse2; qp.dQ = b.dQ; qp.mask = pr.mask;
@@ -999,6 +998,8 @@ hipError_t dq_t(const Problem &pr, const BwdPtrs &b)
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t dkdv_t(const Problem &pr, const BwdPtrs &b)
 {
+    // 64 < d <= 128 without dropout: the slot-scheduled kernel (at d = 64,
+    // where the softmax work per MFMA doubles, this kernel is faster)
     if constexpr (D == 128) {
         if (!pr.dropout)
             return launch_bwd_dkdv_bf16_slot(pr, b.dO, b.Q, b.K, b.V, b.dK, b.dV, b.ndelta, b.lse2);

@@ -59,22 +59,24 @@ struct WideParams {
 // one MFMA per slot. A step's softmax elements pass three stages (F: the
 // exponent argument, E: the exponential and the mask, M: the product and
 // the packing into MFMA operands) in consecutive slots; element e of B(0)
-// starts at slot NA + e NA / 16, of B(1) at slot 2 NA + e NCS / 16 (two
-// elements a slot when C has 8 MFMAs), so that no slot waits on a value it
-// produced itself. The last stages run into the next phase, whose MFMAs
-// take the operand half of elements 8..15 only from their second half on
-// (checked below).
+// starts at slot NA + e NA / 16, of B(1) at slot 2 NA + e NCS / 16 (up to
+// four elements a slot when a phase has fewer than 16 MFMAs), so that no
+// slot waits on a value it produced itself. The last stages run into the
+// next phase, whose MFMAs take the operand half of elements 8..15 only from
+// their second half on (checked below).
 template <int NA, int NCS>
 struct WidePlan {
     static constexpr int NSLOT = 2 * NA + 2 * NCS;
     static constexpr int PF = 5;  // operand reads issued this many slots ahead
+    // most elements of one step in one slot's stage
+    static constexpr int MAXE = (NA >= 16 && NCS >= 16) ? 1 : (NA >= 8 && NCS >= 8) ? 2 : 4;
     // slot of stage k (0 F, 1 E, 2 M) of element e of step st
     __device__ static constexpr int slot(int st, int k, int e)
     {
         return (st == 0 ? NA + e * NA / 16 : 2 * NA + e * NCS / 16) + k;
     }
     // the elements of step st whose stage k falls into slot m: the j-th
-    // (j < 2) of them, or 16 when there are fewer
+    // (j < MAXE) of them, or 16 when there are fewer
     __device__ static constexpr int elem(int m, int st, int k, int j)
     {
         const int S = st == 0 ? NA : NCS;
@@ -88,9 +90,10 @@ struct WidePlan {
     // before the first C MFMA that takes them
     static constexpr bool ordered()
     {
-        return NA % 16 == 0 && NCS % 8 == 0 && slot(0, 0, 0) >= NA && slot(0, 2, 7) < 2 * NA &&
-               slot(0, 2, 15) < 2 * NA + NCS / 2 && slot(1, 0, 0) >= 2 * NA &&
-               slot(1, 2, 7) < 2 * NA + NCS && slot(1, 2, 15) < 2 * NA + NCS + NCS / 2;
+        return NA % 8 == 0 && NCS % 4 == 0 && 16 / NA <= MAXE && 16 / NCS <= MAXE &&
+               slot(0, 0, 0) >= NA && slot(0, 2, 7) < 2 * NA && slot(0, 2, 15) < 2 * NA + NCS / 2 &&
+               slot(1, 0, 0) >= 2 * NA && slot(1, 2, 7) < 2 * NA + NCS &&
+               slot(1, 2, 15) < 2 * NA + NCS + NCS / 2;
     }
     static_assert(ordered(), "slot plan");
 };
@@ -241,9 +244,10 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
                 dma.issue_block(rk, m, nbase, wave);
             else if constexpr (m < 2 * LPW)
                 dma.issue_block(rv, m - LPW, nbase + TB, wave);
-            static_for<12>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int st = decltype(ic)::value / 6, k = 2 - decltype(ic)::value / 2 % 3;
-                constexpr int e = Plan::elem(m, st, k, decltype(ic)::value % 2);
+            static_for<6 * Plan::MAXE>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                constexpr int st = i / (3 * Plan::MAXE), k = 2 - i / Plan::MAXE % 3;
+                constexpr int e = Plan::elem(m, st, k, i % Plan::MAXE);
                 if constexpr (e < 16)
                     stage(st, k, e);
             });
@@ -522,9 +526,10 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 dma.issue_block(rg, m - LPW, nbase + TB, wave);
             else if constexpr (m == 2 * LPW)
                 issue_vec(tl, 1 - b);
-            static_for<12>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int st = decltype(ic)::value / 6, k = 2 - decltype(ic)::value / 2 % 3;
-                constexpr int e = Plan::elem(m, st, k, decltype(ic)::value % 2);
+            static_for<6 * Plan::MAXE>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                constexpr int st = i / (3 * Plan::MAXE), k = 2 - i / Plan::MAXE % 3;
+                constexpr int e = Plan::elem(m, st, k, i % Plan::MAXE);
                 if constexpr (e < 16)
                     stage(st, k, e);
             });
@@ -606,23 +611,34 @@ hipError_t launch_wide(const WideParams &wp, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <bool CAUSAL, bool SPARSE>
-hipError_t launch_dkdv128(const WideParams &wp, hipStream_t stream)
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_dkdv_slot(const WideParams &wp, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<128, kPassBoth, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds),
+    hipLaunchKernelGGL((bwd_wide_dkdv_kernel<D, kPassBoth, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds),
                        dim3(WW * kWave), 0, stream, wp);
     return hipGetLastError();
 }
 
-template <bool CAUSAL, bool SPARSE>
-hipError_t launch_dq128(const WideParams &wp, hipStream_t stream)
+template <int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_dq_slot(const WideParams &wp, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bwd_wide_dq_kernel<128, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
+    hipLaunchKernelGGL((bwd_wide_dq_kernel<D, CAUSAL, SPARSE>), dim3(wp.per_xcd * kXcds), dim3(WW * kWave), 0,
                        stream, wp);
     return hipGetLastError();
 }
 
-// The parameters of the slot-scheduled kernels at 64 < d <= 128.
+// Dispatch on (d <= 64, causal, sparse) for the launchers above.
+#define FA_SLOT_DISPATCH(FN, pr, wp)                                                               \
+    ((pr).d <= 64 ? ((pr).causal ? ((pr).mask ? FN<64, true, true>(wp, (pr).stream)              \
+                                              : FN<64, true, false>(wp, (pr).stream))             \
+                                 : ((pr).mask ? FN<64, false, true>(wp, (pr).stream)              \
+                                              : FN<64, false, false>(wp, (pr).stream)))           \
+                  : ((pr).causal ? ((pr).mask ? FN<128, true, true>(wp, (pr).stream)              \
+                                              : FN<128, true, false>(wp, (pr).stream))            \
+                                 : ((pr).mask ? FN<128, false, true>(wp, (pr).stream)             \
+                                              : FN<128, false, false>(wp, (pr).stream))))
+
+// The parameters of the slot-scheduled kernels at d <= 128.
 WideParams slot_params(const Problem &pr, const uint16_t *dO, const uint16_t *Q, const uint16_t *K,
                        const uint16_t *V, const float *ndelta, const float *lse2)
 {
@@ -655,10 +671,11 @@ hipError_t launch_bwd_dkdv_bf16_slot(const Problem &pr, const uint16_t *dO, cons
     WideParams wp = slot_params(pr, dO, Q, K, V, ndelta, lse2);
     wp.dK = dK;
     wp.dV = dV;
-    const bool sparse = pr.mask != nullptr;
     if (pr.causal)
-        return sparse ? launch_dkdv128<true, true>(wp, pr.stream) : launch_dkdv128<true, false>(wp, pr.stream);
-    return sparse ? launch_dkdv128<false, true>(wp, pr.stream) : launch_dkdv128<false, false>(wp, pr.stream);
+        return pr.mask ? launch_dkdv_slot<128, true, true>(wp, pr.stream)
+                       : launch_dkdv_slot<128, true, false>(wp, pr.stream);
+    return pr.mask ? launch_dkdv_slot<128, false, true>(wp, pr.stream)
+                   : launch_dkdv_slot<128, false, false>(wp, pr.stream);
 }
 
 hipError_t launch_bwd_dq_bf16_slot(const Problem &pr, const uint16_t *dO, const uint16_t *Q,
@@ -667,10 +684,7 @@ hipError_t launch_bwd_dq_bf16_slot(const Problem &pr, const uint16_t *dO, const 
 {
     WideParams wp = slot_params(pr, dO, Q, K, V, ndelta, lse2);
     wp.dQ = dQ;
-    const bool sparse = pr.mask != nullptr;
-    if (pr.causal)
-        return sparse ? launch_dq128<true, true>(wp, pr.stream) : launch_dq128<true, false>(wp, pr.stream);
-    return sparse ? launch_dq128<false, true>(wp, pr.stream) : launch_dq128<false, false>(wp, pr.stream);
+    return FA_SLOT_DISPATCH(launch_dq_slot, pr, wp);
 }
 
 hipError_t launch_bwd_bf16_wide(const Problem &pr, const uint16_t *dO, const uint16_t *Q,

@@ -89,9 +89,9 @@ hipError_t launch_fwd_f32(const Problem &p, const float *Q, const float *K, cons
 // and dK passes).
 hipError_t launch_fwd_bf16_wide(const Problem &p, const uint16_t *Q, const uint16_t *K,
                                 const uint16_t *V, uint16_t *O, float *LSE);
-// dQ, and dK and dV in one pass, at 64 < d <= 128 without dropout, in the
-// slot-scheduled kernels (the -D and LSE * log2(e) rows of the workspace
-// already written).
+// dQ at d <= 128, and dK and dV in one pass at 64 < d <= 128, without
+// dropout, in the slot-scheduled kernels (the -D and LSE * log2(e) rows of
+// the workspace already written).
 hipError_t launch_bwd_dq_bf16_slot(const Problem &p, const uint16_t *dO, const uint16_t *Q,
                                    const uint16_t *K, const uint16_t *V, uint16_t *dQ, const float *ndelta,
                                    const float *lse2);

@@ -18,14 +18,17 @@ constexpr int WROWS = 32 * WW;   // query rows or keys per workgroup
 static_assert(WROWS == kMaskBlock, "a workgroup covers one mask block");
 
 // Tile layout: logical 16-byte chunk c of row r sits at chunk c ^ swz(r).
-// swz is a bijection on any 16 consecutive rows (the 16 rows of one b128
-// read cycle hit 16 distinct 4-bank groups) and swz / 4 differs across any 4
-// aligned rows (a transpose read's 4 rows x 64 bytes cover all 64 banks);
-// the bank of a byte depends on its address modulo 256, so 512-byte rows
-// behave as the 256-byte rows this swizzle was laid out for.
+// For rows of 256 bytes or more, swz is a bijection on any 16 consecutive
+// rows (the 16 rows of one b128 read cycle hit 16 distinct 4-bank groups)
+// and swz / 4 differs across any 4 aligned rows (a transpose read's 4 rows
+// x 64 bytes cover all 64 banks); the bank of a byte depends on its address
+// modulo 256, so 512-byte rows behave as 256-byte rows. 128-byte rows
+// (D = 64) put two rows in one 256-byte bank window, and the row parity
+// takes the place of one bit. swz depends on the row modulo 16 only.
+template <int D>
 __device__ __forceinline__ int wide_swz(int r)
 {
-    return 4 * (r % 4) + (r / 4) % 4;
+    return D >= 128 ? 4 * (r % 4) + (r / 4) % 4 : 4 * ((r / 2) % 2) + (r / 4) % 4;
 }
 
 // Direct global->LDS loads of rows row0 .. row0 + 63 of a [N][dh] bf16
@@ -45,7 +48,7 @@ struct WideDmaT {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int r = (512 / D) * (LPW * wave + i) + lane / CPR;
-            const int c = (lane % CPR) ^ wide_swz(r);
+            const int c = (lane % CPR) ^ wide_swz<D>(r);
             off[i] = 8 * c < dh ? 2 * (r * dh + 8 * c) : kBufferOutOfRange;
         }
     }
@@ -71,7 +74,8 @@ using WideDma = WideDmaT<WD>;
 
 // Lane parts of the LDS operand addresses on a 64 x D tile (rows of 2 D
 // bytes). The swizzle is an XOR on the address bits 4..8 of a row's bytes
-// (4..7 for 256-byte rows), which a tile base (a multiple of 512) and the
+// (4..7 for 256-byte rows, 4..6 for 128-byte rows), which a tile base (a
+// multiple of 512) and the
 // row offsets leave clear, so a read takes the tile base plus the lane
 // part, XORs in a per-read constant and adds the row offset through the
 // instruction's immediate:
@@ -82,21 +86,20 @@ using WideDma = WideDmaT<WD>;
 //     rl = 4 (g / 2) + t and rl + 8, logical chunk 4 db + lc with
 //     lc = 2 (g % 2) + u / 2 (= (4 db) ^ lc), element 4 (u % 2) in it:
 //     ((base + tr0) ^ (64 db)) + 2 D r0 and the same with tr1.
-// (wide_swz depends on the row modulo 16, so row blocks at multiples of 16
-// share the lane parts.)
+// (Row blocks at multiples of 16 share the lane parts.)
 template <int D>
 struct WideLaneT {
     uint32_t b128, tr0, tr1;
     __device__ __forceinline__ explicit WideLaneT(int lane)
     {
         const int l32 = lane % 32, hi = lane / 32;
-        b128 = l32 * (2 * D) + 16 * (hi ^ wide_swz(l32));
+        b128 = l32 * (2 * D) + 16 * (hi ^ wide_swz<D>(l32));
         const int g = lane / 16, sl = lane % 16;
         const int rl = 4 * (g / 2) + sl / 4;
         const int lc = 2 * (g % 2) + (sl % 4) / 2;
         const int in = 4 * (sl % 2);
-        tr0 = rl * (2 * D) + 16 * (lc ^ wide_swz(rl)) + 2 * in;
-        tr1 = (rl + 8) * (2 * D) + 16 * (lc ^ wide_swz(rl + 8)) + 2 * in;
+        tr0 = rl * (2 * D) + 16 * (lc ^ wide_swz<D>(rl)) + 2 * in;
+        tr1 = (rl + 8) * (2 * D) + 16 * (lc ^ wide_swz<D>(rl + 8)) + 2 * in;
     }
     // base: tile address (a multiple of 512); off: byte offset of the row
     // block (and of the tile within a slot), a compile-time constant
