@@ -1,8 +1,13 @@
-// Backward of exact attention for head dims in (128, 256] on the matrix
-// cores, by recomputation as in the 64/128-wide kernels
-// (lukebest.github.io FlashAttention, "反向：重算而非存储"; mstx.cn/posts/485
-// §三.3): P = 2^(c s - lse2), dP = dO V^T, dS = P o (dP - D), dQ = scale dS K,
-// dK = scale dS^T Q, dV = P^T dO.
+// Slot-scheduled backward kernels of exact attention on the matrix cores,
+// by recomputation (lukebest.github.io FlashAttention, "反向：重算而非存储";
+// mstx.cn/posts/485 §三.3): P = 2^(c s - lse2), dP = dO V^T,
+// dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO. They
+// run the backward at every head dim without dropout, except dK/dV at
+// d <= 64: dQ at row widths 64, 128 and 256; dK and dV in one pass at 128
+// (both accumulators fit beside the K and V rows) and in a pass each at 256.
+// The description below is written for d = 256; the 128- and 64-wide
+// instances differ only in sizes (8 or 4 depth steps, 4 or 2 column blocks,
+// tiles of 256- or 128-byte rows).
 //
 // At d = 256 a wave holds 32 rows of two 256-wide MFMA B operands and the
 // accumulators of one 256-column gradient (128 + 128 AGPRs), but not those
