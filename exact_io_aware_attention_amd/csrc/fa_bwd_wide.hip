@@ -24,9 +24,8 @@
 //     8 contractions of work against the method's 5 (splitting each
 //     gradient into column halves whose workgroups both rebuild S and dP
 //     would take 11).
-// The D and lse2 rows come from the 256-wide instance of the backward's
-// preprocessing kernel. LDS tiles (512-byte rows, 16-byte chunks
-// XOR-swizzled) are double-buffered: the next tile streams in by direct
+// The D and lse2 rows come from the backward's preprocessing kernel. LDS
+// tiles (512-byte rows, 16-byte chunks XOR-swizzled) are double-buffered: the next tile streams in by direct
 // global->LDS loads while the current one is computed, one barrier per tile.
 // With one wave per SIMD nothing hides a wave's own latencies, so a tile's
 // work is laid out by hand in MFMA slots (WidePlan): every LDS operand is
@@ -104,13 +103,13 @@ struct WidePlan {
 };
 
 // One workgroup per 128 query rows; each wave holds 32 query rows of Q and
-// dO, the B operands of S^T and dP^T, in AGPRs beside its eight dQ^T
-// accumulators, so that the VGPRs hold the scores, the softmax and the
+// dO (D columns), the B operands of S^T and dP^T, in AGPRs beside its D / 32
+// dQ^T accumulators, so that the VGPRs hold the scores, the softmax and the
 // operands read ahead. Per 32 keys (a step):
-//   A: S^T = K Q^T and dP^T = V dO^T (lane = query; 16 MFMA pairs, K and V
-//      rows read from LDS);
+//   A: S^T = K Q^T and dP^T = V dO^T (lane = query; D / 16 MFMA pairs, K
+//      and V rows read from LDS);
 //   B: P^T = 2^(c s - lse2), dS^T = P^T o (dP^T - D) (vector ALU);
-//   C: dQ^T += K^T dS^T over all 256 columns (16 MFMAs, K^T by transpose
+//   C: dQ^T += K^T dS^T over all D columns (D / 16 MFMAs, K^T by transpose
 //      reads).
 // Every step ends inside its tile (WidePlan), so two LDS slots suffice: the
 // next tile streams into the other one, a load per slot of the first step.
