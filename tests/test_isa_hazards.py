@@ -209,7 +209,7 @@ def test_asm_reads_of_mfma_results_wait_long_enough():
         req = _probe_requirements(tmp)
         assert set(req) == {"v_mfma_f32_32x32x16_bf16", "v_mfma_scale_f32_32x32x64_f8f6f4"}, req
         assert all(n >= 1 for n in req.values()), req
-        srcs = ["fa_fwd.hip", "fa_decode.hip", "fa_fp8.hip", "fa_bwd.hip", "fa_bwd_wide.hip"]
+        srcs = ["fa_fwd.hip", "fa_fwd_wide.hip", "fa_decode.hip", "fa_fp8.hip", "fa_bwd.hip", "fa_bwd_wide.hip"]
         with concurrent.futures.ThreadPoolExecutor(len(srcs)) as ex:
             listings = list(ex.map(lambda s: _asm(os.path.join(build.CSRC, s), tmp, s), srcs))
         for name, lines in zip(srcs, listings):
