@@ -208,11 +208,10 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
     qk(0, s);
     for (int t = 0; t < t_end; ++t) {
         const int slot = t % 3;
-        const bool more = t + 2 < t_end;
-        if (more)
-            issue(t + 2, (t + 2) % 3);  // buffers of tile t-1, free since the last barrier
-        if (t + 1 < t_end)
-            qk((t + 1) % 3, s_nxt);
+        // tile t+2 into the buffers of tile t-1, free since the last barrier
+        // (without a tile t+2 tile t is loaded again: no branch, so that the
+        // MFMAs below stay in the block of the softmax)
+        issue(t + 2 < t_end ? t + 2 : t, (t + 2) % 3);
         const uint32_t vbuf = lds0 + (3 + slot) * TB;
         // keys past the end, above the diagonal (causal)
         const int kb = t * BC;
@@ -226,18 +225,21 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                         s[blk][r] = -INFINITY;
                 }
         }
-        // the asm max chain first reads s[0][0], then s[1][0] (two MFMA
-        // accumulators): both pass through a compiler-visible add first
+        // row max: one asm max chain per 32-key block, starting at s[0][0]
+        // and s[1][0] (two MFMA accumulators), which pass through a
+        // compiler-visible add first
         mfma_result_touch(s[0], 0);
         mfma_result_touch(s[1], 0);
-        float mx = vmax3(s[0][0], s[0][1], s[0][2]);
+        float ma = vmax3(s[0][0], s[0][1], s[0][2]);
+        float mb = vmax3(s[1][0], s[1][1], s[1][2]);
 #pragma unroll
-        for (int r = 3; r < 16; ++r)
-            mx = vmax2(mx, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            mx = vmax2(mx, s[1][r]);
-        mx = halves_max(mx) * c;
+        for (int r = 3; r < 15; r += 2) {
+            ma = vmax3(ma, s[0][r], s[0][r + 1]);
+            mb = vmax3(mb, s[1][r], s[1][r + 1]);
+        }
+        ma = vmax2(ma, s[0][15]);
+        mb = vmax2(mb, s[1][15]);
+        const float mx = halves_max(vmax2(ma, mb)) * c;
         // The reference follows the row max exactly (no slack): every weight
         // is <= 1 and the one that sets a new max is exactly 1 in E4M3.
         if (__any(mx > m)) {
@@ -252,6 +254,10 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
                 for (int r = 0; r < 16; ++r)
                     o[db][r] *= alpha;
         }
+        // The next tile's S^T MFMAs (on the last tile a stale buffer is read
+        // and the result unused) in the same block as this tile's softmax,
+        // so that the scheduler interleaves them.
+        qk((t + 1) % 3, s_nxt);
         // P = 2^(c s - m) <= 1 in fp32 for the row sum, E4M3 for P V
         i32x8 pp;
         float ls = 0.f;
@@ -278,19 +284,18 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p)
             const i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
             o[db] = mfma_fp8(va, pp, o[db]);
         }
+        slot_done(l);  // the row sum in this block, not sunk past the wait below
         // Tile t+1's V^T and tile t+2's K have landed (the next iteration
         // computes tile t+2's S^T), tile t+2's V^T may still be in flight;
         // the barrier extends that to all waves and frees tile t's buffers.
-        if (more)
-            lds_dma_wait<1>();
-        else
-            lds_dma_wait<0>();
+        lds_dma_wait<1>();
         __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
             s[blk] = s_nxt[blk];
     }
 
+    lds_dma_wait<0>();  // the last (repeated) tile load has landed: none outlives the workgroup
     const float lt = halves_sum(l);
     if (row < N) {
         const float inv = lt > 0.f ? p.o_mul / lt : 0.f;
