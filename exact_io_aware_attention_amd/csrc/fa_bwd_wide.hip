@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     constexpr uint32_t TB = WBT * ROW;     // bytes per tile
     constexpr uint32_t SLOT = 2 * TB;      // [K tile | V tile]
     using Plan = WidePlan<2 * KK, 2 * NC>;
-    using Lane = WideLaneT<D>;
+    using Lane = WideLaneXT<D>;
     using Dma = WideDmaT<D>;
     constexpr int NA = 2 * KK, NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLOT];
@@ -178,11 +178,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     };
     const Dma dma(wave, lane, dh);
 
-    // One tile (keys t * 64..) in the slot at `base`; the loads of tile tl
-    // go into the slot at `nbase`. MASKED applies the element mask: key
+    // One tile (keys t * 64..) in slot b (a compile-time constant, so that
+    // every operand read is a lane register plus an immediate); the loads
+    // of tile tl go into slot 1 - b. MASKED applies the element mask: key
     // past the end or above the query (causal).
-    auto tile = [&](auto mtag, int t, uint32_t base, int tl, uint32_t nbase) __attribute__((always_inline)) {
+    auto tile = [&](auto mtag, auto btag, int t, int tl) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
+        constexpr int b = decltype(btag)::value;
+        const uint32_t base = lds0 + b * SLOT, nbase = lds0 + (1 - b) * SLOT;
         const int kbase = t * WBT;
         const i32x4 rk = Dma::rsrc(p.K + head, tl * WBT, N, dh);
         const i32x4 rv = Dma::rsrc(p.V + head, tl * WBT, N, dh);
@@ -192,10 +195,10 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         auto read_op = [&](int m) __attribute__((always_inline)) {
             if (m < 2 * NA) {
                 const int st = m / NA, kk = (m % NA) / 2;
-                op[m] = wl.rows(base, (m % 2) * TB + 32 * st * ROW, kk);
+                op[m] = wl.rows(base + (m % 2) * TB + 32 * st * ROW, kk);
             } else {
                 const int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
-                op[m] = wl.trans(base, (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
+                op[m] = wl.trans(base + (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
             }
         };
         f32x16 s[2], dp[2];
@@ -278,25 +281,38 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         const int kbase = t * WBT;
         return (kbase + WBT > N) || (CAUSAL && kbase + WBT - 1 > wr0);
     };
-    int j = 0;
     // One tile and the barrier after which the next one has landed (without
     // a next tile the current one is loaded again, into the free slot).
-    auto step_tile = [&](auto mtag) __attribute__((always_inline)) {
+    auto step_tile = [&](auto mtag, auto btag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
-        tile(mtag, t, lds0 + (j % 2) * SLOT, tn < t_end ? tn : t, lds0 + ((j + 1) % 2) * SLOT);
+        tile(mtag, btag, t, tn < t_end ? tn : t);
         mfma_drain();  // before the loop edges, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
-        ++j;
     };
     // Runs of masked and unmasked tiles each get a loop of their own
-    // (causal: the masked tiles are the last ones, on the diagonal).
+    // (causal: the masked tiles are the last ones, on the diagonal),
+    // unrolled twice so that each copy knows its slot.
+    int phase = 0;  // the slot of tile t
+    auto run = [&](auto mtag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        for (;;) {
+            if (phase == 0) {
+                if (t >= t_end || tile_masked(t) != MASKED)
+                    return;
+                step_tile(mtag, std::integral_constant<int, 0>{});
+                phase = 1;
+            }
+            if (t >= t_end || tile_masked(t) != MASKED)
+                return;
+            step_tile(mtag, std::integral_constant<int, 1>{});
+            phase = 0;
+        }
+    };
     while (t < t_end) {
-        while (t < t_end && !tile_masked(t))
-            step_tile(std::false_type{});
-        while (t < t_end && tile_masked(t))
-            step_tile(std::true_type{});
+        run(std::false_type{});
+        run(std::true_type{});
     }
 #pragma unroll
     for (int db = 0; db < NC; ++db)
@@ -339,7 +355,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     constexpr int NA = DO_DK ? 2 * KK : KK;                  // A MFMAs per step
     constexpr int NCS = (DO_DV && DO_DK ? 2 : 1) * 2 * NC;   // C MFMAs per step
     using Plan = WidePlan<NA, NCS>;
-    using Lane = WideLaneT<D>;
+    using Lane = WideLaneXT<D>;
     using Dma = WideDmaT<D>;
     constexpr int NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[VEC + 4 * WBT * 4];
@@ -402,11 +418,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         lds_dma_buf_b32(rs, 4 * lane, lds0 + VEC + (2 * b + (wave & 1)) * WBT * 4);
     };
 
-    // One tile (queries t * 64..) in slot b; the loads of tile tl go into
-    // slot 1 - b. MASKED applies the element mask: query past the end or
-    // key above the query (causal).
-    auto tile = [&](auto mtag, int t, int b, int tl) __attribute__((always_inline)) {
+    // One tile (queries t * 64..) in slot b (a compile-time constant, so
+    // that every operand read is a lane register plus an immediate); the
+    // loads of tile tl go into slot 1 - b. MASKED applies the element mask:
+    // query past the end or key above the query (causal).
+    auto tile = [&](auto mtag, auto btag, int t, int tl) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(mtag)::value;
+        constexpr int b = decltype(btag)::value;
         const uint32_t base = lds0 + b * SLOT, nbase = lds0 + (1 - b) * SLOT;
         const int qbase = t * WBT;
         const i32x4 rq = Dma::rsrc(p.Q + head, tl * WBT, N, dh);
@@ -449,13 +467,13 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 const int st = m / NA, i = m % NA;
                 const int kk = DO_DK ? i / 2 : i;
                 const uint32_t mat = (DO_DK && i % 2 == 1) ? TB : 0;
-                op[m] = wl.rows(base, mat + 32 * st * ROW, kk);
+                op[m] = wl.rows(base + mat + 32 * st * ROW, kk);
             } else {
                 const int st = (m - 2 * NA) / NCS;
                 int pr;
                 bool is_v;
                 c_slot((m - 2 * NA) % NCS, pr, is_v);
-                op[m] = wl.trans(base, (is_v ? TB : 0) + (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
+                op[m] = wl.trans(base + (is_v ? TB : 0) + (32 * st + 16 * (pr / NC)) * ROW, pr % NC);
             }
         };
         f32x16 s[2], dp[2];
@@ -560,26 +578,38 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         const int qbase = t * WBT;
         return (qbase + WBT > N) || (CAUSAL && qbase < wk0 + 31);
     };
-    int j = 0;
     // One tile and the barrier after which the next one has landed (without
     // a next tile the current one is loaded again, into the free slot).
-    auto step_tile = [&](auto mtag) __attribute__((always_inline)) {
+    auto step_tile = [&](auto mtag, auto btag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
-        tile(mtag, t, j % 2, tn < p.ntile ? tn : t);
+        tile(mtag, btag, t, tn < p.ntile ? tn : t);
         mfma_drain();  // before the loop edges, where accumulators may be moved
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
-        ++j;
     };
     // Runs of masked and unmasked tiles each get a loop of their own
     // (causal: the masked tiles are the first ones, on the diagonal, and
-    // the ragged last one).
+    // the ragged last one), unrolled twice so that each copy knows its slot.
+    int phase = 0;  // the slot of tile t
+    auto run = [&](auto mtag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mtag)::value;
+        for (;;) {
+            if (phase == 0) {
+                if (t >= p.ntile || tile_masked(t) != MASKED)
+                    return;
+                step_tile(mtag, std::integral_constant<int, 0>{});
+                phase = 1;
+            }
+            if (t >= p.ntile || tile_masked(t) != MASKED)
+                return;
+            step_tile(mtag, std::integral_constant<int, 1>{});
+            phase = 0;
+        }
+    };
     while (t < p.ntile) {
-        while (t < p.ntile && tile_masked(t))
-            step_tile(std::true_type{});
-        while (t < p.ntile && !tile_masked(t))
-            step_tile(std::false_type{});
+        run(std::true_type{});
+        run(std::false_type{});
     }
 #pragma unroll
     for (int db = 0; db < NC; ++db) {

@@ -114,6 +114,38 @@ struct WideLaneT {
 };
 using WideLane = WideLaneT<WD>;
 
+// The lane parts with each read's XOR constant already applied (computed
+// once, D / 8 registers): a tile base that is a multiple of 512 adds to them
+// without touching the XORed bits ((base + x) ^ c = base + (x ^ c) for
+// c < 512), so a read whose tile base and row offset are compile-time
+// constants takes no address arithmetic at all, the sum going into the
+// instruction's offset field.
+template <int D>
+struct WideLaneXT {
+    uint32_t rx[D / 16], tx0[D / 32], tx1[D / 32];
+    __device__ __forceinline__ explicit WideLaneXT(int lane)
+    {
+        const WideLaneT<D> w(lane);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            rx[kk] = w.b128 ^ (32u * kk);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            tx0[db] = w.tr0 ^ (64u * db);
+            tx1[db] = w.tr1 ^ (64u * db);
+        }
+    }
+    // at: tile base (a multiple of 512) plus the row block's byte offset
+    __device__ __forceinline__ bf16x8 rows(uint32_t at, int kk) const
+    {
+        return lds_b128_at(rx[kk] + at);
+    }
+    __device__ __forceinline__ bf16x8 trans(uint32_t at, int db) const
+    {
+        return lds_tr_pair_at(tx0[db] + at, tx1[db] + at);
+    }
+};
+
 // Stores a 32-column accumulator block (lane = row, register r = column
 // c0 + 8 (r / 4) + 4 hi + r % 4) as bf16 times `mul`, columns < dh only.
 __device__ __forceinline__ void wide_store(uint16_t *row_ptr, const f32x16 &acc, int c0, int hi, float mul,
