@@ -243,7 +243,11 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
                     dp[st] = mfma32x32x16(op[m], gf[kk], kk == 0 ? ndv : dp[st]);
             } else {
                 constexpr int st = (m - 2 * NA) / (2 * NC), pr = (m - 2 * NA) % (2 * NC);
-                mfma_acc_agpr_ordered(dq[pr % NC], op[m], sb[st][pr / NC]);
+                // (at D = 64 the plan packs an operand just before its MFMA)
+                if constexpr (D == 64)
+                    mfma_acc_agpr_ordered(dq[pr % NC], op[m], sb[st][pr / NC]);
+                else
+                    mfma_acc_agpr_nowait(dq[pr % NC], op[m], sb[st][pr / NC]);
             }
             if constexpr (m + PF < NSLOT)
                 read_op(m + PF);
@@ -534,9 +538,9 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 constexpr int pr = (DO_DV && DO_DK) ? ci / 2 : ci;
                 constexpr bool is_v = (DO_DV && DO_DK) ? ci % 2 == 0 : DO_DV;
                 if constexpr (is_v)
-                    mfma_acc_agpr_ordered(acc_v[pr % NC], op[m], ob_v[st][pr / NC]);
+                    mfma_acc_agpr_nowait(acc_v[pr % NC], op[m], ob_v[st][pr / NC]);
                 else
-                    mfma_acc_agpr_ordered(acc_k[pr % NC], op[m], ob_k[st][pr / NC]);
+                    mfma_acc_agpr_nowait(acc_k[pr % NC], op[m], ob_k[st][pr / NC]);
             }
             if constexpr (m + PF < NSLOT)
                 read_op(m + PF);

@@ -66,6 +66,16 @@ __device__ __forceinline__ void mfma_acc_agpr_ordered(f32x16 &acc, bf16x8 a, bf1
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// The ordered form without a wait of its own, for hand-scheduled loops in
+// which every operand's last vector ALU write lies far enough ahead of the
+// MFMA anyway: the ISA hazard test checks that in the generated code of
+// every kernel, along every path, so a schedule change that brings a write
+// too close fails that test instead of reading a stale operand.
+__device__ __forceinline__ void mfma_acc_agpr_nowait(f32x16 &acc, bf16x8 a, bf16x8 b)
+{
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Marks a value as needed at this point of a hand-scheduled loop: code that
 // computes it cannot be sunk past the next ordered MFMA.
 __device__ __forceinline__ void slot_done(float x)

@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) fwd_wide_kernel(WideFwdParams p
                 s_nxt = mfma32x32x16(op[i], qf[i], i == 0 ? f32x16{} : s_nxt);
             } else {
                 constexpr int pr = i - WKK;
-                mfma_acc_agpr_ordered(o[pr % NC], op[i], pb[pr / NC]);
+                mfma_acc_agpr_nowait(o[pr % NC], op[i], pb[pr / NC]);
             }
             read_op(i + PF);
             dma_hook(i);

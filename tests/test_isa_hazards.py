@@ -17,6 +17,14 @@ path of the control-flow graph (one wait state per instruction, N + 1 per
 s_nop N; a compiler-generated write of the register ends the check for it).
 With the waits taken out of the forward and decode sources, the check
 reports 12 and 11 wait states missing before their first asm row max.
+
+The reverse order is checked too: an MFMA written as inline asm (the
+hand-scheduled backward kernels accumulate into AGPRs that way) reads A and
+B operands that vector ALU instructions may have written just before, which
+the ISA also separates by wait states the compiler does not insert for asm.
+The count again comes from the compiler (a probe whose MFMA reads a freshly
+converted operand), and every asm MFMA's A and B registers are checked
+against the last vector ALU write along every path.
 """
 import concurrent.futures
 import os
@@ -47,6 +55,18 @@ __global__ void probe_fp8(const i32x8 *a, float *o) {
   f32x16 s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[threadIdx.x], a[threadIdx.x + 64], f32x16{},
                                                              0, 0, 0, 127, 0, 127);
   o[threadIdx.x] = s[0] + s[5];
+}
+"""
+
+PROBE_V = r"""
+#include <hip/hip_runtime.h>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ void probe_valu_to_mfma(const float *x, const bf16x8 *a, f32x16 *o) {
+  const float v = x[threadIdx.x];
+  bf16x8 b;
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)(v * (float)(i + 1));
+  o[threadIdx.x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[threadIdx.x], b, f32x16{}, 0, 0, 0);
 }
 """
 
@@ -108,6 +128,28 @@ def _probe_requirements(tmp):
             continue
         since += _wait_states(op, ops)
     return req
+
+
+def _probe_valu_to_mfma(tmp):
+    """Wait states the compiler puts between the last vector ALU write of an
+    MFMA's A or B operand and the MFMA (probe_valu_to_mfma)."""
+    src = os.path.join(tmp, "probe_v.hip")
+    open(src, "w").write(PROBE_V)
+    lines = _asm(src, tmp, "probe_v")
+    fn = _blocks(lines)
+    for blocks in fn:
+        seq = [i for b in blocks for i in b[1]]
+        if not any(op.startswith("v_mfma") for op, _, _ in seq):
+            continue
+        k = next(i for i, (op, _, _) in enumerate(seq) if op.startswith("v_mfma"))
+        srcs = {r for t in seq[k][1][1:3] for r in _vgprs(t)}
+        since = 0
+        for op, ops, _ in reversed(seq[:k]):
+            if op.startswith("v_") and not op.startswith("v_mfma") and ops and \
+                    any(r in srcs for r in _vgprs(ops[0])):
+                return since
+            since += _wait_states(op, ops)
+    raise AssertionError("no MFMA reading a vector ALU result in the probe")
 
 
 def _blocks(lines):
@@ -203,6 +245,48 @@ def _check(lines, req):
     return worst
 
 
+def _check_operands(lines, need):
+    """Largest deficit over the A and B operand reads of asm MFMAs that follow
+    a vector ALU write of the register too closely, along every path."""
+    worst = (0, None)
+    for blocks in _blocks(lines):
+        index = {b[0]: k for k, b in enumerate(blocks) if b[0] is not None}
+        entry = [None] * len(blocks)
+        entry[0] = {}
+        work = [0]
+        while work:
+            k = work.pop()
+            pend = dict(entry[k])
+            _, instrs, succ, fall = blocks[k]
+            for op, ops, in_asm in instrs:
+                if op.startswith("v_mfma") and in_asm:
+                    for t in ops[1:3]:
+                        for r in _vgprs(t):
+                            if pend.get(r, 0) > worst[0]:
+                                worst = (pend[r], f"{op} {', '.join(ops)}")
+                w = _wait_states(op, ops)
+                pend = {r: n - w for r, n in pend.items() if n - w > 0}
+                if ops and op.startswith("v_") and not op.startswith(("v_mfma", "v_accvgpr_read")):
+                    for r in _vgprs(ops[0]):
+                        pend[r] = need
+                elif ops and op.startswith(("v_mfma", "v_accvgpr_read", "ds_read", "buffer_load",
+                                            "global_load")):
+                    for r in _vgprs(ops[0]):
+                        pend.pop(r, None)
+            nxt = [index[t] for t in succ if t in index]
+            if fall and k + 1 < len(blocks):
+                nxt.append(k + 1)
+            for n in nxt:
+                old = entry[n]
+                merged = dict(old or {})
+                for r, v in pend.items():
+                    merged[r] = max(merged.get(r, 0), v)
+                if old is None or merged != old:
+                    entry[n] = merged
+                    work.append(n)
+    return worst
+
+
 def test_asm_reads_of_mfma_results_wait_long_enough():
     tmp = tempfile.mkdtemp(prefix="fa_isa_")
     try:
@@ -212,9 +296,14 @@ def test_asm_reads_of_mfma_results_wait_long_enough():
         srcs = ["fa_fwd.hip", "fa_fwd_wide.hip", "fa_decode.hip", "fa_fp8.hip", "fa_bwd.hip", "fa_bwd_wide.hip"]
         with concurrent.futures.ThreadPoolExecutor(len(srcs)) as ex:
             listings = list(ex.map(lambda s: _asm(os.path.join(build.CSRC, s), tmp, s), srcs))
+        need = _probe_valu_to_mfma(tmp)
+        assert need >= 1, need
         for name, lines in zip(srcs, listings):
             deficit, where = _check(lines, req)
             print(f"{name}: largest deficit {deficit} ({where})")
             assert deficit == 0, f"{name}: asm read of an MFMA result {deficit} wait states early: {where}"
+            deficit, where = _check_operands(lines, need)
+            print(f"{name}: asm MFMA operands, largest deficit {deficit} ({where})")
+            assert deficit == 0, f"{name}: asm MFMA reads a vector ALU result {deficit} wait states early: {where}"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
