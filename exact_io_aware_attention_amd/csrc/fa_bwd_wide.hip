@@ -290,7 +290,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     auto step_tile = [&](auto mtag, auto btag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
         tile(mtag, btag, t, tn < t_end ? tn : t);
-        mfma_drain();  // before the loop edges, where accumulators may be moved
+        // Before the loop edges, where the compiler may copy accumulators, the
+        // MFMAs must have written them; the 128- and 256-wide instances need
+        // no drain there: their generated code moves no accumulator that soon
+        // (the ISA hazard test checks every access to an AGPR an MFMA is still
+        // writing, on every path), while the 64-wide dQ kernel's block-sparse
+        // instances do copy one at a loop edge.
+        if constexpr (D == 64)
+            mfma_drain();
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
@@ -318,6 +325,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
         run(std::false_type{});
         run(std::true_type{});
     }
+    mfma_drain();
 #pragma unroll
     for (int db = 0; db < NC; ++db)
         mfma_settle(dq[db]);
@@ -587,7 +595,14 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     auto step_tile = [&](auto mtag, auto btag) __attribute__((always_inline)) {
         const int tn = next_tile(t);
         tile(mtag, btag, t, tn < p.ntile ? tn : t);
-        mfma_drain();  // before the loop edges, where accumulators may be moved
+        // Before the loop edges, where the compiler may copy accumulators, the
+        // MFMAs must have written them; the 128- and 256-wide instances need
+        // no drain there: their generated code moves no accumulator that soon
+        // (the ISA hazard test checks every access to an AGPR an MFMA is still
+        // writing, on every path), while the 64-wide dQ kernel's block-sparse
+        // instances do copy one at a loop edge.
+        if constexpr (D == 64)
+            mfma_drain();
         lds_dma_wait<0>();
         __syncthreads();
         t = tn;
@@ -615,6 +630,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
         run(std::true_type{});
         run(std::false_type{});
     }
+    mfma_drain();
 #pragma unroll
     for (int db = 0; db < NC; ++db) {
         if constexpr (DO_DV)

@@ -343,7 +343,8 @@ __global__ void __launch_bounds__(WW * kWave, 1) fwd_wide_kernel(WideFwdParams p
         auto no_dma = [](int) {};
         half(mtag, std::integral_constant<int, 0>{}, t * WBT + 32, true, kc, kn, vc, dma_first);
         half(mtag, std::integral_constant<int, 1>{}, tn * WBT, tn < t_end, kn, kn, vc, no_dma);
-        mfma_drain();  // before the loop edges, where accumulators may be moved
+        // (no MFMA drain before the loop edges: the generated code moves no
+        // accumulator there, which the ISA hazard test checks)
         lds_dma_wait<0>();
         barrier_reads_in_flight();  // the carried K reads (tile j+1's) stay in flight
         t = tn;

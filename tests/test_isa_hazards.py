@@ -130,6 +130,62 @@ def _probe_requirements(tmp):
     return req
 
 
+def _agprs(tok):
+    m = re.fullmatch(r"a\[(\d+):(\d+)\]", tok)
+    if m:
+        return range(int(m.group(1)), int(m.group(2)) + 1)
+    m = re.fullmatch(r"a(\d+)", tok)
+    return [int(m.group(1))] if m else []
+
+
+def _check_agprs(lines, req):
+    """Largest deficit over accesses to AGPRs that an MFMA is still writing:
+    any instruction other than an MFMA taking the register as its own
+    accumulator (C operand and destination, which the matrix core chains
+    without waits) must come at least the MFMA's result latency after it,
+    along every path. The compiler inserts these waits for its own MFMAs; the
+    asm ones (the AGPR accumulators of the hand-scheduled loops) rely on the
+    code around them."""
+    worst = (0, None)
+    for blocks in _blocks(lines):
+        index = {b[0]: k for k, b in enumerate(blocks) if b[0] is not None}
+        entry = [None] * len(blocks)
+        entry[0] = {}
+        work = [0]
+        while work:
+            k = work.pop()
+            pend = dict(entry[k])
+            _, instrs, succ, fall = blocks[k]
+            for op, ops, in_asm in instrs:
+                if op.startswith("v_mfma"):
+                    chained = set(_agprs(ops[0])) if ops else set()
+                    touched = [r for t in ops[1:3] for r in _agprs(t)]
+                    touched += [r for t in ops[3:4] for r in _agprs(t) if r not in chained]
+                else:
+                    touched = [r for t in ops for r in _agprs(t)]
+                for r in touched:
+                    if pend.get(r, 0) > worst[0]:
+                        worst = (pend[r], f"{op} {', '.join(ops)}")
+                w = _wait_states(op, ops)
+                pend = {r: n - w for r, n in pend.items() if n - w > 0}
+                if op.startswith("v_mfma") and ops:
+                    need = next((n for kk, n in req.items() if op.startswith(kk)), max(req.values()))
+                    for r in _agprs(ops[0]):
+                        pend[r] = need
+            nxt = [index[t] for t in succ if t in index]
+            if fall and k + 1 < len(blocks):
+                nxt.append(k + 1)
+            for n in nxt:
+                old = entry[n]
+                merged = dict(old or {})
+                for r, v in pend.items():
+                    merged[r] = max(merged.get(r, 0), v)
+                if old is None or merged != old:
+                    entry[n] = merged
+                    work.append(n)
+    return worst
+
+
 def _probe_valu_to_mfma(tmp):
     """Wait states the compiler puts between the last vector ALU write of an
     MFMA's A or B operand and the MFMA (probe_valu_to_mfma)."""
@@ -305,5 +361,8 @@ def test_asm_reads_of_mfma_results_wait_long_enough():
             deficit, where = _check_operands(lines, need)
             print(f"{name}: asm MFMA operands, largest deficit {deficit} ({where})")
             assert deficit == 0, f"{name}: asm MFMA reads a vector ALU result {deficit} wait states early: {where}"
+            deficit, where = _check_agprs(lines, req)
+            print(f"{name}: AGPR accumulators, largest deficit {deficit} ({where})")
+            assert deficit == 0, f"{name}: access to an AGPR {deficit} wait states before its MFMA is done: {where}"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
