@@ -25,13 +25,17 @@
 //     gradient into column halves whose workgroups both rebuild S and dP
 //     would take 11).
 // The D and lse2 rows come from the backward's preprocessing kernel. LDS
-// tiles (512-byte rows, 16-byte chunks XOR-swizzled) are double-buffered: the next tile streams in by direct
-// global->LDS loads while the current one is computed, one barrier per tile.
-// With one wave per SIMD nothing hides a wave's own latencies, so a tile's
-// work is laid out by hand in MFMA slots (WidePlan): every LDS operand is
-// read a few slots ahead of its MFMA and the softmax of one step runs beside
-// the MFMAs of the next phase; the B operands sit in AGPRs, which leaves the
-// VGPRs room for the reads in flight. Only tiles on the diagonal or at the
+// tiles (512-byte rows, 16-byte chunks XOR-swizzled) are double-buffered:
+// the next tile streams in by direct global->LDS loads while the current
+// one is computed, one barrier per tile; the tile loop is unrolled by
+// buffer, so every operand read is a per-lane register (the swizzle's XOR
+// already applied) plus an immediate. With one wave per SIMD nothing hides
+// a wave's own latencies, and the wave issues every instruction of its tile
+// itself, so a tile's work is laid out by hand in MFMA slots (WidePlan):
+// every LDS operand is read a few slots ahead of its MFMA and the softmax of
+// one step runs beside the MFMAs of the next phase; the B operands sit in
+// AGPRs, which leaves the VGPRs room for the reads in flight. Only tiles on
+// the diagonal or at the
 // ragged end apply the element mask. Work items (128-row blocks) are dealt
 // so that each XCD takes one contiguous range of them: a head's blocks then
 // share that XCD's L2, which reads their K/V (or Q/dO) tiles once for all of

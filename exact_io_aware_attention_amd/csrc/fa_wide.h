@@ -1,8 +1,8 @@
-// Tiles of 64 rows x D columns (bf16, D = 256 for head dims in (128, 256],
-// 128 for the slot-scheduled dK/dV kernel below that) shared by the
-// slot-scheduled kernels: the LDS swizzle, the direct global->LDS loads that
-// fill a tile, the lane parts of the MFMA operand reads and the bf16 stores
-// of a 32-column accumulator block.
+// Tiles of 64 rows x D columns (bf16; D = 256 for head dims in (128, 256],
+// 128 or 64 below that) shared by the slot-scheduled kernels: the LDS
+// swizzle, the direct global->LDS loads that fill a tile, the lane parts of
+// the MFMA operand reads and the bf16 stores of a 32-column accumulator
+// block.
 #pragma once
 
 #include "fa_common.h"
