@@ -129,6 +129,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
     using Lane = WideLaneXT<D>;
     using Dma = WideDmaT<D>;
     constexpr int NA = 2 * KK, NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
+    static_assert(4 * LPW <= NSLOT, "a tile's loads, one every second slot, fit its slots");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * SLOT];
     const uint32_t lds0 = lds_byte_addr(smem);
 
@@ -255,10 +256,12 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dq_kernel(WideParams p
             }
             if constexpr (m + PF < NSLOT)
                 read_op(m + PF);
-            if constexpr (m < LPW)
-                dma.issue_block(rk, m, nbase, wave);
-            else if constexpr (m < 2 * LPW)
-                dma.issue_block(rv, m - LPW, nbase + TB, wave);
+            // the next tile's loads, one every second slot (spread over more
+            // slots, their writes into LDS compete less with the operand reads)
+            if constexpr (m % 2 == 0 && m / 2 < LPW)
+                dma.issue_block(rk, m / 2, nbase, wave);
+            else if constexpr (m % 2 == 0 && m / 2 < 2 * LPW)
+                dma.issue_block(rv, m / 2 - LPW, nbase + TB, wave);
             static_for<6 * Plan::MAXE>([&](auto ic) __attribute__((always_inline)) {
                 constexpr int i = decltype(ic)::value;
                 constexpr int st = i / (3 * Plan::MAXE), k = 2 - i / Plan::MAXE % 3;
@@ -374,6 +377,7 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
     using Lane = WideLaneXT<D>;
     using Dma = WideDmaT<D>;
     constexpr int NSLOT = Plan::NSLOT, PF = Plan::PF, LPW = Dma::LPW;
+    static_assert(4 * LPW < NSLOT, "a tile's loads, one every second slot, fit its slots");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[VEC + 4 * WBT * 4];
     const uint32_t lds0 = lds_byte_addr(smem);
 
@@ -558,11 +562,12 @@ __global__ void __launch_bounds__(WW * kWave, 1) bwd_wide_dkdv_kernel(WideParams
                 read_op(m + PF);
             if constexpr (m == 4)
                 read_vec(1);
-            if constexpr (m < LPW)
-                dma.issue_block(rq, m, nbase, wave);
-            else if constexpr (m < 2 * LPW)
-                dma.issue_block(rg, m - LPW, nbase + TB, wave);
-            else if constexpr (m == 2 * LPW)
+            // the next tile's loads, one every second slot
+            if constexpr (m % 2 == 0 && m / 2 < LPW)
+                dma.issue_block(rq, m / 2, nbase, wave);
+            else if constexpr (m % 2 == 0 && m / 2 < 2 * LPW)
+                dma.issue_block(rg, m / 2 - LPW, nbase + TB, wave);
+            else if constexpr (m == 4 * LPW)
                 issue_vec(tl, 1 - b);
             static_for<6 * Plan::MAXE>([&](auto ic) __attribute__((always_inline)) {
                 constexpr int i = decltype(ic)::value;
