@@ -10,8 +10,8 @@
 //     registers for the whole key loop, so O, m and l never leave registers
 //     (the key loop is the inner loop, the order of the pages'
 //     sequence-parallel successor, lukebest.github.io "谱系");
-//   - K and V stream through LDS in 64-key tiles (K triple-, V
-//     double-buffered) by direct global->LDS loads, which need no staging
+//   - K and V stream through LDS in 64-key tiles (three buffers each) by
+//     direct global->LDS loads, which need no staging
 //     registers; the loads of later tiles are in flight while one is
 //     computed, and one barrier per tile orders the buffers;
 //   - scores are computed transposed, S^T = K Q^T, so that each lane owns one
@@ -373,11 +373,13 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         // K and V of tile j+2 replace tile j-1's, last read before the
         // previous barrier; tile j+1's were issued one iteration ago (its K
         // has landed, its V may still be in flight).
+        // (without a tile j+2 tile j is loaded again, into the free buffer:
+        // no branch, so the tile's code stays one block for the scheduler;
+        // the last iteration's second half-step reads that buffer for scores
+        // it does not use)
         const bool more = tnn < t_end;
-        if (more) {
-            issue_k(tnn, KB_NN);
-            issue_v(tnn, KB_NN);
-        }
+        issue_k(more ? tnn : t, KB_NN);
+        issue_v(more ? tnn : t, KB_NN);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             // S^T of the next 32 keys: the second half of this tile, then the
@@ -511,10 +513,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
         // last, may still be in flight); the barrier extends that to all
         // waves. The next iteration reads tile j+2's K from its second
         // half-step on and its V one iteration later.
-        if (more)
-            lds_dma_wait<LPWV>();
-        else
-            lds_dma_wait<0>();
+        lds_dma_wait<LPWV>();
         barrier_reads_in_flight();
         t = tn;
         t1 = tnn;
@@ -546,6 +545,7 @@ __global__ void __launch_bounds__((64 * W), 1) fwd_bf16_kernel(FwdParams p)
 
     // Epilogue: O = O^T / lb (transposed back per lane), LSE from l in
     // natural log.
+    lds_dma_wait<0>();  // the last (repeated) tile load has landed: none outlives the workgroup
     const float lt = halves_sum(l);
     const float lbt = RSUM ? halves_sum(lb) : lt;
     if (row < N) {
